@@ -1,0 +1,224 @@
+#!/usr/bin/env python3
+"""Benchmark of the gemm15 hot path on one MI355X.
+
+Headline: TFLOPS = 2*M*N*K / median call time at M = N = K = 4096 with bf16
+inputs, fp32 accumulation and fp32 C (the square-GEMM workload), reported as a
+fraction of the gfx950 dense bf16 matrix peak; the same 4096^3 product with
+fp32 inputs (SGEMM) is measured beside it against the fp32 peak. Inputs are
+seeded synthetic uniform[-1, 1) matrices already resident in HBM.
+
+Protocol: W untimed warm-up calls, then K timed calls, each bracketed by a pair
+of HIP events recorded on the stream the kernel runs on; per-call time is the
+median (throughput) and the mean (roofline: average launch duration). The
+whole timed region is also bracketed by device synchronisation.
+
+``cpu_baseline`` times the fp64 host oracle on a bounded row-block of the same
+product on the host's cores.
+
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--all] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # 256 CU x 2.4 GHz x {4096, 256}
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--all", action="store_true", help="also time every workload (stderr + json)")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--json-out", default=None, help="write per-workload results here")
+    return ap.parse_args()
+
+
+def time_calls(fn, steps, warmup):
+    """Median and mean per-call milliseconds over `steps` event-bracketed calls."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in ev:
+        a.record(st)
+        fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = sorted(a.elapsed_time(b) for a, b in ev)
+    med = ms[len(ms) // 2] if len(ms) % 2 else 0.5 * (ms[len(ms) // 2 - 1] + ms[len(ms) // 2])
+    return med, sum(ms) / len(ms), wall
+
+
+def gemm_workload(g, name, steps, warmup):
+    import torch
+    import synth
+    w = synth.WORKLOADS[name]
+    A, B = synth.gemm_inputs(name)
+    dev = torch.device("cuda")
+    A, B = A.to(dev), B.to(dev)
+    M, N, K = w["M"], w["N"], w["K"]
+    plan = g.Plan(M, N, K, w["dtype"])
+    C = torch.empty((M, N), dtype=torch.float32, device=dev)
+    med, mean, wall = time_calls(lambda: plan.run(A, B, out=C), steps, warmup)
+    flops = 2 * M * N * K
+    es = 4 if w["dtype"] == "f32" else 2
+    byts = (M * K + K * N) * es + M * N * 4
+    return dict(workload=name, M=M, N=N, K=K, dtype=w["dtype"], config=plan.config_name,
+                median_ms=med, mean_ms=mean, wall_s=wall, flops=flops, bytes=byts,
+                tflops=flops / (med * 1e-3) / 1e12,
+                tflops_mean=flops / (mean * 1e-3) / 1e12,
+                gbs=byts / (med * 1e-3) / 1e9,
+                frac_peak=flops / (mean * 1e-3) / 1e12 / PEAK_TFLOPS[w["dtype"]])
+
+
+def ffn_workload(g, steps, warmup):
+    import torch
+    import synth
+    X, W1, b1, W2, b2 = synth.ffn_inputs()
+    dev = torch.device("cuda")
+    X, W1, b1, W2, b2 = (t.to(dev) for t in (X, W1, b1, W2, b2))
+    T, Hd, F = X.shape[0], X.shape[1], W1.shape[1]
+    p1 = g.Plan(T, F, Hd, "bf16", bias=True, gelu=True, out_dtype="bf16")
+    p2 = g.Plan(T, Hd, F, "bf16", bias=True, resid=True, out_dtype="bf16")
+    H = torch.empty((T, F), dtype=torch.bfloat16, device=dev)
+    Y = torch.empty((T, Hd), dtype=torch.bfloat16, device=dev)
+    out = {}
+    for tag, fn, fl, by in (
+        ("ffn1", lambda: p1.run(X, W1, bias=b1, out=H), 2 * T * F * Hd,
+         (T * Hd + Hd * F + T * F) * 2 + F * 4),
+        ("ffn2", lambda: p2.run(H, W2, bias=b2, resid=X, out=Y), 2 * T * F * Hd,
+         (T * F + F * Hd + 2 * T * Hd) * 2 + Hd * 4),
+    ):
+        med, mean, wall = time_calls(fn, steps, warmup)
+        out[tag] = dict(workload=tag, median_ms=med, mean_ms=mean, flops=fl, bytes=by,
+                        config=(p1 if tag == "ffn1" else p2).config_name,
+                        tflops=fl / (med * 1e-3) / 1e12, gbs=by / (med * 1e-3) / 1e9,
+                        frac_peak=fl / (mean * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"])
+    return out
+
+
+def qk_workload(g, steps, warmup):
+    import torch
+    import synth
+    Q, Kt = synth.qk_inputs()
+    dev = torch.device("cuda")
+    Q, Kt = Q.to(dev), Kt.to(dev)
+    nb, S, D = Q.shape
+    plan = g.Plan(S, S, D, "bf16", batch_hint=nb)
+    out = torch.empty((nb, S, S), dtype=torch.float32, device=dev)
+    med, mean, wall = time_calls(lambda: plan.run_batched(Q, Kt, out=out), steps, warmup)
+    fl = 2 * nb * S * S * D
+    by = nb * (2 * S * D * 2 + S * S * 4)
+    return dict(workload="qk_96x512x512x64", median_ms=med, mean_ms=mean, flops=fl, bytes=by,
+                config=plan.config_name, tflops=fl / (med * 1e-3) / 1e12,
+                gbs=by / (med * 1e-3) / 1e9, frac_hbm=by / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS)
+
+
+def cpu_baseline(target_s=12.0):
+    """The fp64 oracle on a row-block of the 4096^3 bf16 product, on all host cores."""
+    import numpy as np
+    import oracle
+    import synth
+    A, B = synth.gemm_inputs("bf16_4096")
+    Ab, Bb = synth.bits(A), synth.bits(B)
+    lib = oracle.load()
+    rows = 16
+    t0 = time.perf_counter()
+    oracle.gemm(Ab[:rows], Bb, "bf16", lib=lib)
+    t1 = time.perf_counter() - t0
+    rows2 = int(max(16, min(4096, rows * target_s / max(t1, 1e-3))))
+    t0 = time.perf_counter()
+    oracle.gemm(Ab[:rows2], Bb, "bf16", lib=lib)
+    t2 = time.perf_counter() - t0
+    fl = 2 * rows2 * 4096 * 4096
+    return dict(value=fl / t2 / 1e12, unit="TFLOPS", cores=oracle.threads(lib), kind="oracle",
+                sample=f"rows 0..{rows2 - 1} of the 4096^3 bf16 product (fp64 loop), {t2:.1f} s")
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the product shards by rows of A across GPUs, which is not measured here)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    import dense_gemm_15_amd as g
+
+    print("[bench] bf16_4096", file=sys.stderr, flush=True)
+    head = gemm_workload(g, "bf16_4096", args.steps, args.warmup)
+    print(f"[bench] {json.dumps(head)}", file=sys.stderr, flush=True)
+    print("[bench] fp32_4096", file=sys.stderr, flush=True)
+    f32 = gemm_workload(g, "fp32_4096", args.steps, args.warmup)
+    print(f"[bench] {json.dumps(f32)}", file=sys.stderr, flush=True)
+
+    extra = {}
+    if args.all:
+        for name in ("fp16_4096", "fp16_512", "gemv_1x4096x4096", "odd_127x1000x771",
+                     "odd_4095x4097x63"):
+            extra[name] = gemm_workload(g, name, args.steps, args.warmup)
+            print(f"[bench] {json.dumps(extra[name])}", file=sys.stderr, flush=True)
+        extra.update(ffn_workload(g, args.steps, args.warmup))
+        print(f"[bench] ffn {json.dumps(extra['ffn1'])} {json.dumps(extra['ffn2'])}",
+              file=sys.stderr, flush=True)
+        extra["qk"] = qk_workload(g, args.steps, args.warmup)
+        print(f"[bench] {json.dumps(extra['qk'])}", file=sys.stderr, flush=True)
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline()
+
+    line = {
+        "metric": "TFLOPS (2MNK/median time) at 4096^3 BF16 & FP32; % of gfx950 peak",
+        "value": round(head["tflops"], 2),
+        "unit": "TFLOPS",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["median_ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "square GEMM M=N=K=4096, bf16 A and B ~U[-1,1), fp32 accumulate, "
+                               "fp32 C", "M": 4096, "N": 4096, "K": 4096,
+                   "kernel": head["config"]},
+        "pct_of_peak": round(100 * head["tflops"] / PEAK_TFLOPS["bf16"], 2),
+        "roofline": {"bound": "mfma", "achieved": round(head["tflops_mean"], 2),
+                     "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
+                     "frac": round(head["frac_peak"], 4), "traffic": None},
+        "fp32_sgemm_4096": {"value": round(f32["tflops"], 2), "unit": "TFLOPS",
+                            "ms_per_call": round(f32["median_ms"], 5),
+                            "kernel": f32["config"],
+                            "pct_of_peak": round(100 * f32["tflops"] / PEAK_TFLOPS["f32"], 2),
+                            "roofline": {"bound": "mfma", "achieved": round(f32["tflops_mean"], 2),
+                                         "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
+                                         "frac": round(f32["frac_peak"], 4), "traffic": None}},
+        "cpu_baseline": cpu,
+    }
+    if args.json_out:
+        os.makedirs(os.path.dirname(os.path.abspath(args.json_out)), exist_ok=True)
+        with open(args.json_out, "w") as f:
+            json.dump(dict(headline=head, fp32=f32, extra=extra, cpu=cpu), f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

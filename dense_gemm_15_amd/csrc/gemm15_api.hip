@@ -1,0 +1,451 @@
+// gemm15_api.hip -- the C ABI: plans, the shape-bucket configuration choice with
+// its exact-shape cache, argument checking and launches.
+//
+// Configuration choice follows the DeepGEMM page (section 2.3: tile parameters
+// per size bucket, repeated shapes served from a cache; section 4.3: a
+// small-tile path when M or N is small; section 4.2: a configuration must fit
+// the shared-memory and register budget and balance the number of blocks
+// against per-block resources). Here the budget is gfx950's 160 KB of LDS per
+// workgroup and its compute-unit count, and the balance is an explicit cost
+// model: rounds of workgroups over the CUs times the work of one round at the
+// configuration's relative efficiency.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "../../include/gemm15.h"
+#include "kernels.hpp"
+
+using namespace g15;
+
+struct gemm_plan {
+  int64_t M, N, K;
+  int32_t dtype;
+  gemm_epilogue epi;
+  int device;
+  int config;    // primary configuration
+  int fallback;  // configuration for pointers without 16-byte alignment (may equal config)
+  int64_t batch_hint;
+  void* workspace;
+  int64_t workspace_bytes;
+  int split;
+};
+
+namespace {
+
+thread_local int t_last_error = GEMM_OK;
+
+struct Registry {
+  std::vector<KernelEntry> all;
+  Registry() {
+    const KernelEntry* p = nullptr;
+    int n = simple_entries(&p);
+    all.insert(all.end(), p, p + n);
+    n = mfma16_entries(&p);
+    all.insert(all.end(), p, p + n);
+    n = f32_entries(&p);
+    all.insert(all.end(), p, p + n);
+    n = gemv_entries(&p);
+    all.insert(all.end(), p, p + n);
+  }
+};
+
+const Registry& registry() {
+  static Registry r;
+  return r;
+}
+
+int elem_bytes(int dt) { return dt == GEMM_F32 ? 4 : 2; }
+
+bool valid_dtype(int dt) { return dt == GEMM_F32 || dt == GEMM_F16 || dt == GEMM_BF16; }
+
+gemm_epilogue norm_epi(const gemm_epilogue* e) {
+  gemm_epilogue d{0u, 1.0f, GEMM_F32};
+  return e ? *e : d;
+}
+
+// Relative sustained efficiency of a CU running a configuration at its
+// occupancy (1.0 = the best large tile). Measured on MI355X, rounded.
+double cfg_efficiency(const KernelEntry& k) {
+  if (k.kind == KIND_SIMPLE) return 0.02;
+  const int area = k.bm * k.bn;
+  double e;
+  if (area >= 256 * 256)
+    e = 1.0;
+  else if (area >= 256 * 128)
+    e = 0.92;
+  else if (area >= 128 * 128)
+    e = 0.8;
+  else if (area >= 128 * 64)
+    e = 0.6;
+  else
+    e = 0.4;
+  if (!k.vec_a || !k.vec_b) e *= 0.25;
+  return e;
+}
+
+// Workgroups one CU can hold for a configuration (LDS-limited; registers allow
+// at least as many for every configuration compiled here).
+int cfg_occupancy(const KernelEntry& k, const gemm_device_desc& dev) {
+  int occ = k.lds_bytes > 0 ? dev.lds_bytes / k.lds_bytes : 8;
+  if (occ < 1) occ = 1;
+  if (occ > 2) occ = 2;
+  return occ;
+}
+
+bool cfg_fits(const KernelEntry& k, int dtype, bool vec_a, bool vec_b, const gemm_device_desc& dev,
+              int64_t M) {
+  if (k.in_dtype != -1 && k.in_dtype != dtype) return false;
+  if (k.vec_a && !vec_a) return false;
+  if (k.vec_b && !vec_b) return false;
+  if (k.lds_bytes > dev.lds_bytes) return false;
+  if (k.kind == KIND_GEMV && M > k.bm) return false;
+  return true;
+}
+
+// Modelled time (arbitrary units) of a configuration on a problem.
+double cfg_cost(const KernelEntry& k, int64_t M, int64_t N, int64_t K, int64_t batch,
+                const gemm_device_desc& dev) {
+  const int64_t tm = (M + k.bm - 1) / k.bm, tn = (N + k.bn - 1) / k.bn;
+  const int64_t tiles = tm * tn * batch;
+  const int occ = cfg_occupancy(k, dev);
+  const int64_t slots = static_cast<int64_t>(dev.cu_count) * occ;
+  const int64_t rounds = (tiles + slots - 1) / slots;
+  const int64_t kpad = ((K + k.bk - 1) / k.bk) * k.bk;
+  // one round: each CU runs `occ` tiles sharing its throughput
+  const double round_work = static_cast<double>(k.bm) * k.bn * kpad * occ;
+  double t = static_cast<double>(rounds) * round_work / cfg_efficiency(k);
+  // a fixed per-tile cost (prologue, epilogue) keeps tiny-K shapes honest
+  t += static_cast<double>(rounds) * occ * k.bm * k.bn * 64.0;
+  return t;
+}
+
+int select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dtype,
+                  const gemm_epilogue& epi, int64_t batch, bool aligned16, int* fallback) {
+  (void)epi;
+  const auto& all = registry().all;
+  const int es = elem_bytes(dtype);
+  const bool vec_a = aligned16 && (K * es) % 16 == 0;
+  const bool vec_b = aligned16 && (N * es) % 16 == 0;
+  auto best_for = [&](bool va, bool vb) {
+    int best = -1;
+    double best_cost = 0;
+    for (int i = 0; i < static_cast<int>(all.size()); ++i) {
+      const KernelEntry& k = all[i];
+      if (!cfg_fits(k, dtype, va, vb, dev, M)) continue;
+      const double c = cfg_cost(k, M, N, K, batch, dev);
+      if (best < 0 || c < best_cost * 0.999) {
+        best = i;
+        best_cost = c;
+      }
+    }
+    return best;
+  };
+  const int primary = best_for(vec_a, vec_b);
+  *fallback = best_for(false, false);
+  return primary;
+}
+
+struct CacheKey {
+  int64_t M, N, K, batch;
+  int dtype, flags, out_dtype, aligned, cu, lds;
+  bool operator<(const CacheKey& o) const {
+    return std::tie(M, N, K, batch, dtype, flags, out_dtype, aligned, cu, lds) <
+           std::tie(o.M, o.N, o.K, o.batch, o.dtype, o.flags, o.out_dtype, o.aligned, o.cu, o.lds);
+  }
+};
+
+struct Cache {
+  std::mutex mu;
+  std::map<CacheKey, std::pair<int, int>> map;
+  int64_t hits = 0, misses = 0;
+};
+
+Cache& cache() {
+  static Cache c;
+  return c;
+}
+
+int forced_config() {
+  const char* s = std::getenv("GEMM15_FORCE_CONFIG");
+  if (!s || !*s) return -1;
+  const auto& all = registry().all;
+  for (int i = 0; i < static_cast<int>(all.size()); ++i)
+    if (std::strcmp(all[i].name, s) == 0) return i;
+  return -2;
+}
+
+// Cached choice for (shape, types, device facts).
+int choose(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dtype,
+           const gemm_epilogue& epi, int64_t batch, bool aligned16, int* fallback) {
+  CacheKey key{M, N, K, batch, dtype, static_cast<int>(epi.flags), epi.out_dtype,
+               aligned16 ? 1 : 0, dev.cu_count, dev.lds_bytes};
+  Cache& c = cache();
+  {
+    std::lock_guard<std::mutex> lk(c.mu);
+    auto it = c.map.find(key);
+    if (it != c.map.end()) {
+      ++c.hits;
+      *fallback = it->second.second;
+      return it->second.first;
+    }
+  }
+  int fb = -1;
+  const int cfg = select_config(dev, M, N, K, dtype, epi, batch, aligned16, &fb);
+  std::lock_guard<std::mutex> lk(c.mu);
+  ++c.misses;
+  c.map[key] = {cfg, fb};
+  *fallback = fb;
+  return cfg;
+}
+
+int check_problem(int64_t M, int64_t N, int64_t K, int32_t dtype, const gemm_epilogue& e,
+                  int64_t batch) {
+  if (M < 1 || N < 1 || K < 1) return GEMM_ERR_SHAPE;
+  if (batch < 1) return GEMM_ERR_ARG;
+  if (!valid_dtype(dtype) || !valid_dtype(e.out_dtype)) return GEMM_ERR_DTYPE;
+  if (e.flags & ~0xFu) return GEMM_ERR_DTYPE;
+  if (!std::isfinite(e.scale)) return GEMM_ERR_ARG;
+  // element indices are 64-bit; tile ids and batch index must fit the grid
+  if (M > (int64_t(1) << 31) || N > (int64_t(1) << 31) || K > (int64_t(1) << 31))
+    return GEMM_ERR_SHAPE;
+  return GEMM_OK;
+}
+
+int device_desc(int dev, gemm_device_desc* out) {
+  static std::mutex mu;
+  static std::map<int, gemm_device_desc> known;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = known.find(dev);
+  if (it != known.end()) {
+    *out = it->second;
+    return GEMM_OK;
+  }
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_ERR_HIP;
+  gemm_device_desc d;
+  d.cu_count = prop.multiProcessorCount;
+  d.lds_bytes = static_cast<int32_t>(prop.sharedMemPerBlock);
+  if (d.lds_bytes <= 0) d.lds_bytes = 65536;
+  known[dev] = d;
+  *out = d;
+  return GEMM_OK;
+}
+
+gemm_plan* fail(int code) {
+  t_last_error = code;
+  return nullptr;
+}
+
+bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
+                               const gemm_epilogue* epi_in, int64_t batch_hint, int32_t config) {
+  const gemm_epilogue epi = norm_epi(epi_in);
+  int rc = check_problem(M, N, K, dtype, epi, batch_hint);
+  if (rc) return fail(rc);
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(GEMM_ERR_NO_DEVICE);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(GEMM_ERR_HIP);
+  gemm_device_desc desc;
+  rc = device_desc(dev, &desc);
+  if (rc) return fail(rc);
+
+  const auto& all = registry().all;
+  int cfg, fb;
+  const int forced = config >= 0 ? config : forced_config();
+  if (forced == -2) return fail(GEMM_ERR_CONFIG);
+  if (forced >= 0) {
+    if (forced >= static_cast<int>(all.size())) return fail(GEMM_ERR_CONFIG);
+    const KernelEntry& k = all[forced];
+    const int es = elem_bytes(dtype);
+    if (!cfg_fits(k, dtype, (K * es) % 16 == 0, (N * es) % 16 == 0, desc, M))
+      return fail(GEMM_ERR_CONFIG);
+    cfg = forced;
+    fb = forced;
+    if (k.vec_a || k.vec_b) {
+      int dummy;
+      fb = select_config(desc, M, N, K, dtype, epi, batch_hint, false, &dummy);
+    }
+  } else {
+    cfg = choose(desc, M, N, K, dtype, epi, batch_hint, true, &fb);
+  }
+  if (cfg < 0 || fb < 0) return fail(GEMM_ERR_CONFIG);
+
+  gemm_plan* p = new (std::nothrow) gemm_plan();
+  if (!p) return fail(GEMM_ERR_NOMEM);
+  p->M = M;
+  p->N = N;
+  p->K = K;
+  p->dtype = dtype;
+  p->epi = epi;
+  p->device = dev;
+  p->config = cfg;
+  p->fallback = fb;
+  p->batch_hint = batch_hint;
+  p->workspace = nullptr;
+  p->workspace_bytes = 0;
+  p->split = 1;
+  return p;
+}
+
+gemm_plan* gemm_plan_create(int64_t M, int64_t N, int64_t K, int32_t dtype,
+                            const gemm_epilogue* epi) {
+  return gemm_plan_create_ex(M, N, K, dtype, epi, 1, -1);
+}
+
+int gemm_run_strided_batched(const gemm_plan* p, int64_t batch, const void* A, int64_t sA,
+                             const void* B, int64_t sB, const float* bias, const void* resid,
+                             int64_t sR, void* C, int64_t sC, void* stream) {
+  if (!p) return GEMM_ERR_PLAN;
+  if (batch < 1 || batch > 65535 || sA < 0 || sB < 0 || sC < 0 || sR < 0) return GEMM_ERR_ARG;
+  if (!A || !B || !C) return GEMM_ERR_NULL;
+  const gemm_epilogue& e = p->epi;
+  if ((e.flags & GEMM_EPI_BIAS) && !bias) return GEMM_ERR_NULL;
+  if ((e.flags & GEMM_EPI_RESID) && !resid) return GEMM_ERR_NULL;
+  const size_t ie = elem_bytes(p->dtype), oe = elem_bytes(e.out_dtype);
+  if (!aligned_to(A, ie) || !aligned_to(B, ie) || !aligned_to(C, oe)) return GEMM_ERR_ALIGN;
+  if ((e.flags & GEMM_EPI_BIAS) && !aligned_to(bias, 4)) return GEMM_ERR_ALIGN;
+  if ((e.flags & GEMM_EPI_RESID) && !aligned_to(resid, oe)) return GEMM_ERR_ALIGN;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+  if (dev != p->device) return GEMM_ERR_PLAN;
+
+  // The vector kernels need 16-byte aligned base pointers and batch strides.
+  const bool a16 = aligned_to(A, 16) && aligned_to(B, 16) && aligned_to(C, 16) &&
+                   (sA * ie) % 16 == 0 && (sB * ie) % 16 == 0 && (sC * oe) % 16 == 0 &&
+                   (!(e.flags & GEMM_EPI_RESID) || (aligned_to(resid, 16) && (sR * oe) % 16 == 0));
+  const auto& all = registry().all;
+  const KernelEntry& k = all[a16 ? p->config : p->fallback];
+
+  const int64_t tiles = ((p->M + k.bm - 1) / k.bm) * ((p->N + k.bn - 1) / k.bn);
+  if (tiles > 0x7fffffff) return GEMM_ERR_SHAPE;
+  if (k.kind == KIND_SIMPLE && (p->M + k.bm - 1) / k.bm > 65535) return GEMM_ERR_SHAPE;
+
+  LaunchArgs la;
+  la.M = p->M;
+  la.N = p->N;
+  la.K = p->K;
+  la.batch = batch;
+  la.A = A;
+  la.sA = sA;
+  la.B = B;
+  la.sB = sB;
+  la.C = C;
+  la.sC = sC;
+  la.sR = sR;
+  la.epi.flags = e.flags;
+  la.epi.scale = e.scale;
+  la.epi.bias = bias;
+  la.epi.resid = resid;
+  la.epi.out_dtype = e.out_dtype;
+  la.workspace = p->workspace;
+  la.workspace_bytes = p->workspace_bytes;
+  la.split = p->split;
+  const hipError_t err = k.launch(la, static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+int gemm_run(const gemm_plan* p, const void* A, const void* B, const float* bias,
+             const void* resid, void* C, void* stream) {
+  if (!p) return GEMM_ERR_PLAN;
+  return gemm_run_strided_batched(p, 1, A, 0, B, 0, bias, resid, 0, C, 0, stream);
+}
+
+void gemm_plan_destroy(gemm_plan* p) {
+  if (!p) return;
+  if (p->workspace) (void)hipFree(p->workspace);
+  delete p;
+}
+
+int gemm_last_error(void) { return t_last_error; }
+
+const char* gemm_strerror(int s) {
+  switch (s) {
+    case GEMM_OK: return "success";
+    case GEMM_ERR_SHAPE: return "invalid shape (a dimension < 1, or too large for the grid)";
+    case GEMM_ERR_DTYPE: return "invalid element type or epilogue flags";
+    case GEMM_ERR_NULL: return "a required pointer is NULL";
+    case GEMM_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    case GEMM_ERR_NO_DEVICE: return "no HIP device is visible";
+    case GEMM_ERR_HIP: return "a HIP runtime call or kernel launch failed";
+    case GEMM_ERR_PLAN: return "NULL plan, or plan used on another device";
+    case GEMM_ERR_NOMEM: return "out of memory while creating a plan";
+    case GEMM_ERR_CONFIG: return "the requested configuration cannot run this problem";
+    case GEMM_ERR_ARG: return "invalid argument";
+  }
+  return "unknown status";
+}
+
+int gemm_plan_describe(const gemm_plan* p, char* buf, size_t len) {
+  if (!p) return GEMM_ERR_PLAN;
+  const auto& all = registry().all;
+  const KernelEntry& k = all[p->config];
+  const int64_t tiles = ((p->M + k.bm - 1) / k.bm) * ((p->N + k.bn - 1) / k.bn);
+  char tmp[256];
+  const int n = std::snprintf(
+      tmp, sizeof(tmp),
+      "config=%s id=%d tile=%dx%dx%d threads=%d lds=%d workgroups=%lld split=%d fallback=%s",
+      k.name, p->config, k.bm, k.bn, k.bk, k.threads, k.lds_bytes,
+      static_cast<long long>(tiles * p->batch_hint), p->split, all[p->fallback].name);
+  if (buf && len > 0) {
+    std::strncpy(buf, tmp, len - 1);
+    buf[len - 1] = '\0';
+  }
+  return n;
+}
+
+int gemm_select(const gemm_device_desc* dev, int64_t M, int64_t N, int64_t K, int32_t dtype,
+                const gemm_epilogue* epi_in, int64_t batch_hint, int32_t aligned16,
+                gemm_choice* out) {
+  if (!dev || !out) return GEMM_ERR_NULL;
+  if (dev->cu_count < 1 || dev->lds_bytes < 1) return GEMM_ERR_ARG;
+  const gemm_epilogue epi = norm_epi(epi_in);
+  const int rc = check_problem(M, N, K, dtype, epi, batch_hint);
+  if (rc) return rc;
+  int fb;
+  const int cfg = choose(*dev, M, N, K, dtype, epi, batch_hint, aligned16 != 0, &fb);
+  if (cfg < 0) return GEMM_ERR_CONFIG;
+  const KernelEntry& k = registry().all[cfg];
+  out->config = cfg;
+  out->kind = k.kind;
+  out->bm = k.bm;
+  out->bn = k.bn;
+  out->bk = k.bk;
+  out->threads = k.threads;
+  out->lds_bytes = k.lds_bytes;
+  out->split = 1;
+  out->workgroups = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn) * batch_hint;
+  return GEMM_OK;
+}
+
+int gemm_config_count(void) { return static_cast<int>(registry().all.size()); }
+
+const char* gemm_config_name(int32_t i) {
+  const auto& all = registry().all;
+  if (i < 0 || i >= static_cast<int32_t>(all.size())) return nullptr;
+  return all[i].name;
+}
+
+void gemm_cache_stats(int64_t* hits, int64_t* misses, int64_t* entries) {
+  Cache& c = cache();
+  std::lock_guard<std::mutex> lk(c.mu);
+  if (hits) *hits = c.hits;
+  if (misses) *misses = c.misses;
+  if (entries) *entries = static_cast<int64_t>(c.map.size());
+}
+
+}  // extern "C"

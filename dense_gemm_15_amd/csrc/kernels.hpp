@@ -1,0 +1,56 @@
+// kernels.hpp -- host-side view of the gemm15 kernel family: launch arguments
+// and the registry of instantiated tile configurations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "device_common.hpp"
+
+namespace g15 {
+
+enum KernelKind : int {
+  KIND_SIMPLE = 0,  // LDS-tiled scalar kernel, any shape / alignment / type
+  KIND_MFMA16 = 1,  // bf16 / fp16 MFMA kernel
+  KIND_F32 = 2,     // fp32 MFMA kernel
+  KIND_GEMV = 3,    // few-row split-K kernel (M small)
+};
+
+// One launch: a strided batch of row-major products C = epi(A x B).
+struct LaunchArgs {
+  int64_t M, N, K;
+  int64_t batch;
+  const void* A;
+  int64_t sA;  // batch strides, in elements
+  const void* B;
+  int64_t sB;
+  void* C;
+  int64_t sC;
+  int64_t sR;  // residual batch stride (elements of out_dtype)
+  Epi epi;
+  void* workspace;      // split-K partials + counters (GEMV kind only)
+  int64_t workspace_bytes;
+  int split;            // split-K factor (GEMV kind only)
+};
+
+typedef hipError_t (*LaunchFn)(const LaunchArgs&, hipStream_t);
+
+struct KernelEntry {
+  const char* name;
+  int kind;       // KernelKind
+  int in_dtype;   // DT_* the kernel reads; -1: any
+  int bm, bn, bk; // block tile
+  int threads;    // workgroup size
+  int lds_bytes;  // static LDS per workgroup
+  int vec_a;      // 1: needs 16-byte aligned A rows (K multiple of 16 B / elem size)
+  int vec_b;      // 1: needs 16-byte aligned B rows
+  LaunchFn launch;
+};
+
+// Each kernel file appends its instantiations.
+int simple_entries(const KernelEntry** out);
+int mfma16_entries(const KernelEntry** out);
+int f32_entries(const KernelEntry** out);
+int gemv_entries(const KernelEntry** out);
+
+}  // namespace g15

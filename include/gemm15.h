@@ -1,0 +1,195 @@
+/*
+ * gemm15.h -- C ABI of the gemm15 dense GEMM library for AMD MI355X (gfx950).
+ *
+ * The library computes the row-major product
+ *
+ *     C[M x N] = epi( A[M x K] x B[K x N] )
+ *
+ * with element (i, k) of A at A[i*K + k], (k, j) of B at B[k*N + j] and (i, j)
+ * of C at C[i*N + j] (tutorial page "from CUDA tile parallelism to GEMM
+ * kernels", section 4.1; SGEMM page, section 1.1). A and B are both FP16, both
+ * BF16 or both FP32. Products and sums are FP32 whatever the input type
+ * (DeepGEMM page, section 3.4: 16-bit inputs, FP32 accumulation). The work is
+ * 2*M*N*K floating-point operations (SGEMM page, section 1.1).
+ *
+ * The optional epilogue runs on the FP32 accumulator in registers before the
+ * single store of C (DeepGEMM page, section 1.2: activation, residual add and
+ * vector scale fused into the GEMM instead of a second pass over C):
+ *
+ *     v = acc;  v *= scale (SCALE);  v += bias[j] (BIAS);
+ *     v = GELU(v) = v * Phi(v) (GELU, exact-erf form);  v += resid[i][j] (RESID);
+ *     C[i][j] = round_to_out_dtype(v)   (round to nearest, ties to even)
+ *
+ * Plans: gemm_plan_create chooses a kernel configuration for the problem shape
+ * from size buckets and caches the choice per exact shape, so repeated shapes
+ * hit the cache (DeepGEMM page, sections 2.3 and 4.3: different tile parameters
+ * per size bucket, a small-tile path for small M or N, cached configurations).
+ *
+ * Conventions of every entry point below:
+ *  - All pointers to matrix data are DEVICE pointers (memory of the GPU that is
+ *    current on the calling thread). The caller allocates and owns them; the
+ *    library never frees, copies or synchronises them.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
+ *    gemm_run* only enqueue work on it and return; results are ready when the
+ *    stream reaches that point.
+ *  - Errors are negative gemm_status codes; the creating calls return NULL and
+ *    record the code for gemm_last_error(). No call aborts the process.
+ *  - Thread safety: plans are immutable after creation and may be run from
+ *    several host threads. A plan whose description says "split" owns a device
+ *    workspace; two runs of such a plan must not overlap in time (use one plan
+ *    per stream).
+ */
+#ifndef GEMM15_H
+#define GEMM15_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types of A and B (both the same), of C and of the residual. */
+typedef enum gemm_dtype { GEMM_F32 = 0, GEMM_F16 = 1, GEMM_BF16 = 2 } gemm_dtype;
+
+/* Epilogue flags, applied in the order SCALE, BIAS, GELU, RESID. */
+enum {
+  GEMM_EPI_BIAS = 1u,  /* v += bias[j]; bias is FP32 of length N, shared by all rows */
+  GEMM_EPI_GELU = 2u,  /* v = v * Phi(v), Phi the standard normal CDF */
+  GEMM_EPI_RESID = 4u, /* v += resid[i][j]; resid is M x N row-major of type out_dtype */
+  GEMM_EPI_SCALE = 8u  /* v *= scale */
+};
+
+/* The epilogue of a plan. Passing NULL means {0, 1.0f, GEMM_F32}: plain C in FP32. */
+typedef struct gemm_epilogue {
+  uint32_t flags;    /* GEMM_EPI_* bits */
+  float scale;       /* multiplier when GEMM_EPI_SCALE is set */
+  int32_t out_dtype; /* gemm_dtype of C and of resid */
+} gemm_epilogue;
+
+typedef enum gemm_status {
+  GEMM_OK = 0,
+  GEMM_ERR_SHAPE = -1,     /* a dimension < 1, or a grid or index too large */
+  GEMM_ERR_DTYPE = -2,     /* unknown dtype, out_dtype or epilogue flag */
+  GEMM_ERR_NULL = -3,      /* NULL A, B or C, or NULL bias / resid when its flag is set */
+  GEMM_ERR_ALIGN = -4,     /* a pointer not aligned to its element size */
+  GEMM_ERR_NO_DEVICE = -5, /* no HIP device is visible */
+  GEMM_ERR_HIP = -6,       /* a HIP runtime call or a kernel launch failed */
+  GEMM_ERR_PLAN = -7,      /* NULL plan, or a plan used on another device than its own */
+  GEMM_ERR_NOMEM = -8,     /* host or device memory for a plan could not be allocated */
+  GEMM_ERR_CONFIG = -9,    /* a forced configuration does not exist or does not fit */
+  GEMM_ERR_ARG = -10       /* another invalid argument (batch < 1, a bad stride, ...) */
+} gemm_status;
+
+typedef struct gemm_plan gemm_plan;
+
+/*
+ * Create a plan for C = epi(A x B) with A M x K and B K x N of type `dtype`.
+ * Chooses the kernel configuration (shape-bucket rules, exact-shape cache) for
+ * the device current on the calling thread. Host work only, except that a plan
+ * whose configuration splits K allocates and zeroes its own device workspace.
+ * Returns NULL on error (see gemm_last_error()).
+ */
+gemm_plan* gemm_plan_create(int64_t M, int64_t N, int64_t K, int32_t dtype,
+                            const gemm_epilogue* epi);
+
+/*
+ * As gemm_plan_create, with two extra inputs:
+ *  batch_hint  expected batch of gemm_run_strided_batched calls (>= 1); the
+ *              configuration is chosen for that many independent products.
+ *  config      -1: choose automatically; otherwise the index of a configuration
+ *              listed by gemm_config_name (GEMM_ERR_CONFIG if it cannot run this
+ *              problem). Used by tuning sweeps and by tests of each kernel.
+ */
+gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
+                               const gemm_epilogue* epi, int64_t batch_hint, int32_t config);
+
+/*
+ * Enqueue C = epi(A x B) on `stream`.
+ *  A      device, M x K row-major, plan dtype
+ *  B      device, K x N row-major, plan dtype
+ *  bias   device, N FP32 values; required iff GEMM_EPI_BIAS, else ignored
+ *  resid  device, M x N row-major of out_dtype; required iff GEMM_EPI_RESID, else
+ *         ignored. resid may equal C (each element is read before it is written).
+ *  C      device, M x N row-major of out_dtype; must not overlap A or B
+ * Returns GEMM_OK, or GEMM_ERR_PLAN / _NULL / _ALIGN / _HIP. Pointers need only
+ * element alignment; 16-byte aligned rows take the vector-load kernels.
+ */
+int gemm_run(const gemm_plan* plan, const void* A, const void* B, const float* bias,
+             const void* resid, void* C, void* stream);
+
+/*
+ * Enqueue `batch` independent products C_b = epi(A_b x B_b), b = 0..batch-1, with
+ * A_b = A + b*strideA, B_b = B + b*strideB, C_b = C + b*strideC and residual
+ * resid + b*strideR (strides in ELEMENTS of the respective type; a stride of 0
+ * shares one operand across the batch). bias is shared by the whole batch.
+ * This is the batched QK^T product of attention: per (batch, head) an
+ * [S x D] x [D x S] GEMM (tutorial page, section 2; DeepGEMM page, section 1.1).
+ * Same pointer rules and errors as gemm_run, plus GEMM_ERR_ARG for batch < 1 or a
+ * negative stride.
+ */
+int gemm_run_strided_batched(const gemm_plan* plan, int64_t batch, const void* A,
+                             int64_t strideA, const void* B, int64_t strideB, const float* bias,
+                             const void* resid, int64_t strideR, void* C, int64_t strideC,
+                             void* stream);
+
+/* Release a plan and its workspace. NULL is ignored. The caller must make sure no
+ * enqueued run of the plan is still pending on a stream. */
+void gemm_plan_destroy(gemm_plan* plan);
+
+/* The status of the last failing gemm_plan_create* call on this thread. */
+int gemm_last_error(void);
+
+/* A static English message for a status code (never NULL). */
+const char* gemm_strerror(int status);
+
+/*
+ * Write a one-line description of the plan (configuration name, tile, grid,
+ * LDS bytes, split) into buf (always NUL-terminated when len > 0).
+ * Returns the number of characters the full line needs, or a negative status.
+ */
+int gemm_plan_describe(const gemm_plan* plan, char* buf, size_t len);
+
+/* ---------------- host-only introspection (no GPU needed) ------------------ */
+
+/* The hardware facts configuration choice depends on. */
+typedef struct gemm_device_desc {
+  int32_t cu_count;  /* compute units (256 on MI355X) */
+  int32_t lds_bytes; /* LDS per workgroup (163840 on gfx950) */
+} gemm_device_desc;
+
+/* What a configuration choice resolves to. */
+typedef struct gemm_choice {
+  int32_t config;    /* index for gemm_config_name / gemm_plan_create_ex */
+  int32_t kind;      /* 0 simple, 1 mfma16, 2 fp32 mfma, 3 few-row split-K */
+  int32_t bm, bn, bk;
+  int32_t threads;
+  int32_t lds_bytes;
+  int32_t split;     /* K split factor (1 = none) */
+  int64_t workgroups;
+} gemm_choice;
+
+/*
+ * Choose a configuration for a problem on a described device, without touching
+ * a GPU, through the same rules and exact-shape cache gemm_plan_create uses.
+ * `aligned16` says whether A, B and C will be 16-byte aligned (the allocator's
+ * usual guarantee). Returns GEMM_OK or a negative status.
+ */
+int gemm_select(const gemm_device_desc* dev, int64_t M, int64_t N, int64_t K, int32_t dtype,
+                const gemm_epilogue* epi, int64_t batch_hint, int32_t aligned16,
+                gemm_choice* out);
+
+/* Number of configurations compiled into the library. */
+int gemm_config_count(void);
+
+/* Name of configuration i (NULL when out of range). */
+const char* gemm_config_name(int32_t i);
+
+/* Exact-shape cache counters since load (any pointer may be NULL). */
+void gemm_cache_stats(int64_t* hits, int64_t* misses, int64_t* entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM15_H */

@@ -1,0 +1,148 @@
+"""The C ABI on the host: exports, argument checking and configuration choice.
+
+CPU only: nothing here launches a kernel. ``gemm_select`` runs the same
+shape-bucket rules and exact-shape cache as plan creation against a described
+device, so the dispatch logic is testable without a GPU.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+import dense_gemm_15_amd as g
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm15.h")
+MI355X = dict(cu_count=256, lds_bytes=163840)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(g.lib, n), n
+    assert set(names) == set(g.SIGNATURES), "binding and header disagree"
+
+
+def test_library_is_the_in_tree_build():
+    maps = open("/proc/self/maps").read()
+    assert g.LIB_PATH in maps
+
+
+def test_strerror_every_status():
+    for code in list(g.STATUS) + [-99, 5]:
+        s = g.strerror(code)
+        assert isinstance(s, str) and s
+    assert g.strerror(0) == "success"
+
+
+def test_config_names_unique():
+    names = g.config_names()
+    assert len(names) == len(set(names)) == g.lib.gemm_config_count()
+    assert g.lib.gemm_config_name(-1) is None
+    assert g.lib.gemm_config_name(len(names)) is None
+
+
+@pytest.mark.skipif(torch.cuda.is_available(), reason="checks the no-device path")
+def test_plan_create_without_device():
+    with pytest.raises(g.GemmError) as e:
+        g.Plan(64, 64, 64, "bf16")
+    assert e.value.status == -5
+
+
+def test_null_plan_rejected():
+    assert g.lib.gemm_run(None, None, None, None, None, None, None) == -7
+    assert g.lib.gemm_plan_describe(None, None, 0) == -7
+    g.lib.gemm_plan_destroy(None)  # no-op
+
+
+@pytest.mark.parametrize("shape,code", [((0, 4, 4), -1), ((4, -1, 4), -1), ((4, 4, 0), -1),
+                                        ((1 << 32, 4, 4), -1)])
+def test_select_rejects_bad_shapes(shape, code):
+    with pytest.raises(g.GemmError) as e:
+        g.select(*shape, "bf16", **MI355X)
+    assert e.value.status == code
+
+
+def test_select_rejects_bad_dtype_and_args():
+    ch = g.Choice()
+    dev = g.DeviceDesc(256, 163840)
+    e = g.Epilogue(0, 1.0, 0)
+    assert g.lib.gemm_select(ctypes.byref(dev), 8, 8, 8, 7, ctypes.byref(e), 1, 1,
+                             ctypes.byref(ch)) == -2
+    bad = g.Epilogue(0, 1.0, 9)
+    assert g.lib.gemm_select(ctypes.byref(dev), 8, 8, 8, 0, ctypes.byref(bad), 1, 1,
+                             ctypes.byref(ch)) == -2
+    bad = g.Epilogue(64, 1.0, 0)
+    assert g.lib.gemm_select(ctypes.byref(dev), 8, 8, 8, 0, ctypes.byref(bad), 1, 1,
+                             ctypes.byref(ch)) == -2
+    assert g.lib.gemm_select(ctypes.byref(dev), 8, 8, 8, 0, ctypes.byref(e), 0, 1,
+                             ctypes.byref(ch)) == -10
+    assert g.lib.gemm_select(None, 8, 8, 8, 0, ctypes.byref(e), 1, 1, ctypes.byref(ch)) == -3
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("shape", [(4096, 4096, 4096), (8192, 3072, 768), (8192, 768, 3072),
+                                   (512, 512, 512), (1, 4096, 4096), (127, 1000, 771),
+                                   (4095, 4097, 63), (1, 1, 1), (33, 65, 17)])
+def test_select_fits_budget_and_type(dtype, shape):
+    ch = g.select(*shape, dtype, **MI355X)
+    name = g.config_names()[ch.config]
+    assert ch.lds_bytes <= MI355X["lds_bytes"]
+    assert dtype in name
+    es = 4 if dtype == "f32" else 2
+    M, N, K = shape
+    if (K * es) % 16 or (N * es) % 16:
+        # rows that are not 16-byte multiples never take a 16-byte-load kernel
+        assert "scalar" in name or name.startswith("simple")
+
+
+def test_select_small_lds_device():
+    ch = g.select(4096, 4096, 4096, "bf16", cu_count=64, lds_bytes=65536)
+    assert ch.lds_bytes <= 65536
+
+
+def test_select_large_square_uses_big_tiles():
+    ch = g.select(4096, 4096, 4096, "bf16", **MI355X)
+    assert ch.bm * ch.bn >= 128 * 128
+    assert ch.workgroups >= 256  # at least one workgroup per CU
+
+
+def test_select_small_problem_uses_small_tiles():
+    big = g.select(4096, 4096, 4096, "f16", **MI355X)
+    small = g.select(1, 4096, 4096, "f16", **MI355X)
+    assert small.bm * small.bn < big.bm * big.bn
+
+
+def test_select_batch_hint_changes_tiles():
+    one = g.select(512, 512, 64, "bf16", batch_hint=1, **MI355X)
+    many = g.select(512, 512, 64, "bf16", batch_hint=96, **MI355X)
+    assert many.bm * many.bn >= one.bm * one.bn
+    assert many.workgroups >= 256
+
+
+def test_exact_shape_cache_hit():
+    h0, m0, e0 = g.cache_stats()
+    g.select(777, 555, 333, "bf16", **MI355X)
+    h1, m1, e1 = g.cache_stats()
+    g.select(777, 555, 333, "bf16", **MI355X)
+    h2, m2, e2 = g.cache_stats()
+    assert (m1, e1) == (m0 + 1, e0 + 1)
+    assert (h2, m2, e2) == (h1 + 1, m1, e1)
+
+
+def test_package_never_touches_oracle():
+    pkg = os.path.join(ROOT, "dense_gemm_15_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f

@@ -1,0 +1,247 @@
+"""Parity of the HIP path (through the C ABI) against the fp64 oracle.
+
+Tolerances (see ``oracle.check``): |C - ref| <= c (1e-4 |scale| s + 1e-6) per
+element, plus half a 16-bit ulp for 16-bit outputs; small-integer inputs must
+match exactly; the fp32 4096^3 SGEMM must also stay within 1e-3 absolute
+(the SGEMM page, section 4.1).
+"""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from tests import gpu_cases as gc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def g():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dense_gemm_15_amd as g
+    return g
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def _configs():
+    # configuration names without importing the library at collection time
+    try:
+        import dense_gemm_15_amd as g
+        return g.config_names()
+    except Exception:
+        return []
+
+
+def _dtype_of(name):
+    for d in ("bf16", "f16", "f32"):
+        if f"_{d}" in name or name.startswith(d + "_"):
+            return d
+    return None
+
+
+CONFIGS = _configs()
+
+
+@pytest.mark.parametrize("name", CONFIGS)
+def test_each_config_ragged(g, name):
+    """Every compiled configuration on shapes spanning several tiles with ragged tails."""
+    dtype = _dtype_of(name)
+    idx = g.config_index(name)
+    vec = "scalar" not in name and not name.startswith("simple")
+    parts = name.split("_")
+    tile = [p for p in parts if "x" in p and p[0].isdigit()][0] if not name.startswith("simple") \
+        else "64x64"
+    bm, bn = map(int, tile.split("x"))
+    bk = 32 if dtype == "f32" and not name.startswith("simple") else 64
+    align = 4 if dtype == "f32" else 8
+    shapes = [(2 * bm + 3, bn + align, 2 * bk + align), (bm, bn, bk), (1, align, align)]
+    if not vec:
+        shapes += [(2 * bm + 3, bn + 5, 2 * bk + 7), (1, 1, 1), (5, 3, 2)]
+    for si, (M, N, K) in enumerate(shapes):
+        say(f"[{name}] M={M} N={N} K={K}")
+        plan = g.Plan(M, N, K, dtype, config=idx)
+        assert plan.config_name == name
+        for kind in ("uniform", "int"):
+            A, B = gc.inputs(M, N, K, dtype, 1000 + 17 * si, kind)
+            C = gc.run_gpu(plan, A, B)
+            r = gc.check_full(C, A, B, dtype, exact=(kind == "int"))
+            assert r["ok"], (name, M, N, K, kind, r)
+
+
+EPI_CASES = [
+    dict(bias=True),
+    dict(bias=True, gelu=True),
+    dict(bias=True, resid=True),
+    dict(scale=0.125),
+    dict(scale=0.5, bias=True, gelu=True, resid=True),
+    dict(gelu=True, resid=True),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("epi", range(len(EPI_CASES)))
+def test_epilogues(g, dtype, out_dtype, epi):
+    """Fused epilogues on the automatically chosen kernel, every output type."""
+    e = EPI_CASES[epi]
+    M, N, K = 300, 264, 200
+    say(f"[epi] {dtype}->{out_dtype} {e}")
+    plan = g.Plan(M, N, K, dtype, out_dtype=out_dtype, **e)
+    A, B = gc.inputs(M, N, K, dtype, 77)
+    bias = synth.normal(78, (N,), 0.5, "f32") if e.get("bias") else None
+    resid = synth.uniform(79, (M, N), out_dtype) if e.get("resid") else None
+    C = gc.run_gpu(plan, A, B, bias, resid)
+    r = gc.check_full(C, A, B, dtype, out_dtype, bias, resid, e.get("scale"), e.get("gelu", False))
+    assert r["ok"], (dtype, out_dtype, e, plan.describe(), r)
+
+
+def test_workload_fp16_512(g):
+    """FP16 512^3, fp32 out: every element against the oracle."""
+    A, B = synth.gemm_inputs("fp16_512")
+    plan = g.Plan(512, 512, 512, "f16")
+    say("[fp16_512]", plan.describe())
+    C = gc.run_gpu(plan, A, B)
+    r = gc.check_full(C, A, B, "f16")
+    assert r["ok"], r
+
+
+@pytest.mark.parametrize("name", ["bf16_4096", "fp16_4096", "fp32_4096"])
+def test_workload_square_4096(g, name):
+    """4096^3 at the benchmark's launch configuration: sampled elements (random,
+    corners, tile edges) against the oracle; the fp32 case also within 1e-3."""
+    w = synth.WORKLOADS[name]
+    A, B = synth.gemm_inputs(name)
+    plan = g.Plan(4096, 4096, 4096, w["dtype"])
+    say(f"[{name}]", plan.describe())
+    C = gc.run_gpu(plan, A, B)
+    rows, cols = gc.sample_indices(4096, 4096, 3000, 5)
+    r = gc.check_sampled(C, A, B, w["dtype"], rows, cols,
+                         abs_max=1e-3 if w["dtype"] == "f32" else None)
+    assert r["ok"], r
+    assert np.isfinite(C.float().numpy()).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_square_4096_integer_rowsums(g, dtype):
+    """Small-integer 4096^3: sampled elements exact, and every row sum of C equals
+    A (B 1) computed by the oracle (a property covering all 16.7M outputs)."""
+    import oracle
+    M = N = K = 4096
+    A = synth.small_int(61, (M, K), dtype)
+    B = synth.small_int(62, (K, N), dtype)
+    plan = g.Plan(M, N, K, dtype)
+    C = gc.run_gpu(plan, A, B)
+    rows, cols = gc.sample_indices(M, N, 2000, 6)
+    r = gc.check_sampled(C, A, B, dtype, rows, cols, exact=True)
+    assert r["ok"], r
+    Bones = synth.bits(B).astype(np.float64) if dtype == "f32" else oracle.decode(dtype, synth.bits(B))
+    bsum = Bones.sum(axis=1)  # exact: integers below 2^53
+    # A (B 1) through the oracle: a K x 1 right operand of the row sums
+    bcol = torch.from_numpy(bsum.astype(np.float32)).reshape(K, 1)
+    ref, _ = oracle.gemm(synth.bits(A.float()), synth.bits(bcol), "f32")
+    got = C.double().numpy().sum(axis=1)
+    assert np.array_equal(got, ref[:, 0]), np.abs(got - ref[:, 0]).max()
+
+
+def test_workload_ffn(g):
+    """Encoder FFN: H = GELU(X W1 + b1) in bf16, Y = H W2 + b2 + X in bf16.
+    GEMM1 sampled against the oracle; GEMM2 sampled against the oracle fed the
+    GPU's own H (stage-wise parity)."""
+    X, W1, b1, W2, b2 = synth.ffn_inputs()
+    T, Hd, F = X.shape[0], X.shape[1], W1.shape[1]
+    p1 = g.Plan(T, F, Hd, "bf16", bias=True, gelu=True, out_dtype="bf16")
+    p2 = g.Plan(T, Hd, F, "bf16", bias=True, resid=True, out_dtype="bf16")
+    say("[ffn1]", p1.describe())
+    say("[ffn2]", p2.describe())
+    dev = torch.device("cuda")
+    Xd = X.to(dev)
+    H = p1.run(Xd, W1.to(dev), bias=b1.to(dev))
+    Y = p2.run(H, W2.to(dev), bias=b2.to(dev), resid=Xd)
+    torch.cuda.synchronize()
+    H, Y = H.cpu(), Y.cpu()
+    rows, cols = gc.sample_indices(T, F, 3000, 7)
+    r = gc.check_sampled(H, X, W1, "bf16", rows, cols, "bf16", bias=b1, gelu=True)
+    assert r["ok"], ("ffn1", r)
+    rows, cols = gc.sample_indices(T, Hd, 3000, 8)
+    r = gc.check_sampled(Y, H, W2, "bf16", rows, cols, "bf16", bias=b2, resid=X)
+    assert r["ok"], ("ffn2", r)
+
+
+def test_workload_qk_batched(g):
+    """96 attention-score GEMMs 512 x 512 x 64 in one strided-batched call; every
+    element of every head against the oracle."""
+    import oracle
+    Q, Kt = synth.qk_inputs()
+    nb, S, D = Q.shape
+    plan = g.Plan(S, S, D, "bf16", batch_hint=nb)
+    say("[qk]", plan.describe())
+    dev = torch.device("cuda")
+    Sc = plan.run_batched(Q.to(dev), Kt.to(dev))
+    torch.cuda.synchronize()
+    Sc = Sc.cpu()
+    for b in range(nb):
+        ref, s = oracle.gemm(synth.bits(Q[b]), synth.bits(Kt[b]), "bf16")
+        r = oracle.check(synth.bits(Sc[b]), ref, s)
+        assert r["ok"], (b, r)
+
+
+@pytest.mark.parametrize("name", ["gemv_1x4096x4096", "odd_127x1000x771", "odd_4095x4097x63"])
+def test_workload_odd_shapes(g, name):
+    """M = 1, and shapes with ragged, unaligned rows: every element."""
+    w = synth.WORKLOADS[name]
+    A, B = synth.gemm_inputs(name)
+    plan = g.Plan(w["M"], w["N"], w["K"], w["dtype"])
+    say(f"[{name}]", plan.describe())
+    C = gc.run_gpu(plan, A, B)
+    r = gc.check_full(C, A, B, w["dtype"])
+    assert r["ok"], r
+
+
+def test_repeat_shape_hits_cache(g):
+    """A repeated shape is served from the exact-shape cache."""
+    h0, m0, _ = g.cache_stats()
+    g.Plan(333, 444, 555, "bf16")
+    h1, m1, _ = g.cache_stats()
+    g.Plan(333, 444, 555, "bf16")
+    h2, m2, _ = g.cache_stats()
+    assert m2 == m1 and h2 == h1 + 1
+
+
+def test_unaligned_pointer_fallback(g):
+    """A 16-bit operand offset by one element is not 16-byte aligned: the plan
+    takes its scalar fallback and the result is still right."""
+    M, N, K = 200, 136, 72
+    A, B = gc.inputs(M, N, K, "bf16", 91)
+    dev = torch.device("cuda")
+    Abuf = torch.empty(M * K + 1, dtype=torch.bfloat16, device=dev)
+    Abuf[1:] = A.reshape(-1).to(dev)
+    Aoff = Abuf[1:].view(M, K)
+    plan = g.Plan(M, N, K, "bf16")
+    C = plan.run(Aoff, B.to(dev))
+    torch.cuda.synchronize()
+    r = gc.check_full(C.cpu(), A, B, "bf16")
+    assert r["ok"], r
+
+
+def test_errors_on_device(g):
+    """Error paths that need a live device: NULL pointers and misalignment."""
+    import ctypes
+    plan = g.Plan(64, 64, 64, "f32", bias=True)
+    dev = torch.device("cuda")
+    A = torch.zeros(64, 64, device=dev)
+    rc = g.lib.gemm_run(plan._h, ctypes.c_void_p(A.data_ptr()), ctypes.c_void_p(A.data_ptr()),
+                        None, None, ctypes.c_void_p(A.data_ptr()), None)
+    assert rc == -3  # bias flag set, bias NULL
+    rc = g.lib.gemm_run(plan._h, ctypes.c_void_p(A.data_ptr() + 2), ctypes.c_void_p(A.data_ptr()),
+                        ctypes.c_void_p(A.data_ptr()), None, ctypes.c_void_p(A.data_ptr()), None)
+    assert rc == -4  # fp32 A not 4-byte aligned
+    rc = g.lib.gemm_run(None, None, None, None, None, None, None)
+    assert rc == -7
