@@ -27,6 +27,33 @@ import time
 
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # 256 CU x 2.4 GHz x {4096, 256}
 PEAK_HBM_GBS = 8000.0
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def kernel_source_hash() -> str:
+    """Hash of the device sources; counter data taken from other sources is stale."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "dense_gemm_15_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel_config: str):
+    """Bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary, or None
+    when it is missing or was taken from different kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_hash") != kernel_source_hash():
+        return None
+    row = t.get("kernels", {}).get(kernel_config)
+    return None if row is None else row["traffic_bytes"]
 
 
 def parse():
@@ -37,6 +64,8 @@ def parse():
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr + json)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--json-out", default=None, help="write per-workload results here")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -126,7 +155,7 @@ def qk_workload(g, steps, warmup):
                 gbs=by / (med * 1e-3) / 1e9, frac_hbm=by / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS)
 
 
-def cpu_baseline(target_s=12.0):
+def cpu_baseline(target_s=15.0):
     """The fp64 oracle on a row-block of the 4096^3 bf16 product, on all host cores."""
     import numpy as np
     import oracle
@@ -134,7 +163,8 @@ def cpu_baseline(target_s=12.0):
     A, B = synth.gemm_inputs("bf16_4096")
     Ab, Bb = synth.bits(A), synth.bits(B)
     lib = oracle.load()
-    rows = 16
+    oracle.gemm(Ab[:16], Bb, "bf16", lib=lib)  # first call: thread pool start-up
+    rows = 128
     t0 = time.perf_counter()
     oracle.gemm(Ab[:rows], Bb, "bf16", lib=lib)
     t1 = time.perf_counter() - t0
@@ -147,7 +177,70 @@ def cpu_baseline(target_s=12.0):
                 sample=f"rows 0..{rows2 - 1} of the 4096^3 bf16 product (fp64 loop), {t2:.1f} s")
 
 
+def symbol_to_config(sym: str):
+    """Configuration name of a gemm15 kernel symbol (None for other kernels)."""
+    import re
+    m = re.search(r"gemm_m16d_kernel<g15::(\w+)_t, (\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)>", sym)
+    if m:
+        t, bm, bn, wm, wn, sa, kr, r = m.groups()
+        return f"m16d_{t}_{bm}x{bn}x64_w{wm}x{wn}_a{sa}_b{kr}_r{r}"
+    m = re.search(r"gemm_f32_kernel<(\d+), (\d+), (\d+), (\d+), (\w+), (\w+)>", sym)
+    if m:
+        bm, bn, wm, wn, va, vb = m.groups()
+        return f"f32_{bm}x{bn}_w{wm}x{wn}" + ("" if va == "true" else "_scalar")
+    return None
+
+
+def summarize(db_dir: str, kind: str) -> None:
+    """Print a text summary of rocprofv3 results under db_dir (kernel trace or
+    FETCH_SIZE / WRITE_SIZE counters) and, for counters, update the traffic file."""
+    import collections
+    import glob
+    import sqlite3
+    dbs = glob.glob(os.path.join(db_dir, "**", "*.db"), recursive=True)
+    if kind == "trace":
+        for db in dbs:
+            d = sqlite3.connect(db)
+            print(f"{'kernel':96s} {'calls':>6s} {'avg_us':>10s} {'pct':>6s}")
+            for name, calls, tot, avg, pct in d.execute(
+                    "select name, total_calls, total_duration, average, percentage from top_kernels"):
+                print(f"{name[:96]:96s} {calls:6d} {avg:10.2f} {pct:6.2f}")
+        return
+    acc = collections.defaultdict(list)
+    for db in dbs:
+        d = sqlite3.connect(db)
+        for name, cn, val in d.execute("select kernel_name, counter_name, value from counters_collection"):
+            acc[(name, cn)].append(val)
+    print(f"{'kernel':96s} {'counter':12s} {'n':>4s} {'KiB/dispatch':>14s}")
+    for (name, cn), v in sorted(acc.items()):
+        print(f"{name[:96]:96s} {cn:12s} {len(v):4d} {sum(v) / len(v):14.1f}")
+    # update the traffic file with the scale of each counter on the 256 MiB copy
+    t = {"kernels": {}}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    copy = {cn: sum(v) / len(v) for (name, cn), v in acc.items() if "copyBuffer" in name}
+    for cn, kib in copy.items():
+        t.setdefault("scale", {})[cn] = 262144.0 / kib
+    for (name, cn), v in acc.items():
+        cfg = symbol_to_config(name)
+        if cfg is None:
+            continue
+        t["kernels"].setdefault(cfg, {})[cn + "_kib"] = sum(v) / len(v)
+    sc = t.get("scale", {})
+    for cfg, row in t["kernels"].items():
+        if "FETCH_SIZE_kib" in row and "WRITE_SIZE_kib" in row and sc:
+            row["traffic_bytes"] = round(row["FETCH_SIZE_kib"] * 1024 * sc.get("FETCH_SIZE", 1.0)
+                                         + row["WRITE_SIZE_kib"] * 1024 * sc.get("WRITE_SIZE", 1.0))
+    t["source_hash"] = kernel_source_hash()
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(t, f, indent=1, sort_keys=True)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
+        summarize(sys.argv[2], sys.argv[3])
+        return
     args = parse()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
@@ -168,6 +261,14 @@ def main():
     print(f"[bench] {json.dumps(f32)}", file=sys.stderr, flush=True)
 
     extra = {}
+    if args.copy_calibration:
+        import torch as _t
+        src = _t.empty(64 * 2**20, dtype=_t.float32, device="cuda")  # 256 MiB
+        dst = _t.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        _t.cuda.synchronize()
+        print("[bench] copy calibration: 3 x 256 MiB device copies", file=sys.stderr, flush=True)
     if args.all:
         for name in ("fp16_4096", "fp16_512", "gemv_1x4096x4096", "odd_127x1000x771",
                      "odd_4095x4097x63"):
@@ -203,14 +304,16 @@ def main():
         "pct_of_peak": round(100 * head["tflops"] / PEAK_TFLOPS["bf16"], 2),
         "roofline": {"bound": "mfma", "achieved": round(head["tflops_mean"], 2),
                      "peak": PEAK_TFLOPS["bf16"], "unit": "TFLOP/s",
-                     "frac": round(head["frac_peak"], 4), "traffic": None},
+                     "frac": round(head["frac_peak"], 4),
+                     "traffic": measured_traffic(head["config"])},
         "fp32_sgemm_4096": {"value": round(f32["tflops"], 2), "unit": "TFLOPS",
                             "ms_per_call": round(f32["median_ms"], 5),
                             "kernel": f32["config"],
                             "pct_of_peak": round(100 * f32["tflops"] / PEAK_TFLOPS["f32"], 2),
                             "roofline": {"bound": "mfma", "achieved": round(f32["tflops_mean"], 2),
                                          "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
-                                         "frac": round(f32["frac_peak"], 4), "traffic": None}},
+                                         "frac": round(f32["frac_peak"], 4),
+                                         "traffic": measured_traffic(f32["config"])}},
         "cpu_baseline": cpu,
     }
     if args.json_out:

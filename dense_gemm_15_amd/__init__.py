@@ -78,7 +78,7 @@ SIGNATURES = {
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
-            f"{LIB_PATH} is not built; run `python -m dense_gemm_15_amd.build` (hipcc, gfx950)")
+            f"{LIB_PATH} is not built; run `python dense_gemm_15_amd/build.py` (hipcc, gfx950)")
     lib = ctypes.CDLL(LIB_PATH)
     for name, (res, args) in SIGNATURES.items():
         fn = getattr(lib, name)

@@ -1,6 +1,7 @@
 """Build libgemm15.so in-tree: every csrc/*.hip compiled for gfx950, then linked.
 
-Run ``python -m dense_gemm_15_amd.build`` (or ``__graft_entry__.build()``).
+Run ``python dense_gemm_15_amd/build.py`` (or ``__graft_entry__.build()``); it
+does not import the package, so a stale or broken library never blocks a rebuild.
 """
 from __future__ import annotations
 
@@ -51,6 +52,12 @@ def build(jobs: int | None = None, verbose: bool = True) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
+    # every kernel's host launch stub must be defined in the library; a missing
+    # one means a kernel template failed to instantiate for the host pass
+    nm = subprocess.run(["nm", "-u", "-C", tmp], capture_output=True, text=True)
+    missing = [ln.strip() for ln in nm.stdout.splitlines() if "g15::" in ln]
+    if missing:
+        raise RuntimeError("library has undefined internal symbols:\n" + "\n".join(missing))
     os.replace(tmp, OUT)
     if verbose:
         print(f"built {OUT} from {len(srcs)} sources", file=sys.stderr)

@@ -51,6 +51,10 @@ struct Registry {
     all.insert(all.end(), p, p + n);
     n = mfma16_entries(&p);
     all.insert(all.end(), p, p + n);
+    n = mfma16_pipe_entries(&p);
+    all.insert(all.end(), p, p + n);
+    n = mfma16_dlds_entries(&p);
+    all.insert(all.end(), p, p + n);
     n = f32_entries(&p);
     all.insert(all.end(), p, p + n);
     n = gemv_entries(&p);
@@ -72,24 +76,41 @@ gemm_epilogue norm_epi(const gemm_epilogue* e) {
   return e ? *e : d;
 }
 
-// Relative sustained efficiency of a CU running a configuration at its
-// occupancy (1.0 = the best large tile). Measured on MI355X, rounded.
+// Relative sustained throughput of one CU running a configuration at full
+// occupancy (1.0 = the fastest configuration of the same input type). Measured
+// on MI355X with square 4096 products (whole rounds of tiles, so wave
+// quantisation does not enter) and rounded; the cost model below adds the
+// rounds of tiles a shape needs.
+struct EffRow {
+  const char* name_prefix;
+  double eff;
+};
+const EffRow kEff[] = {
+    // bf16 / fp16
+    {"m16d_bf16_256x256x64_w4x2_a3_b4_r1", 1.00}, {"m16d_f16_256x256x64_w4x2_a3_b4_r1", 1.00},
+    {"m16d_bf16_256x256x64_w2x4_a3_b4_r1", 0.97}, {"m16d_f16_256x256x64_w2x4_a3_b4_r1", 0.97},
+    {"m16d_bf16_256x256x64_w2x4_a3_b4_r2", 0.82}, {"m16d_f16_256x256x64_w2x4_a3_b4_r2", 0.82},
+    {"m16d_bf16_256x128", 0.81}, {"m16d_f16_256x128", 0.81},
+    {"m16d_bf16_256x256x64_w2x2", 0.79}, {"m16d_f16_256x256x64_w2x2", 0.79},
+    {"m16p_bf16_256x256x64_w2x2", 0.68}, {"m16p_f16_256x256x64_w2x2", 0.68},
+    {"m16p_bf16_256x256x64_w2x4", 0.62}, {"m16p_f16_256x256x64_w2x4", 0.62},
+    {"m16p_bf16_128x128", 0.48}, {"m16p_f16_128x128", 0.48},
+    {"mfma16_bf16_128x128_w2x2_scalar", 0.10}, {"mfma16_f16_128x128_w2x2_scalar", 0.10},
+    {"mfma16_bf16_64x64_w2x2_scalar", 0.08}, {"mfma16_f16_64x64_w2x2_scalar", 0.08},
+    {"mfma16_bf16_128x128", 0.52}, {"mfma16_f16_128x128", 0.52},
+    {"mfma16_bf16_128x64", 0.45}, {"mfma16_f16_128x64", 0.45},
+    {"mfma16_bf16_64x64", 0.33}, {"mfma16_f16_64x64", 0.33},
+    // fp32 (relative to the fp32 matrix-core peak path)
+    {"f32_128x128_w2x2_scalar", 0.69}, {"f32_64x64_w2x2_scalar", 0.6},
+    {"f32_128x128", 1.00}, {"f32_128x256", 0.97}, {"f32_256x128", 0.95},
+    {"f32_64x64", 0.92}, {"f32_256x256", 0.56},
+};
+
 double cfg_efficiency(const KernelEntry& k) {
-  if (k.kind == KIND_SIMPLE) return 0.02;
-  const int area = k.bm * k.bn;
-  double e;
-  if (area >= 256 * 256)
-    e = 1.0;
-  else if (area >= 256 * 128)
-    e = 0.92;
-  else if (area >= 128 * 128)
-    e = 0.8;
-  else if (area >= 128 * 64)
-    e = 0.6;
-  else
-    e = 0.4;
-  if (!k.vec_a || !k.vec_b) e *= 0.25;
-  return e;
+  for (const EffRow& r : kEff)
+    if (std::strncmp(k.name, r.name_prefix, std::strlen(r.name_prefix)) == 0) return r.eff;
+  if (k.kind == KIND_SIMPLE) return 0.03;
+  return 0.3;  // other tiles: measured well below the configurations above
 }
 
 // Workgroups one CU can hold for a configuration (LDS-limited; registers allow
@@ -102,8 +123,13 @@ int cfg_occupancy(const KernelEntry& k, const gemm_device_desc& dev) {
 }
 
 bool cfg_fits(const KernelEntry& k, int dtype, bool vec_a, bool vec_b, const gemm_device_desc& dev,
-              int64_t M) {
+              int64_t M, int64_t N, int64_t K, int out_dtype) {
   if (k.in_dtype != -1 && k.in_dtype != dtype) return false;
+  if (k.buf32) {
+    const int64_t lim = int64_t(1) << 31;
+    const int64_t es = elem_bytes(dtype), oe = elem_bytes(out_dtype);
+    if (M * K * es >= lim || K * N * es >= lim || M * N * oe >= lim) return false;
+  }
   if (k.vec_a && !vec_a) return false;
   if (k.vec_b && !vec_b) return false;
   if (k.lds_bytes > dev.lds_bytes) return false;
@@ -130,7 +156,6 @@ double cfg_cost(const KernelEntry& k, int64_t M, int64_t N, int64_t K, int64_t b
 
 int select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dtype,
                   const gemm_epilogue& epi, int64_t batch, bool aligned16, int* fallback) {
-  (void)epi;
   const auto& all = registry().all;
   const int es = elem_bytes(dtype);
   const bool vec_a = aligned16 && (K * es) % 16 == 0;
@@ -140,7 +165,7 @@ int select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, 
     double best_cost = 0;
     for (int i = 0; i < static_cast<int>(all.size()); ++i) {
       const KernelEntry& k = all[i];
-      if (!cfg_fits(k, dtype, va, vb, dev, M)) continue;
+      if (!cfg_fits(k, dtype, va, vb, dev, M, N, K, epi.out_dtype)) continue;
       const double c = cfg_cost(k, M, N, K, batch, dev);
       if (best < 0 || c < best_cost * 0.999) {
         best = i;
@@ -272,7 +297,7 @@ gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
     if (forced >= static_cast<int>(all.size())) return fail(GEMM_ERR_CONFIG);
     const KernelEntry& k = all[forced];
     const int es = elem_bytes(dtype);
-    if (!cfg_fits(k, dtype, (K * es) % 16 == 0, (N * es) % 16 == 0, desc, M))
+    if (!cfg_fits(k, dtype, (K * es) % 16 == 0, (N * es) % 16 == 0, desc, M, N, K, epi.out_dtype))
       return fail(GEMM_ERR_CONFIG);
     cfg = forced;
     fb = forced;

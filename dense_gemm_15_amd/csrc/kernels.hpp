@@ -45,11 +45,14 @@ struct KernelEntry {
   int vec_a;      // 1: needs 16-byte aligned A rows (K multiple of 16 B / elem size)
   int vec_b;      // 1: needs 16-byte aligned B rows
   LaunchFn launch;
+  int buf32 = 0;  // 1: addresses A, B, C with 32-bit byte offsets (each must be < 2 GiB)
 };
 
 // Each kernel file appends its instantiations.
 int simple_entries(const KernelEntry** out);
 int mfma16_entries(const KernelEntry** out);
+int mfma16_pipe_entries(const KernelEntry** out);
+int mfma16_dlds_entries(const KernelEntry** out);
 int f32_entries(const KernelEntry** out);
 int gemv_entries(const KernelEntry** out);
 

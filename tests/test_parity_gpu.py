@@ -59,8 +59,10 @@ def test_each_config_ragged(g, name):
     parts = name.split("_")
     tile = [p for p in parts if "x" in p and p[0].isdigit()][0] if not name.startswith("simple") \
         else "64x64"
-    bm, bn = map(int, tile.split("x"))
-    bk = 32 if dtype == "f32" and not name.startswith("simple") else 64
+    dims = list(map(int, tile.split("x")))
+    bm, bn = dims[0], dims[1]
+    bk = dims[2] if len(dims) > 2 else (32 if dtype == "f32" and not name.startswith("simple")
+                                        else 64)
     align = 4 if dtype == "f32" else 8
     shapes = [(2 * bm + 3, bn + align, 2 * bk + align), (bm, bn, bk), (1, align, align)]
     if not vec:
