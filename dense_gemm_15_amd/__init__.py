@@ -152,7 +152,7 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h:
+        if h and lib is not None:  # at interpreter exit the module globals may be gone
             lib.gemm_plan_destroy(h)
             self._h = None
 

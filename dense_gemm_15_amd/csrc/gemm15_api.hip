@@ -57,6 +57,8 @@ struct Registry {
     all.insert(all.end(), p, p + n);
     n = f32_entries(&p);
     all.insert(all.end(), p, p + n);
+    n = f32_dlds_entries(&p);
+    all.insert(all.end(), p, p + n);
     n = gemv_entries(&p);
     all.insert(all.end(), p, p + n);
   }
@@ -100,10 +102,13 @@ const EffRow kEff[] = {
     {"mfma16_bf16_128x128", 0.52}, {"mfma16_f16_128x128", 0.52},
     {"mfma16_bf16_128x64", 0.45}, {"mfma16_f16_128x64", 0.45},
     {"mfma16_bf16_64x64", 0.33}, {"mfma16_f16_64x64", 0.33},
-    // fp32 (relative to the fp32 matrix-core peak path)
-    {"f32_128x128_w2x2_scalar", 0.69}, {"f32_64x64_w2x2_scalar", 0.6},
-    {"f32_128x128", 1.00}, {"f32_128x256", 0.97}, {"f32_256x128", 0.95},
-    {"f32_64x64", 0.92}, {"f32_256x256", 0.56},
+    // fp32 (relative to the fastest fp32 configuration)
+    {"f32d_256x256x16_w4x2_a3", 1.00}, {"f32d_128x256x16_w2x4_a4", 0.95},
+    {"f32d_128x128x16_w2x2_a3", 0.95}, {"f32d_128x128x16_w2x2_a4", 0.93},
+    {"f32d_256x128x16_w4x2_a4", 0.91},
+    {"f32_128x128_w2x2_scalar", 0.63}, {"f32_64x64_w2x2_scalar", 0.55},
+    {"f32_128x128", 0.91}, {"f32_128x256", 0.88}, {"f32_256x128", 0.86},
+    {"f32_64x64", 0.83}, {"f32_256x256", 0.51},
 };
 
 double cfg_efficiency(const KernelEntry& k) {

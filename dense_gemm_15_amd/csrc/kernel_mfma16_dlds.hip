@@ -158,8 +158,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16d_kernel(LaunchArgs a)
     for (int i = 0; i < AI; ++i) {
       const int r0 = (wave * AI + i) * 8;
       const uint32_t off = kin ? a_voff[i] : OOB;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)(lds + stage * A_STAGE + r0 * 8), 16,
-                                               off, 0, 0, 0);
+      u32x4* slot = lds + stage * A_STAGE + r0 * 8;
+      // an out-of-range load leaves its LDS slot untouched: zero it here so the
+      // K tail multiplies zeros, never stale or uninitialised LDS contents
+      if (!kin) slot[lane] = u32x4{0u, 0u, 0u, 0u};
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)slot, 16, off, 0, 0, 0);
     }
   };
 

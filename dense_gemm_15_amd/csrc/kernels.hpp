@@ -54,6 +54,7 @@ int mfma16_entries(const KernelEntry** out);
 int mfma16_pipe_entries(const KernelEntry** out);
 int mfma16_dlds_entries(const KernelEntry** out);
 int f32_entries(const KernelEntry** out);
+int f32_dlds_entries(const KernelEntry** out);
 int gemv_entries(const KernelEntry** out);
 
 }  // namespace g15

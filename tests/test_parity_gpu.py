@@ -41,10 +41,14 @@ def _configs():
 
 
 def _dtype_of(name):
-    for d in ("bf16", "f16", "f32"):
-        if f"_{d}" in name or name.startswith(d + "_"):
-            return d
-    return None
+    """Input type a configuration reads, from its name (f32 kernels start with f32)."""
+    if "bf16" in name:
+        return "bf16"
+    if "_f16" in name:
+        return "f16"
+    if name.startswith("f32") or "_f32" in name:
+        return "f32"
+    raise ValueError(f"no input type in configuration name {name}")
 
 
 CONFIGS = _configs()
