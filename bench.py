@@ -90,7 +90,37 @@ def time_calls(fn, steps, warmup):
     return med, sum(ms) / len(ms), wall
 
 
-def gemm_workload(g, name, steps, warmup):
+def time_graph(fn, reps=20, replays=7):
+    """Median per-call milliseconds of `reps` calls captured in one HIP graph and
+    replayed: the GPU time of a call without the host's launch overhead, which
+    dominates the event-per-call time of a kernel of a few microseconds."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for _ in range(reps):
+            fn()
+    graph.replay()
+    torch.cuda.synchronize()
+    ts = []
+    st = torch.cuda.current_stream()
+    for _ in range(replays):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(st)
+        graph.replay()
+        b.record(st)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) / reps)
+    del graph
+    return sorted(ts)[len(ts) // 2]
+
+
+def gemm_workload(g, name, steps, warmup, graph=False):
     import torch
     import synth
     w = synth.WORKLOADS[name]
@@ -100,16 +130,22 @@ def gemm_workload(g, name, steps, warmup):
     M, N, K = w["M"], w["N"], w["K"]
     plan = g.Plan(M, N, K, w["dtype"])
     C = torch.empty((M, N), dtype=torch.float32, device=dev)
-    med, mean, wall = time_calls(lambda: plan.run(A, B, out=C), steps, warmup)
+    run = lambda: plan.run(A, B, out=C)  # noqa: E731
+    med, mean, wall = time_calls(run, steps, warmup)
     flops = 2 * M * N * K
     es = 4 if w["dtype"] == "f32" else 2
     byts = (M * K + K * N) * es + M * N * 4
-    return dict(workload=name, M=M, N=N, K=K, dtype=w["dtype"], config=plan.config_name,
-                median_ms=med, mean_ms=mean, wall_s=wall, flops=flops, bytes=byts,
-                tflops=flops / (med * 1e-3) / 1e12,
-                tflops_mean=flops / (mean * 1e-3) / 1e12,
-                gbs=byts / (med * 1e-3) / 1e9,
-                frac_peak=flops / (mean * 1e-3) / 1e12 / PEAK_TFLOPS[w["dtype"]])
+    r = dict(workload=name, M=M, N=N, K=K, dtype=w["dtype"], config=plan.config_name,
+             median_ms=med, mean_ms=mean, wall_s=wall, flops=flops, bytes=byts,
+             tflops=flops / (med * 1e-3) / 1e12,
+             tflops_mean=flops / (mean * 1e-3) / 1e12,
+             gbs=byts / (med * 1e-3) / 1e9,
+             frac_peak=flops / (mean * 1e-3) / 1e12 / PEAK_TFLOPS[w["dtype"]])
+    if graph:
+        gms = time_graph(run)
+        r.update(graph_ms=gms, graph_tflops=flops / (gms * 1e-3) / 1e12,
+                 graph_gbs=byts / (gms * 1e-3) / 1e9)
+    return r
 
 
 def ffn_workload(g, steps, warmup):
@@ -131,10 +167,12 @@ def ffn_workload(g, steps, warmup):
          (T * F + F * Hd + 2 * T * Hd) * 2 + Hd * 4),
     ):
         med, mean, wall = time_calls(fn, steps, warmup)
+        gms = time_graph(fn)
         out[tag] = dict(workload=tag, median_ms=med, mean_ms=mean, flops=fl, bytes=by,
                         config=(p1 if tag == "ffn1" else p2).config_name,
                         tflops=fl / (med * 1e-3) / 1e12, gbs=by / (med * 1e-3) / 1e9,
-                        frac_peak=fl / (mean * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"])
+                        frac_peak=fl / (mean * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
+                        graph_ms=gms, graph_tflops=fl / (gms * 1e-3) / 1e12)
     return out
 
 
@@ -147,12 +185,16 @@ def qk_workload(g, steps, warmup):
     nb, S, D = Q.shape
     plan = g.Plan(S, S, D, "bf16", batch_hint=nb)
     out = torch.empty((nb, S, S), dtype=torch.float32, device=dev)
-    med, mean, wall = time_calls(lambda: plan.run_batched(Q, Kt, out=out), steps, warmup)
+    run = lambda: plan.run_batched(Q, Kt, out=out)  # noqa: E731
+    med, mean, wall = time_calls(run, steps, warmup)
+    gms = time_graph(run)
     fl = 2 * nb * S * S * D
     by = nb * (2 * S * D * 2 + S * S * 4)
     return dict(workload="qk_96x512x512x64", median_ms=med, mean_ms=mean, flops=fl, bytes=by,
                 config=plan.config_name, tflops=fl / (med * 1e-3) / 1e12,
-                gbs=by / (med * 1e-3) / 1e9, frac_hbm=by / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS)
+                gbs=by / (med * 1e-3) / 1e9, frac_hbm=by / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                graph_ms=gms, graph_tflops=fl / (gms * 1e-3) / 1e12,
+                graph_frac_hbm=by / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS)
 
 
 def cpu_baseline(target_s=15.0):
@@ -184,6 +226,13 @@ def symbol_to_config(sym: str):
     if m:
         t, bm, bn, wm, wn, sa, kr, r = m.groups()
         return f"m16d_{t}_{bm}x{bn}x64_w{wm}x{wn}_a{sa}_b{kr}_r{r}"
+    m = re.search(r"gemm_f32d_kernel<(\d+), (\d+), (\d+), (\d+), (\d+)>", sym)
+    if m:
+        bm, bn, wm, wn, sa = m.groups()
+        return f"f32d_{bm}x{bn}x16_w{wm}x{wn}_a{sa}"
+    m = re.search(r"gemv_kernel<g15::(\w+)_t, (\d+), (\d+), (\d+)>", sym)
+    if m:
+        return f"gemv_{m.group(1)}_m{m.group(2)}"
     m = re.search(r"gemm_f32_kernel<(\d+), (\d+), (\d+), (\d+), (\w+), (\w+)>", sym)
     if m:
         bm, bn, wm, wn, va, vb = m.groups()
@@ -272,7 +321,7 @@ def main():
     if args.all:
         for name in ("fp16_4096", "fp16_512", "gemv_1x4096x4096", "odd_127x1000x771",
                      "odd_4095x4097x63"):
-            extra[name] = gemm_workload(g, name, args.steps, args.warmup)
+            extra[name] = gemm_workload(g, name, args.steps, args.warmup, graph=True)
             print(f"[bench] {json.dumps(extra[name])}", file=sys.stderr, flush=True)
         extra.update(ffn_workload(g, args.steps, args.warmup))
         print(f"[bench] ffn {json.dumps(extra['ffn1'])} {json.dumps(extra['ffn2'])}",

@@ -138,8 +138,34 @@ bool cfg_fits(const KernelEntry& k, int dtype, bool vec_a, bool vec_b, const gem
   if (k.vec_a && !vec_a) return false;
   if (k.vec_b && !vec_b) return false;
   if (k.lds_bytes > dev.lds_bytes) return false;
-  if (k.kind == KIND_GEMV && M > k.bm) return false;
+  if (k.kind == KIND_GEMV && (M > k.bm || K > static_cast<int64_t>(k.bk) * 65535)) return false;
   return true;
+}
+
+// Split-K factor of a few-row (GEMV kind) configuration: enough workgroups to
+// keep every CU streaming B (about four per CU), each with at least 128 rows
+// of K, and never more than bk rows per workgroup (its A staging limit).
+int gemv_split(const KernelEntry& k, int64_t N, int64_t K, int64_t batch,
+               const gemm_device_desc& dev) {
+  const int64_t strips = (N + k.bn - 1) / k.bn;
+  const int64_t s_min = (K + k.bk - 1) / k.bk;
+  int64_t s = (4 * static_cast<int64_t>(dev.cu_count) + strips * batch - 1) / (strips * batch);
+  const int64_t s_rows = (K + 127) / 128;
+  if (s > s_rows) s = s_rows;
+  if (s < s_min) s = s_min;
+  if (s < 1) s = 1;
+  return static_cast<int>(s);
+}
+
+// fp32 partial sums [split][bm][N].
+int64_t gemv_workspace_bytes(const KernelEntry& k, int64_t N, int split) {
+  return split <= 1 ? 0 : static_cast<int64_t>(split) * k.bm * N * 4;
+}
+
+// Workgroups of one launch (one batch item for the GEMV kind, which loops).
+int64_t cfg_workgroups(const KernelEntry& k, int64_t M, int64_t N, int split, int64_t batch) {
+  const int64_t tiles = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn);
+  return k.kind == KIND_GEMV ? tiles * split : tiles * batch;
 }
 
 // Modelled time (arbitrary units) of a configuration on a problem.
@@ -170,6 +196,7 @@ int select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, 
     double best_cost = 0;
     for (int i = 0; i < static_cast<int>(all.size()); ++i) {
       const KernelEntry& k = all[i];
+      if (k.kind == KIND_GEMV) continue;
       if (!cfg_fits(k, dtype, va, vb, dev, M, N, K, epi.out_dtype)) continue;
       const double c = cfg_cost(k, M, N, K, batch, dev);
       if (best < 0 || c < best_cost * 0.999) {
@@ -179,9 +206,19 @@ int select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, 
     }
     return best;
   };
-  const int primary = best_for(vec_a, vec_b);
   *fallback = best_for(false, false);
-  return primary;
+  // A few rows (M <= 8): the product is a stream over B, served by the
+  // split-K few-row kernel with the fewest rows that covers M (DeepGEMM page,
+  // section 4.3: small shapes get their own small-block kernel).
+  int gemv = -1;
+  for (int i = 0; i < static_cast<int>(all.size()); ++i) {
+    const KernelEntry& k = all[i];
+    if (k.kind != KIND_GEMV || !cfg_fits(k, dtype, vec_a, vec_b, dev, M, N, K, epi.out_dtype))
+      continue;
+    if (gemv < 0 || k.bm < all[gemv].bm) gemv = i;
+  }
+  if (gemv >= 0) return gemv;
+  return best_for(vec_a, vec_b);
 }
 
 struct CacheKey {
@@ -329,6 +366,17 @@ gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
   p->workspace = nullptr;
   p->workspace_bytes = 0;
   p->split = 1;
+  const KernelEntry& k = all[cfg];
+  if (k.kind == KIND_GEMV) {
+    p->split = gemv_split(k, N, K, batch_hint, desc);
+    p->workspace_bytes = gemv_workspace_bytes(k, N, p->split);
+    if (p->workspace_bytes > 0 &&
+        hipMalloc(&p->workspace, static_cast<size_t>(p->workspace_bytes)) != hipSuccess) {
+      (void)hipGetLastError();
+      delete p;
+      return fail(GEMM_ERR_NOMEM);
+    }
+  }
   return p;
 }
 
@@ -424,13 +472,13 @@ int gemm_plan_describe(const gemm_plan* p, char* buf, size_t len) {
   if (!p) return GEMM_ERR_PLAN;
   const auto& all = registry().all;
   const KernelEntry& k = all[p->config];
-  const int64_t tiles = ((p->M + k.bm - 1) / k.bm) * ((p->N + k.bn - 1) / k.bn);
   char tmp[256];
   const int n = std::snprintf(
       tmp, sizeof(tmp),
       "config=%s id=%d tile=%dx%dx%d threads=%d lds=%d workgroups=%lld split=%d fallback=%s",
       k.name, p->config, k.bm, k.bn, k.bk, k.threads, k.lds_bytes,
-      static_cast<long long>(tiles * p->batch_hint), p->split, all[p->fallback].name);
+      static_cast<long long>(cfg_workgroups(k, p->M, p->N, p->split, p->batch_hint)), p->split,
+      all[p->fallback].name);
   if (buf && len > 0) {
     std::strncpy(buf, tmp, len - 1);
     buf[len - 1] = '\0';
@@ -457,8 +505,8 @@ int gemm_select(const gemm_device_desc* dev, int64_t M, int64_t N, int64_t K, in
   out->bk = k.bk;
   out->threads = k.threads;
   out->lds_bytes = k.lds_bytes;
-  out->split = 1;
-  out->workgroups = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn) * batch_hint;
+  out->split = k.kind == KIND_GEMV ? gemv_split(k, N, K, batch_hint, *dev) : 1;
+  out->workgroups = cfg_workgroups(k, M, N, out->split, batch_hint);
   return GEMM_OK;
 }
 

@@ -336,8 +336,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16d_kernel(LaunchArgs a)
   }
   if (kt < nk) slice(std::integral_constant<int, 0>{}, kt);
 
-  // ---- epilogue: lane holds C[row][col] of block (i, j) with col = lane % 32 and
-  // row = 8 (r / 4) + 4 (lane / 32) + r % 4; masked lanes store out of range.
+  // ---- epilogue. In the accumulators lane l holds C[row][col] of block (i, j)
+  // with col = l % 32 and row = 8 (r / 4) + 4 (l / 32) + r % 4: one column per
+  // lane, so direct stores would write 2 or 4 bytes per lane. Instead scale, bias
+  // and GELU are applied there (the bias is one value per lane and block column),
+  // then each 32-row block row of the wave's sub-tile goes through the wave's own
+  // LDS area and comes back as 8 consecutive columns per lane: residual loads and
+  // C stores move 16 or 32 contiguous bytes per lane. Columns come in whole
+  // chunks of 8 (N is a multiple of 8 for this kernel), so a chunk is all inside
+  // or all outside the matrix.
+  wait_vm<0>();
+  lds_barrier();  // every wave is done with the operand ring; LDS is free
+  constexpr int EP = WTN + 8;  // floats per staged row: rows 4 apart land 32 banks apart
+  constexpr int CPR = WTN / 8;  // 8-column chunks per row
+  constexpr int RPP = 64 / CPR;  // rows per pass
+  constexpr int PASSES = 32 / RPP;
+  static_assert(NW * 32 * EP * 4 <= static_cast<int>(sizeof(lds)), "staging must fit in LDS");
+  static_assert(64 % CPR == 0 && 32 % RPP == 0, "staging passes");
+  float* stg = reinterpret_cast<float*>(lds) + wave * 32 * EP;
+
   const Epi& e = a.epi;
   const int ob = e.out_dtype == DT_F32 ? 4 : 2;
   const auto rC = rsrc(static_cast<char*>(a.C) + z * a.sC * ob,
@@ -346,36 +363,77 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16d_kernel(LaunchArgs a)
   const auto rR = rsrc(has_r ? static_cast<const char*>(e.resid) + z * a.sR * ob
                              : static_cast<const char*>(a.C),
                        static_cast<uint32_t>(static_cast<int64_t>(M) * N * ob));
+  float bj[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
     const int col = n0 + wn * WTN + j * 32 + lrow;
-    const bool okc = col < N;
-    const float bn = ((e.flags & EPI_BIAS) && okc) ? e.bias[col] : 0.f;
+    bj[j] = ((e.flags & EPI_BIAS) && col < N) ? e.bias[col] : 0.f;
+  }
+  const int q = lane % CPR;  // this lane's chunk within a staged row
+  const int col = n0 + wn * WTN + 8 * q;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * WTM + i * 32 + 8 * (r >> 2) + 4 * lhalf + (r & 3);
-        const uint32_t off = (okc && row < M) ? static_cast<uint32_t>(row * N + col) * ob : OOB;
         float v = acc[i][j][r];
         if (e.flags & EPI_SCALE) v *= e.scale;
-        if (e.flags & EPI_BIAS) v += bn;
+        if (e.flags & EPI_BIAS) v += bj[j];
         if (e.flags & EPI_GELU) v = gelu(v);
-        if (has_r) {
-          if (ob == 4) {
-            v += __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rR, off, 0, 0));
-          } else {
-            const uint16_t h = __builtin_amdgcn_raw_buffer_load_b16(rR, off, 0, 0);
-            v += e.out_dtype == DT_BF16 ? widen(bf16_t{}, h) : widen(f16_t{}, h);
-          }
-        }
+        stg[(8 * (r >> 2) + 4 * lhalf + (r & 3)) * EP + 32 * j + lrow] = v;
+      }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's staging writes are done
+
+    uint32_t off[PASSES];
+    u32x4 res[PASSES][2];
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const int row = m0 + wm * WTM + 32 * i + p * RPP + lane / CPR;
+      off[p] = (row < M && col < N) ? static_cast<uint32_t>(row * N + col) * ob : OOB;
+      if (has_r) {  // every residual load of the block row in flight at once
+        res[p][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rR, off[p], 0, 0));
         if (ob == 4)
-          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), rC, off, 0, 0);
-        else
-          __builtin_amdgcn_raw_buffer_store_b16(
-              e.out_dtype == DT_BF16 ? narrow_bf16(v) : narrow_f16(v), rC, off, 0, 0);
+          res[p][1] = __builtin_bit_cast(
+              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rR, off[p] + 16u, 0, 0));
       }
     }
+#pragma unroll
+    for (int p = 0; p < PASSES; ++p) {
+      const float* src = stg + (p * RPP + lane / CPR) * EP + 8 * q;
+      const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
+      const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
+      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      if (ob == 4) {
+        if (has_r)
+#pragma unroll
+          for (int t = 0; t < 8; ++t) v[t] += __uint_as_float(res[p][t >> 2][t & 3]);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                     __float_as_uint(v[2]), __float_as_uint(v[3])},
+                                               rC, off[p], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]),
+                                                     __float_as_uint(v[6]), __float_as_uint(v[7])},
+                                               rC, off[p] + 16u, 0, 0);
+      } else {
+        const bool bf = e.out_dtype == DT_BF16;
+        uint32_t w[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float x0 = v[2 * t], x1 = v[2 * t + 1];
+          if (has_r) {
+            const uint32_t rr = res[p][0][t];
+            const uint16_t r0 = static_cast<uint16_t>(rr & 0xffffu), r1 = static_cast<uint16_t>(rr >> 16);
+            x0 += bf ? widen(bf16_t{}, r0) : widen(f16_t{}, r0);
+            x1 += bf ? widen(bf16_t{}, r1) : widen(f16_t{}, r1);
+          }
+          const uint16_t h0 = bf ? narrow_bf16(x0) : narrow_f16(x0);
+          const uint16_t h1 = bf ? narrow_bf16(x1) : narrow_f16(x1);
+          w[t] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, rC, off[p], 0, 0);
+      }
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next block row
   }
 }
 

@@ -35,7 +35,7 @@
  *  - Errors are negative gemm_status codes; the creating calls return NULL and
  *    record the code for gemm_last_error(). No call aborts the process.
  *  - Thread safety: plans are immutable after creation and may be run from
- *    several host threads. A plan whose description says "split" owns a device
+ *    several host threads. A plan whose description has split > 1 owns a device
  *    workspace; two runs of such a plan must not overlap in time (use one plan
  *    per stream).
  */
@@ -87,7 +87,7 @@ typedef struct gemm_plan gemm_plan;
  * Create a plan for C = epi(A x B) with A M x K and B K x N of type `dtype`.
  * Chooses the kernel configuration (shape-bucket rules, exact-shape cache) for
  * the device current on the calling thread. Host work only, except that a plan
- * whose configuration splits K allocates and zeroes its own device workspace.
+ * whose configuration splits K allocates its own device workspace.
  * Returns NULL on error (see gemm_last_error()).
  */
 gemm_plan* gemm_plan_create(int64_t M, int64_t N, int64_t K, int32_t dtype,

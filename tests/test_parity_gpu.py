@@ -7,6 +7,7 @@ match exactly; the fp32 4096^3 SGEMM must also stay within 1e-3 absolute
 """
 from __future__ import annotations
 
+import re
 import sys
 
 import numpy as np
@@ -52,9 +53,11 @@ def _dtype_of(name):
 
 
 CONFIGS = _configs()
+TILE_CONFIGS = [c for c in CONFIGS if not c.startswith("gemv")]
+GEMV_CONFIGS = [c for c in CONFIGS if c.startswith("gemv")]
 
 
-@pytest.mark.parametrize("name", CONFIGS)
+@pytest.mark.parametrize("name", TILE_CONFIGS)
 def test_each_config_ragged(g, name):
     """Every compiled configuration on shapes spanning several tiles with ragged tails."""
     dtype = _dtype_of(name)
@@ -82,6 +85,69 @@ def test_each_config_ragged(g, name):
             assert r["ok"], (name, M, N, K, kind, r)
 
 
+def _describe(plan):
+    return dict(kv.split("=", 1) for kv in plan.describe().split())
+
+
+@pytest.mark.parametrize("name", GEMV_CONFIGS)
+def test_gemv_config(g, name):
+    """Few-row split-K kernel: M from 1 to its row limit, N with a ragged last
+    strip of 128 columns, K from 1 to several K slices (split 1 and split > 1).
+    Every plan runs twice: the second run reuses the plan's workspace."""
+    dtype = _dtype_of(name)
+    mr = int(re.search(r"_m(\d+)", name).group(1))
+    idx = g.config_index(name)
+    align = 4 if dtype == "f32" else 8
+    kmax = {1: 4096, 4: 1024, 8: 512}[mr]
+    cases = [(1, align, 1), (mr, 128 + 3 * align, 200), (max(1, mr - 1), 1000, 3 * kmax + 5),
+             (mr, 136, 40000 if mr == 1 else 9000)]
+    splits = set()
+    for si, (M, N, K) in enumerate(cases):
+        say(f"[{name}] M={M} N={N} K={K}")
+        plan = g.Plan(M, N, K, dtype, config=idx)
+        d = _describe(plan)
+        assert d["config"] == name
+        splits.add(int(d["split"]) > 1)
+        for kind in ("uniform", "int"):
+            A, B = gc.inputs(M, N, K, dtype, 2000 + 31 * si, kind)
+            for rep in range(2):
+                C = gc.run_gpu(plan, A, B)
+                r = gc.check_full(C, A, B, dtype, exact=(kind == "int"))
+                assert r["ok"], (name, M, N, K, kind, rep, d, r)
+    assert splits == {False, True}
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+def test_gemv_epilogue_and_batch(g, dtype):
+    """Few-row kernel with every epilogue stage and 16-bit output, then a
+    strided batch (batch items reuse the plan's workspace in stream order)."""
+    M, N, K = 3, 264, 2500
+    plan = g.Plan(M, N, K, dtype, bias=True, gelu=True, resid=True, scale=0.5,
+                  out_dtype="bf16")
+    d = _describe(plan)
+    say(f"[gemv-epi] {dtype} {plan.describe()}")
+    assert d["config"].startswith("gemv") and int(d["split"]) > 1
+    A, B = gc.inputs(M, N, K, dtype, 611)
+    bias = synth.normal(612, (N,), 0.5, "f32")
+    resid = synth.uniform(613, (M, N), "bf16")
+    C = gc.run_gpu(plan, A, B, bias, resid)
+    r = gc.check_full(C, A, B, dtype, "bf16", bias, resid, 0.5, True)
+    assert r["ok"], r
+
+    nb = 3
+    bplan = g.Plan(M, N, K, dtype, batch_hint=nb)
+    assert _describe(bplan)["config"].startswith("gemv")
+    As = torch.stack([gc.inputs(M, N, K, dtype, 620 + 2 * b)[0] for b in range(nb)])
+    Bs = torch.stack([gc.inputs(M, N, K, dtype, 620 + 2 * b)[1] for b in range(nb)])
+    dev = torch.device("cuda")
+    Cs = bplan.run_batched(As.to(dev), Bs.to(dev))
+    torch.cuda.synchronize()
+    Cs = Cs.cpu()
+    for b in range(nb):
+        r = gc.check_full(Cs[b], As[b], Bs[b], dtype)
+        assert r["ok"], (b, r)
+
+
 EPI_CASES = [
     dict(bias=True),
     dict(bias=True, gelu=True),
@@ -107,6 +173,29 @@ def test_epilogues(g, dtype, out_dtype, epi):
     C = gc.run_gpu(plan, A, B, bias, resid)
     r = gc.check_full(C, A, B, dtype, out_dtype, bias, resid, e.get("scale"), e.get("gelu", False))
     assert r["ok"], (dtype, out_dtype, e, plan.describe(), r)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gelu_accuracy(g, dtype):
+    """The device GELU against the oracle's exact-erf GELU: C = gelu(A x 1) with
+    K = 1 puts every value of A through the epilogue unchanged. The device uses a
+    published erfc approximation (relative error below 1.2e-7); the bound allows
+    1.5e-7 |v| plus four fp32 ulps of the result."""
+    import oracle
+    vals = np.concatenate([np.linspace(-12, 12, 4001), [0.0, 1e-30, -1e-30, 1e-6, -1e-6, 0.5,
+                                                       -0.5, 3.0, -3.0, 5.5, -5.5, 9.0, -9.0]])
+    M, N, K = len(vals), 8, 1
+    A = torch.tensor(vals, dtype=torch.float32).reshape(M, 1).to(gc.TORCH[dtype])
+    B = torch.ones(K, N, dtype=gc.TORCH[dtype])
+    plan = g.Plan(M, N, K, dtype, gelu=True)
+    say(f"[gelu] {dtype} {plan.describe()}")
+    C = gc.run_gpu(plan, A, B).double().numpy()
+    v = A.double().numpy()[:, 0]
+    ref = np.array([oracle.gelu(x) for x in v])
+    bound = 1.5e-7 * np.abs(v) + 4 * np.spacing(np.abs(ref).astype(np.float32)).astype(np.float64)
+    err = np.abs(C - ref[:, None])
+    worst = int(np.argmax((err - bound[:, None]).max(axis=1)))
+    assert (err <= bound[:, None]).all(), (v[worst], C[worst, 0], ref[worst], bound[worst])
 
 
 def test_workload_fp16_512(g):
