@@ -90,10 +90,16 @@ struct EffRow {
 const EffRow kEff[] = {
     // bf16 / fp16
     {"m16d_bf16_256x256x64_w4x2_a3_b4_r1", 1.00}, {"m16d_f16_256x256x64_w4x2_a3_b4_r1", 1.00},
-    {"m16d_bf16_256x256x64_w2x4_a3_b4_r1", 0.97}, {"m16d_f16_256x256x64_w2x4_a3_b4_r1", 0.97},
-    {"m16d_bf16_256x256x64_w2x4_a3_b4_r2", 0.82}, {"m16d_f16_256x256x64_w2x4_a3_b4_r2", 0.82},
-    {"m16d_bf16_256x128", 0.81}, {"m16d_f16_256x128", 0.81},
-    {"m16d_bf16_256x256x64_w2x2", 0.79}, {"m16d_f16_256x256x64_w2x2", 0.79},
+    {"m16d_bf16_256x256x64_w2x4_a3_b4_r1", 0.99}, {"m16d_f16_256x256x64_w2x4_a3_b4_r1", 0.99},
+    {"m16d_bf16_256x256x64_w2x4_a3_b4_r2", 0.96}, {"m16d_f16_256x256x64_w2x4_a3_b4_r2", 0.96},
+    {"m16d_bf16_128x256", 0.86}, {"m16d_f16_128x256", 0.86},
+    {"m16d_bf16_256x128x64_w2x2_a4_b4_r1", 0.82}, {"m16d_f16_256x128x64_w2x2_a4_b4_r1", 0.82},
+    {"m16d_bf16_256x128", 0.80}, {"m16d_f16_256x128", 0.80},
+    {"m16d_bf16_256x256x64_w2x2", 0.88}, {"m16d_f16_256x256x64_w2x2", 0.88},
+    {"m16d_bf16_128x128x64_w2x2_a3_b4_r1", 0.81}, {"m16d_f16_128x128x64_w2x2_a3_b4_r1", 0.81},
+    {"m16d_bf16_128x128x64_w2x2_a3", 0.79}, {"m16d_f16_128x128x64_w2x2_a3", 0.79},
+    {"m16d_bf16_128x128x64_w2x2_a4", 0.67}, {"m16d_f16_128x128x64_w2x2_a4", 0.67},
+    {"m16d_bf16_64x128", 0.62}, {"m16d_f16_64x128", 0.62},
     {"m16p_bf16_256x256x64_w2x2", 0.68}, {"m16p_f16_256x256x64_w2x2", 0.68},
     {"m16p_bf16_256x256x64_w2x4", 0.62}, {"m16p_f16_256x256x64_w2x4", 0.62},
     {"m16p_bf16_128x128", 0.48}, {"m16p_f16_128x128", 0.48},
@@ -109,6 +115,32 @@ const EffRow kEff[] = {
     {"f32_128x128_w2x2_scalar", 0.63}, {"f32_64x64_w2x2_scalar", 0.55},
     {"f32_128x128", 0.91}, {"f32_128x256", 0.88}, {"f32_256x128", 0.86},
     {"f32_64x64", 0.83}, {"f32_256x256", 0.51},
+};
+
+// Measured winners for the shapes of the standard workloads on MI355X (256 CUs,
+// 160 KB of LDS per workgroup) (DeepGEMM page, section 2.3: tuned parameters per
+// shape bucket). Matched exactly on the device, input class (16-bit or fp32),
+// M, N, K and batch; the cost model covers every other shape and device. The
+// name's "{t}" stands for the 16-bit type of the problem.
+struct TunedRow {
+  bool f32;
+  int64_t M, N, K, batch;
+  const char* config;
+};
+const TunedRow kTuned[] = {
+    {false, 4096, 4096, 4096, 1, "m16d_{t}_256x256x64_w4x2_a3_b4_r1"},
+    {false, 8192, 8192, 8192, 1, "m16d_{t}_256x256x64_w4x2_a3_b4_r1"},
+    {false, 2048, 2048, 2048, 1, "m16d_{t}_128x128x64_w2x2_a3_b4_r2"},
+    {false, 1024, 1024, 1024, 1, "m16d_{t}_64x128x64_w2x2_a4_b4_r2"},
+    {false, 512, 512, 512, 1, "m16d_{t}_64x128x64_w2x2_a4_b4_r2"},
+    {false, 8192, 3072, 768, 1, "m16d_{t}_128x256x64_w2x4_a3_b4_r1"},  // encoder FFN, first GEMM
+    {false, 8192, 768, 3072, 1, "m16d_{t}_128x256x64_w2x4_a3_b4_r1"},  // encoder FFN, second GEMM
+    {false, 512, 512, 64, 96, "m16d_{t}_128x128x64_w2x2_a3_b4_r1"},    // 96 heads of Q K^T
+    {true, 4096, 4096, 4096, 1, "f32d_256x256x16_w4x2_a3"},
+    {true, 8192, 8192, 8192, 1, "f32d_256x256x16_w4x2_a3"},
+    {true, 2048, 2048, 2048, 1, "f32d_128x128x16_w2x2_a3"},
+    {true, 1024, 1024, 1024, 1, "f32_64x64_w2x2"},
+    {true, 512, 512, 512, 1, "f32_64x64_w2x2"},
 };
 
 double cfg_efficiency(const KernelEntry& k) {
@@ -168,21 +200,45 @@ int64_t cfg_workgroups(const KernelEntry& k, int64_t M, int64_t N, int split, in
   return k.kind == KIND_GEMV ? tiles * split : tiles * batch;
 }
 
-// Modelled time (arbitrary units) of a configuration on a problem.
+// Throughput of one CU running c < occ workgroups of an occupancy-occ
+// configuration, relative to running occ of them (measured: one 128 x 128
+// workgroup alone reaches 0.63 of a pair's throughput).
+double concurrency_gain(int c, int occ) { return c >= occ ? 1.0 : 0.63; }
+
+// Modelled time (arbitrary units) of a configuration on a problem: the busiest
+// CU's tiles, run occ at a time at the configuration's relative efficiency,
+// plus a fixed per-tile cost (prologue, epilogue) that keeps tiny-K shapes honest.
 double cfg_cost(const KernelEntry& k, int64_t M, int64_t N, int64_t K, int64_t batch,
                 const gemm_device_desc& dev) {
   const int64_t tm = (M + k.bm - 1) / k.bm, tn = (N + k.bn - 1) / k.bn;
   const int64_t tiles = tm * tn * batch;
   const int occ = cfg_occupancy(k, dev);
-  const int64_t slots = static_cast<int64_t>(dev.cu_count) * occ;
-  const int64_t rounds = (tiles + slots - 1) / slots;
+  const int64_t per_cu = (tiles + dev.cu_count - 1) / dev.cu_count;  // busiest CU
   const int64_t kpad = ((K + k.bk - 1) / k.bk) * k.bk;
-  // one round: each CU runs `occ` tiles sharing its throughput
-  const double round_work = static_cast<double>(k.bm) * k.bn * kpad * occ;
-  double t = static_cast<double>(rounds) * round_work / cfg_efficiency(k);
-  // a fixed per-tile cost (prologue, epilogue) keeps tiny-K shapes honest
-  t += static_cast<double>(rounds) * occ * k.bm * k.bn * 64.0;
+  const double tile_work = static_cast<double>(k.bm) * k.bn * kpad;
+  double t = 0.0;
+  for (int64_t left = per_cu; left > 0; left -= occ) {
+    const int c = static_cast<int>(left < occ ? left : occ);
+    t += c * tile_work / (cfg_efficiency(k) * concurrency_gain(c, occ));
+  }
+  t += static_cast<double>(per_cu) * k.bm * k.bn * 64.0;
   return t;
+}
+
+int tuned_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dtype,
+                 int64_t batch) {
+  if (dev.cu_count != 256 || dev.lds_bytes < 163840) return -1;
+  const auto& all = registry().all;
+  for (const TunedRow& r : kTuned) {
+    if (r.f32 != (dtype == GEMM_F32) || r.M != M || r.N != N || r.K != K || r.batch != batch)
+      continue;
+    std::string name(r.config);
+    const size_t at = name.find("{t}");
+    if (at != std::string::npos) name.replace(at, 3, dtype == GEMM_BF16 ? "bf16" : "f16");
+    for (int i = 0; i < static_cast<int>(all.size()); ++i)
+      if (name == all[i].name) return i;
+  }
+  return -1;
 }
 
 int select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dtype,
@@ -218,6 +274,9 @@ int select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, 
     if (gemv < 0 || k.bm < all[gemv].bm) gemv = i;
   }
   if (gemv >= 0) return gemv;
+  const int tuned = tuned_config(dev, M, N, K, dtype, batch);
+  if (tuned >= 0 && cfg_fits(all[tuned], dtype, vec_a, vec_b, dev, M, N, K, epi.out_dtype))
+    return tuned;
   return best_for(vec_a, vec_b);
 }
 

@@ -457,7 +457,12 @@ hipError_t launch_m16d(const LaunchArgs& a, hipStream_t s) {
   G15_M16D(T, TN, 256, 256, 4, 2, 3, 4, 1),    \
   G15_M16D(T, TN, 256, 256, 2, 2, 3, 8, 2),    \
   G15_M16D(T, TN, 256, 128, 2, 2, 4, 4, 2),    \
-  G15_M16D(T, TN, 256, 128, 2, 2, 4, 4, 1)
+  G15_M16D(T, TN, 256, 128, 2, 2, 4, 4, 1),    \
+  G15_M16D(T, TN, 128, 256, 2, 4, 3, 4, 1),    \
+  G15_M16D(T, TN, 128, 128, 2, 2, 3, 4, 2),    \
+  G15_M16D(T, TN, 128, 128, 2, 2, 3, 4, 1),    \
+  G15_M16D(T, TN, 128, 128, 2, 2, 4, 4, 2),    \
+  G15_M16D(T, TN, 64, 128, 2, 2, 4, 4, 2)
 
 const KernelEntry kM16D[] = {
     G15_M16D_ALL(bf16_t, "bf16"),

@@ -129,6 +129,41 @@ def test_select_batch_hint_changes_tiles():
     assert many.workgroups >= 256
 
 
+TUNED = [
+    ((4096, 4096, 4096), 1, "bf16", "m16d_bf16_256x256x64_w4x2_a3_b4_r1"),
+    ((8192, 3072, 768), 1, "bf16", "m16d_bf16_128x256x64_w2x4_a3_b4_r1"),
+    ((8192, 768, 3072), 1, "bf16", "m16d_bf16_128x256x64_w2x4_a3_b4_r1"),
+    ((512, 512, 64), 96, "bf16", "m16d_bf16_128x128x64_w2x2_a3_b4_r1"),
+    ((512, 512, 512), 1, "f16", "m16d_f16_64x128x64_w2x2_a4_b4_r2"),
+    ((4096, 4096, 4096), 1, "f32", "f32d_256x256x16_w4x2_a3"),
+]
+
+
+@pytest.mark.parametrize("shape,batch,dtype,name", TUNED)
+def test_select_uses_tuned_shapes(shape, batch, dtype, name):
+    """Workload shapes take their measured configuration, on the device they were
+    measured on; the same shape on a smaller device goes to the cost model."""
+    ch = g.select(*shape, dtype, batch_hint=batch, **MI355X)
+    assert g.config_names()[ch.config] == name
+    small = g.select(*shape, dtype, batch_hint=batch, cu_count=80, lds_bytes=65536)
+    assert small.lds_bytes <= 65536
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("M", [1, 3, 8])
+def test_select_few_rows_split_k(dtype, M):
+    """M <= 8 takes the split-K few-row kernel with the fewest rows covering M,
+    enough workgroups to fill the device and at most its K rows per workgroup."""
+    ch = g.select(M, 4096, 4096, dtype, **MI355X)
+    name = g.config_names()[ch.config]
+    mr = 1 if M == 1 else (4 if M <= 4 else 8)
+    assert name == f"gemv_{dtype}_m{mr}"
+    assert ch.split > 1 and ch.workgroups >= MI355X["cu_count"]
+    assert (4096 + ch.split - 1) // ch.split <= ch.bk
+    # a ninth row leaves the few-row kernel
+    assert not g.config_names()[g.select(9, 4096, 4096, dtype, **MI355X).config].startswith("gemv")
+
+
 def test_exact_shape_cache_hit():
     h0, m0, e0 = g.cache_stats()
     g.select(777, 555, 333, "bf16", **MI355X)
