@@ -52,7 +52,7 @@ class Choice(ctypes.Structure):
     _fields_ = [("config", ctypes.c_int32), ("kind", ctypes.c_int32), ("bm", ctypes.c_int32),
                 ("bn", ctypes.c_int32), ("bk", ctypes.c_int32), ("threads", ctypes.c_int32),
                 ("lds_bytes", ctypes.c_int32), ("split", ctypes.c_int32),
-                ("workgroups", ctypes.c_int64)]
+                ("workgroups", ctypes.c_int64), ("packed", ctypes.c_int32)]
 
 
 # Every symbol include/gemm15.h declares, with its ctypes signature.

@@ -37,6 +37,11 @@ struct gemm_plan {
   void* workspace;
   int64_t workspace_bytes;
   int split;
+  int packed;       // bit 0: A rows padded into pack_a; bit 1: B rows into pack_b
+  int64_t lda_p;    // padded row lengths (elements) of pack_a and pack_b
+  int64_t ldb_p;
+  void* pack_a;
+  void* pack_b;
 };
 
 namespace {
@@ -241,43 +246,77 @@ int tuned_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, i
   return -1;
 }
 
-int select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dtype,
-                  const gemm_epilogue& epi, int64_t batch, bool aligned16, int* fallback) {
+// A configuration choice: the primary configuration, the one taken when the
+// pointers are not 16-byte aligned, and which operands go through padded copies.
+struct Selection {
+  int config = -1;
+  int fallback = -1;
+  int packed = 0;
+};
+
+int64_t round_up8(int64_t x) { return (x + 7) / 8 * 8; }
+
+bool is_m16d(const KernelEntry& k) { return std::strncmp(k.name, "m16d_", 5) == 0; }
+
+Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dtype,
+                        const gemm_epilogue& epi, int64_t batch, bool aligned16) {
   const auto& all = registry().all;
   const int es = elem_bytes(dtype);
   const bool vec_a = aligned16 && (K * es) % 16 == 0;
   const bool vec_b = aligned16 && (N * es) % 16 == 0;
-  auto best_for = [&](bool va, bool vb) {
+  // best configuration by the cost model on problem (M, N, K) (ld dims kp, np
+  // for the fit of 32-bit offsets), among those `use` accepts
+  auto best_for = [&](bool va, bool vb, int64_t kp, int64_t np, auto use, double* cost) {
     int best = -1;
     double best_cost = 0;
     for (int i = 0; i < static_cast<int>(all.size()); ++i) {
       const KernelEntry& k = all[i];
-      if (k.kind == KIND_GEMV) continue;
-      if (!cfg_fits(k, dtype, va, vb, dev, M, N, K, epi.out_dtype)) continue;
+      if (k.kind == KIND_GEMV || !use(k)) continue;
+      if (!cfg_fits(k, dtype, va, vb, dev, M, np, kp, epi.out_dtype)) continue;
       const double c = cfg_cost(k, M, N, K, batch, dev);
       if (best < 0 || c < best_cost * 0.999) {
         best = i;
         best_cost = c;
       }
     }
+    if (cost) *cost = best_cost;
     return best;
   };
-  *fallback = best_for(false, false);
+  auto any = [](const KernelEntry&) { return true; };
+  Selection s;
+  s.fallback = best_for(false, false, K, N, any, nullptr);
   // A few rows (M <= 8): the product is a stream over B, served by the
   // split-K few-row kernel with the fewest rows that covers M (DeepGEMM page,
   // section 4.3: small shapes get their own small-block kernel).
-  int gemv = -1;
   for (int i = 0; i < static_cast<int>(all.size()); ++i) {
     const KernelEntry& k = all[i];
     if (k.kind != KIND_GEMV || !cfg_fits(k, dtype, vec_a, vec_b, dev, M, N, K, epi.out_dtype))
       continue;
-    if (gemv < 0 || k.bm < all[gemv].bm) gemv = i;
+    if (s.config < 0 || k.bm < all[s.config].bm) s.config = i;
   }
-  if (gemv >= 0) return gemv;
+  if (s.config >= 0) return s;
   const int tuned = tuned_config(dev, M, N, K, dtype, batch);
-  if (tuned >= 0 && cfg_fits(all[tuned], dtype, vec_a, vec_b, dev, M, N, K, epi.out_dtype))
-    return tuned;
-  return best_for(vec_a, vec_b);
+  if (tuned >= 0 && cfg_fits(all[tuned], dtype, vec_a, vec_b, dev, M, N, K, epi.out_dtype)) {
+    s.config = tuned;
+    return s;
+  }
+  double cost = 0;
+  s.config = best_for(vec_a, vec_b, K, N, any, &cost);
+  // 16-bit rows that are not 16-byte multiples: rather than a scalar-load kernel,
+  // copy the offending operand into zero-padded rows (plan workspace) and run a
+  // 16-byte-load kernel, when the product is big enough to repay the copy.
+  const bool pa = (K * es) % 16 != 0, pb = (N * es) % 16 != 0;
+  if (dtype != GEMM_F32 && aligned16 && (pa || pb) && M > 8 &&
+      static_cast<double>(M) * N * K >= double(1 << 20)) {
+    double pcost = 0;
+    const int pk = best_for(true, true, pa ? round_up8(K) : K, pb ? round_up8(N) : N,
+                            is_m16d, &pcost);
+    if (pk >= 0 && (s.config < 0 || pcost < cost)) {
+      s.config = pk;
+      s.packed = (pa ? 1 : 0) | (pb ? 2 : 0);
+    }
+  }
+  return s;
 }
 
 struct CacheKey {
@@ -291,7 +330,7 @@ struct CacheKey {
 
 struct Cache {
   std::mutex mu;
-  std::map<CacheKey, std::pair<int, int>> map;
+  std::map<CacheKey, Selection> map;
   int64_t hits = 0, misses = 0;
 };
 
@@ -310,8 +349,8 @@ int forced_config() {
 }
 
 // Cached choice for (shape, types, device facts).
-int choose(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dtype,
-           const gemm_epilogue& epi, int64_t batch, bool aligned16, int* fallback) {
+Selection choose(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dtype,
+                 const gemm_epilogue& epi, int64_t batch, bool aligned16) {
   CacheKey key{M, N, K, batch, dtype, static_cast<int>(epi.flags), epi.out_dtype,
                aligned16 ? 1 : 0, dev.cu_count, dev.lds_bytes};
   Cache& c = cache();
@@ -320,17 +359,14 @@ int choose(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dty
     auto it = c.map.find(key);
     if (it != c.map.end()) {
       ++c.hits;
-      *fallback = it->second.second;
-      return it->second.first;
+      return it->second;
     }
   }
-  int fb = -1;
-  const int cfg = select_config(dev, M, N, K, dtype, epi, batch, aligned16, &fb);
+  const Selection sel = select_config(dev, M, N, K, dtype, epi, batch, aligned16);
   std::lock_guard<std::mutex> lk(c.mu);
   ++c.misses;
-  c.map[key] = {cfg, fb};
-  *fallback = fb;
-  return cfg;
+  c.map[key] = sel;
+  return sel;
 }
 
 int check_problem(int64_t M, int64_t N, int64_t K, int32_t dtype, const gemm_epilogue& e,
@@ -373,6 +409,50 @@ gemm_plan* fail(int code) {
 
 bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// One batch item at a time: copy the unaligned operand(s) into the plan's
+// padded buffers, then run the 16-byte-load kernel with the padded row strides.
+int run_packed(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, const void* B,
+               int64_t sB, const float* bias, const void* resid, int64_t sR, void* C, int64_t sC,
+               bool c16, hipStream_t s) {
+  const KernelEntry& k = registry().all[p->config];
+  const int64_t ie = elem_bytes(p->dtype), oe = elem_bytes(p->epi.out_dtype);
+  for (int64_t z = 0; z < batch; ++z) {
+    const char* Az = static_cast<const char*>(A) + z * sA * ie;
+    const char* Bz = static_cast<const char*>(B) + z * sB * ie;
+    if ((p->packed & 1) && pack_rows16(Az, p->M, p->K, p->pack_a, p->lda_p, s) != hipSuccess)
+      return GEMM_ERR_HIP;
+    if ((p->packed & 2) && pack_rows16(Bz, p->K, p->N, p->pack_b, p->ldb_p, s) != hipSuccess)
+      return GEMM_ERR_HIP;
+    LaunchArgs la;
+    la.M = p->M;
+    la.N = p->N;
+    la.K = p->K;
+    la.batch = 1;
+    la.A = (p->packed & 1) ? p->pack_a : Az;
+    la.sA = 0;
+    la.B = (p->packed & 2) ? p->pack_b : Bz;
+    la.sB = 0;
+    la.C = static_cast<char*>(C) + z * sC * oe;
+    la.sC = 0;
+    la.sR = 0;
+    la.epi.flags = p->epi.flags;
+    la.epi.scale = p->epi.scale;
+    la.epi.bias = bias;
+    la.epi.resid = (p->epi.flags & GEMM_EPI_RESID) ? static_cast<const char*>(resid) + z * sR * oe
+                                                   : nullptr;
+    la.epi.out_dtype = p->epi.out_dtype;
+    la.workspace = nullptr;
+    la.workspace_bytes = 0;
+    la.split = 1;
+    la.lda = p->lda_p;
+    la.ldb = p->ldb_p;
+    la.ldc = p->N;
+    la.c_vec = (c16 && p->N % 8 == 0) ? 1 : 0;
+    if (k.launch(la, s) != hipSuccess) return GEMM_ERR_HIP;
+  }
+  return GEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -391,7 +471,7 @@ gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
   if (rc) return fail(rc);
 
   const auto& all = registry().all;
-  int cfg, fb;
+  Selection sel;
   const int forced = config >= 0 ? config : forced_config();
   if (forced == -2) return fail(GEMM_ERR_CONFIG);
   if (forced >= 0) {
@@ -400,15 +480,14 @@ gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
     const int es = elem_bytes(dtype);
     if (!cfg_fits(k, dtype, (K * es) % 16 == 0, (N * es) % 16 == 0, desc, M, N, K, epi.out_dtype))
       return fail(GEMM_ERR_CONFIG);
-    cfg = forced;
-    fb = forced;
-    if (k.vec_a || k.vec_b) {
-      int dummy;
-      fb = select_config(desc, M, N, K, dtype, epi, batch_hint, false, &dummy);
-    }
+    sel.config = forced;
+    sel.fallback = forced;
+    if (k.vec_a || k.vec_b)
+      sel.fallback = select_config(desc, M, N, K, dtype, epi, batch_hint, false).config;
   } else {
-    cfg = choose(desc, M, N, K, dtype, epi, batch_hint, true, &fb);
+    sel = choose(desc, M, N, K, dtype, epi, batch_hint, true);
   }
+  const int cfg = sel.config, fb = sel.fallback;
   if (cfg < 0 || fb < 0) return fail(GEMM_ERR_CONFIG);
 
   gemm_plan* p = new (std::nothrow) gemm_plan();
@@ -425,6 +504,23 @@ gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
   p->workspace = nullptr;
   p->workspace_bytes = 0;
   p->split = 1;
+  p->packed = sel.packed;
+  p->lda_p = (sel.packed & 1) ? round_up8(K) : K;
+  p->ldb_p = (sel.packed & 2) ? round_up8(N) : N;
+  p->pack_a = nullptr;
+  p->pack_b = nullptr;
+  if (sel.packed) {
+    const int64_t es = elem_bytes(dtype);
+    const bool ok =
+        (!(sel.packed & 1) || hipMalloc(&p->pack_a, static_cast<size_t>(M * p->lda_p * es)) == hipSuccess) &&
+        (!(sel.packed & 2) || hipMalloc(&p->pack_b, static_cast<size_t>(K * p->ldb_p * es)) == hipSuccess);
+    if (!ok) {
+      (void)hipGetLastError();
+      if (p->pack_a) (void)hipFree(p->pack_a);
+      delete p;
+      return fail(GEMM_ERR_NOMEM);
+    }
+  }
   const KernelEntry& k = all[cfg];
   if (k.kind == KIND_GEMV) {
     p->split = gemv_split(k, N, K, batch_hint, desc);
@@ -466,7 +562,16 @@ int gemm_run_strided_batched(const gemm_plan* p, int64_t batch, const void* A, i
                    (sA * ie) % 16 == 0 && (sB * ie) % 16 == 0 && (sC * oe) % 16 == 0 &&
                    (!(e.flags & GEMM_EPI_RESID) || (aligned_to(resid, 16) && (sR * oe) % 16 == 0));
   const auto& all = registry().all;
-  const KernelEntry& k = all[a16 ? p->config : p->fallback];
+  const bool c16 = aligned_to(C, 16) && (p->N * oe) % 16 == 0 && (sC * oe) % 16 == 0 &&
+                   (!(e.flags & GEMM_EPI_RESID) || (aligned_to(resid, 16) && (sR * oe) % 16 == 0));
+  if (p->packed) {
+    // operands that are not copied must still be 16-byte aligned for the kernel
+    const bool a_ok = (p->packed & 1) || (aligned_to(A, 16) && (sA * ie) % 16 == 0);
+    const bool b_ok = (p->packed & 2) || (aligned_to(B, 16) && (sB * ie) % 16 == 0);
+    if (a_ok && b_ok) return run_packed(p, batch, A, sA, B, sB, bias, resid, sR, C, sC, c16,
+                                        static_cast<hipStream_t>(stream));
+  }
+  const KernelEntry& k = all[a16 && !p->packed ? p->config : p->fallback];
 
   const int64_t tiles = ((p->M + k.bm - 1) / k.bm) * ((p->N + k.bn - 1) / k.bn);
   if (tiles > 0x7fffffff) return GEMM_ERR_SHAPE;
@@ -492,6 +597,10 @@ int gemm_run_strided_batched(const gemm_plan* p, int64_t batch, const void* A, i
   la.workspace = p->workspace;
   la.workspace_bytes = p->workspace_bytes;
   la.split = p->split;
+  la.lda = p->K;
+  la.ldb = p->N;
+  la.ldc = p->N;
+  la.c_vec = (a16 && p->N % 8 == 0) ? 1 : 0;
   const hipError_t err = k.launch(la, static_cast<hipStream_t>(stream));
   return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
@@ -505,6 +614,8 @@ int gemm_run(const gemm_plan* p, const void* A, const void* B, const float* bias
 void gemm_plan_destroy(gemm_plan* p) {
   if (!p) return;
   if (p->workspace) (void)hipFree(p->workspace);
+  if (p->pack_a) (void)hipFree(p->pack_a);
+  if (p->pack_b) (void)hipFree(p->pack_b);
   delete p;
 }
 
@@ -534,10 +645,11 @@ int gemm_plan_describe(const gemm_plan* p, char* buf, size_t len) {
   char tmp[256];
   const int n = std::snprintf(
       tmp, sizeof(tmp),
-      "config=%s id=%d tile=%dx%dx%d threads=%d lds=%d workgroups=%lld split=%d fallback=%s",
+      "config=%s id=%d tile=%dx%dx%d threads=%d lds=%d workgroups=%lld split=%d packed=%d "
+      "fallback=%s",
       k.name, p->config, k.bm, k.bn, k.bk, k.threads, k.lds_bytes,
       static_cast<long long>(cfg_workgroups(k, p->M, p->N, p->split, p->batch_hint)), p->split,
-      all[p->fallback].name);
+      p->packed, all[p->fallback].name);
   if (buf && len > 0) {
     std::strncpy(buf, tmp, len - 1);
     buf[len - 1] = '\0';
@@ -553,8 +665,8 @@ int gemm_select(const gemm_device_desc* dev, int64_t M, int64_t N, int64_t K, in
   const gemm_epilogue epi = norm_epi(epi_in);
   const int rc = check_problem(M, N, K, dtype, epi, batch_hint);
   if (rc) return rc;
-  int fb;
-  const int cfg = choose(*dev, M, N, K, dtype, epi, batch_hint, aligned16 != 0, &fb);
+  const Selection sel = choose(*dev, M, N, K, dtype, epi, batch_hint, aligned16 != 0);
+  const int cfg = sel.config;
   if (cfg < 0) return GEMM_ERR_CONFIG;
   const KernelEntry& k = registry().all[cfg];
   out->config = cfg;
@@ -566,6 +678,7 @@ int gemm_select(const gemm_device_desc* dev, int64_t M, int64_t N, int64_t K, in
   out->lds_bytes = k.lds_bytes;
   out->split = k.kind == KIND_GEMV ? gemv_split(k, N, K, batch_hint, *dev) : 1;
   out->workgroups = cfg_workgroups(k, M, N, out->split, batch_hint);
+  out->packed = sel.packed;
   return GEMM_OK;
 }
 

@@ -121,6 +121,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16d_kernel(LaunchArgs a)
   const int wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), K = static_cast<int>(a.K);
+  const int LDA = static_cast<int>(a.lda), LDB = static_cast<int>(a.ldb),
+            LDC = static_cast<int>(a.ldc);
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -148,10 +150,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16d_kernel(LaunchArgs a)
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
     const int gm = m0 + (wave * AI + i) * 8 + a_lrow;
-    a_voff[i] = gm < M ? static_cast<uint32_t>(gm * K + a_chunk * 8) * 2u : OOB;
+    a_voff[i] = gm < M ? static_cast<uint32_t>(gm * LDA + a_chunk * 8) * 2u : OOB;
   }
   auto issue_a = [&](int k0, int stage) {
-    const int64_t left = static_cast<int64_t>(M) * K - k0;
+    const int64_t left = static_cast<int64_t>(M) * LDA - k0;
     const auto r = rsrc(Abase + k0, static_cast<uint32_t>(left > 0 ? left * 2 : 0));
     const bool kin = k0 + a_chunk * 8 < K;  // k past K inside a row would read the next row
 #pragma unroll
@@ -188,11 +190,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16d_kernel(LaunchArgs a)
     const int gn = n0 + nb * 8;
 #pragma unroll
     for (int r = 0; r < KR; ++r)
-      b_voff[i][r] = gn < N ? static_cast<uint32_t>((kr0 + r) * N + gn) * 2u : OOB;
+      b_voff[i][r] = gn < N ? static_cast<uint32_t>((kr0 + r) * LDB + gn) * 2u : OOB;
   }
   auto issue_b = [&](int k0, int set) {
-    const int64_t left = static_cast<int64_t>(K - k0) * N;
-    const auto r = rsrc(Bbase + static_cast<int64_t>(k0) * N,
+    const int64_t left = static_cast<int64_t>(K - k0) * LDB;
+    const auto r = rsrc(Bbase + static_cast<int64_t>(k0) * LDB,
                         static_cast<uint32_t>(left > 0 ? left * 2 : 0));
 #pragma unroll
     for (int i = 0; i < NB; ++i)
@@ -342,9 +344,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16d_kernel(LaunchArgs a)
   // and GELU are applied there (the bias is one value per lane and block column),
   // then each 32-row block row of the wave's sub-tile goes through the wave's own
   // LDS area and comes back as 8 consecutive columns per lane: residual loads and
-  // C stores move 16 or 32 contiguous bytes per lane. Columns come in whole
-  // chunks of 8 (N is a multiple of 8 for this kernel), so a chunk is all inside
-  // or all outside the matrix.
+  // C stores move 16 or 32 contiguous bytes per lane. That needs c_vec: N a
+  // multiple of 8 (a chunk of 8 columns is all inside or all outside the matrix)
+  // and 16-byte aligned rows; otherwise each lane moves single elements.
   wait_vm<0>();
   lds_barrier();  // every wave is done with the operand ring; LDS is free
   constexpr int EP = WTN + 8;  // floats per staged row: rows 4 apart land 32 banks apart
@@ -357,12 +359,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16d_kernel(LaunchArgs a)
 
   const Epi& e = a.epi;
   const int ob = e.out_dtype == DT_F32 ? 4 : 2;
-  const auto rC = rsrc(static_cast<char*>(a.C) + z * a.sC * ob,
-                       static_cast<uint32_t>(static_cast<int64_t>(M) * N * ob));
+  char* Cz = static_cast<char*>(a.C) + z * a.sC * ob;
   const bool has_r = (e.flags & EPI_RESID) != 0;
-  const auto rR = rsrc(has_r ? static_cast<const char*>(e.resid) + z * a.sR * ob
-                             : static_cast<const char*>(a.C),
-                       static_cast<uint32_t>(static_cast<int64_t>(M) * N * ob));
+  const char* Rz = has_r ? static_cast<const char*>(e.resid) + z * a.sR * ob : Cz;
+  const auto rC = rsrc(Cz, static_cast<uint32_t>(static_cast<int64_t>(M) * LDC * ob));
+  const auto rR = rsrc(Rz, static_cast<uint32_t>(static_cast<int64_t>(M) * LDC * ob));
   float bj[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
@@ -385,12 +386,32 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16d_kernel(LaunchArgs a)
       }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's staging writes are done
 
+    if (!a.c_vec) {
+      // C rows not 16-byte aligned: the lanes take consecutive columns of one row
+      // and move one element each (coalesced, no vector access)
+      for (int rr = 0; rr < 32; ++rr) {
+        const int row = m0 + wm * WTM + 32 * i + rr;
+#pragma unroll
+        for (int cc = lane; cc < WTN; cc += 64) {
+          const int cl = n0 + wn * WTN + cc;
+          if (row < M && cl < N) {
+            const int64_t idx = static_cast<int64_t>(row) * LDC + cl;
+            float v = stg[rr * EP + cc];
+            if (has_r) v += load_out_elem(Rz, e.out_dtype, idx);
+            store_out_elem(Cz, e.out_dtype, idx, v);
+          }
+        }
+      }
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      continue;
+    }
+
     uint32_t off[PASSES];
     u32x4 res[PASSES][2];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int row = m0 + wm * WTM + 32 * i + p * RPP + lane / CPR;
-      off[p] = (row < M && col < N) ? static_cast<uint32_t>(row * N + col) * ob : OOB;
+      off[p] = (row < M && col < N) ? static_cast<uint32_t>(row * LDC + col) * ob : OOB;
       if (has_r) {  // every residual load of the block row in flight at once
         res[p][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rR, off[p], 0, 0));
         if (ob == 4)

@@ -1,0 +1,46 @@
+// kernel_pack.hip -- copy a 16-bit matrix into rows padded to a multiple of 8
+// elements (16 bytes) with zeros, so that the 16-byte-load kernels can take
+// operands whose rows are not 16-byte multiples (K or N not a multiple of 8).
+// The padding adds zero products only: A's extra columns meet B rows past K,
+// which the kernels read as zeros, and B's extra columns produce C columns
+// past N, which are never stored.
+#include "kernels.hpp"
+
+namespace g15 {
+namespace {
+
+// Thread t of the grid fills 8 consecutive destination elements of one row.
+__global__ __launch_bounds__(256) void pack16_kernel(const uint16_t* __restrict__ src, int64_t rows,
+                                                     int64_t cols, uint16_t* __restrict__ dst,
+                                                     int64_t ld_dst) {
+  const int64_t chunks = ld_dst / 8;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= rows * chunks) return;
+  const int64_t r = t / chunks, c0 = (t - r * chunks) * 8;
+  const uint16_t* s = src + r * cols;
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t c = c0 + 2 * j;
+    const uint32_t lo = c < cols ? s[c] : 0u;
+    const uint32_t hi = c + 1 < cols ? s[c + 1] : 0u;
+    w[j] = lo | (hi << 16);
+  }
+  *reinterpret_cast<u32x4*>(dst + r * ld_dst + c0) = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+}  // namespace
+
+hipError_t pack_rows16(const void* src, int64_t rows, int64_t cols, void* dst, int64_t ld_dst,
+                       hipStream_t s) {
+  if (rows < 1 || cols < 1 || ld_dst < cols || ld_dst % 8 != 0) return hipErrorInvalidValue;
+  const int64_t threads = rows * (ld_dst / 8);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(src), rows, cols, static_cast<uint16_t*>(dst),
+                     ld_dst);
+  return hipGetLastError();
+}
+
+}  // namespace g15

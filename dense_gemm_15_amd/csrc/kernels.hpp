@@ -28,10 +28,19 @@ struct LaunchArgs {
   int64_t sC;
   int64_t sR;  // residual batch stride (elements of out_dtype)
   Epi epi;
-  void* workspace;      // split-K partials + counters (GEMV kind only)
+  void* workspace;      // split-K partials (GEMV kind only)
   int64_t workspace_bytes;
   int split;            // split-K factor (GEMV kind only)
+  // Row strides in elements. Every kernel handles lda = K, ldb = N, ldc = N;
+  // only the m16d kernels take other strides (operands packed into padded rows).
+  int64_t lda, ldb, ldc;
+  int c_vec;            // 1: C (and resid) rows and base are 16-byte aligned (m16d reads it)
 };
+
+// Copy a rows x cols matrix of 16-bit elements (row stride cols) into rows of
+// ld_dst >= cols elements, zero-filling columns cols .. ld_dst-1.
+hipError_t pack_rows16(const void* src, int64_t rows, int64_t cols, void* dst, int64_t ld_dst,
+                       hipStream_t s);
 
 typedef hipError_t (*LaunchFn)(const LaunchArgs&, hipStream_t);
 

@@ -35,9 +35,9 @@
  *  - Errors are negative gemm_status codes; the creating calls return NULL and
  *    record the code for gemm_last_error(). No call aborts the process.
  *  - Thread safety: plans are immutable after creation and may be run from
- *    several host threads. A plan whose description has split > 1 owns a device
- *    workspace; two runs of such a plan must not overlap in time (use one plan
- *    per stream).
+ *    several host threads. A plan whose description has split > 1 or packed > 0
+ *    owns a device workspace; two runs of such a plan must not overlap in time
+ *    (use one plan per stream).
  */
 #ifndef GEMM15_H
 #define GEMM15_H
@@ -87,7 +87,9 @@ typedef struct gemm_plan gemm_plan;
  * Create a plan for C = epi(A x B) with A M x K and B K x N of type `dtype`.
  * Chooses the kernel configuration (shape-bucket rules, exact-shape cache) for
  * the device current on the calling thread. Host work only, except that a plan
- * whose configuration splits K allocates its own device workspace.
+ * whose configuration splits K, or that copies 16-bit operands whose rows are not
+ * 16-byte multiples (K or N not a multiple of 8) into zero-padded rows, allocates
+ * its own device workspace (freed by gemm_plan_destroy).
  * Returns NULL on error (see gemm_last_error()).
  */
 gemm_plan* gemm_plan_create(int64_t M, int64_t N, int64_t K, int32_t dtype,
@@ -167,6 +169,7 @@ typedef struct gemm_choice {
   int32_t lds_bytes;
   int32_t split;     /* K split factor (1 = none) */
   int64_t workgroups;
+  int32_t packed;    /* bit 0: A, bit 1: B copied into 16-byte-padded rows before the kernel */
 } gemm_choice;
 
 /*

@@ -100,9 +100,17 @@ def test_select_fits_budget_and_type(dtype, shape):
     assert dtype in name
     es = 4 if dtype == "f32" else 2
     M, N, K = shape
-    if (K * es) % 16 or (N * es) % 16:
-        # rows that are not 16-byte multiples never take a 16-byte-load kernel
-        assert "scalar" in name or name.startswith("simple")
+    pa, pb = (K * es) % 16 != 0, (N * es) % 16 != 0
+    if pa or pb:
+        # rows that are not 16-byte multiples take a scalar-load kernel, or (16-bit
+        # inputs) a 16-byte-load kernel on copies of exactly those operands in padded rows
+        if ch.packed:
+            assert dtype != "f32" and name.startswith("m16d")
+            assert ch.packed == (1 if pa else 0) | (2 if pb else 0)
+        else:
+            assert "scalar" in name or name.startswith("simple")
+    else:
+        assert ch.packed == 0
 
 
 def test_select_small_lds_device():

@@ -300,6 +300,63 @@ def test_workload_odd_shapes(g, name):
     assert r["ok"], r
 
 
+PACKED_CASES = [
+    # (M, N, K, dtype, out_dtype, epilogue, expected packed bits)
+    (300, 264, 203, "bf16", "f32", dict(), 1),                        # A rows unaligned
+    (300, 261, 200, "f16", "f32", dict(), 2),                         # B (and C) rows unaligned
+    (517, 1003, 77, "bf16", "bf16", dict(bias=True, resid=True), 3),  # both, 16-bit C, residual
+    (257, 777, 130, "f16", "f16", dict(bias=True, gelu=True), 3),
+]
+
+
+@pytest.mark.parametrize("case", range(len(PACKED_CASES)))
+def test_packed_operands(g, case):
+    """16-bit operands whose rows are not 16-byte multiples are copied into
+    zero-padded rows and run through a 16-byte-load kernel; C rows that are not
+    16-byte multiples are stored element by element. Every element, float and
+    small-integer inputs, two runs of the same plan."""
+    M, N, K, dtype, out_dtype, epi, bits = PACKED_CASES[case]
+    plan = g.Plan(M, N, K, dtype, out_dtype=out_dtype, **epi)
+    d = _describe(plan)
+    say(f"[packed] {plan.describe()}")
+    assert int(d["packed"]) == bits and d["config"].startswith("m16d")
+    for kind in ("uniform", "int"):
+        A, B = gc.inputs(M, N, K, dtype, 700 + case, kind)
+        bias = synth.normal(710 + case, (N,), 0.5, "f32") if epi.get("bias") else None
+        resid = synth.uniform(720 + case, (M, N), out_dtype) if epi.get("resid") else None
+        for rep in range(2):
+            C = gc.run_gpu(plan, A, B, bias, resid)
+            # integer inputs are exact only without the non-integer epilogue terms
+            r = gc.check_full(C, A, B, dtype, out_dtype, bias, resid, None, epi.get("gelu", False),
+                              exact=(kind == "int" and not epi))
+            assert r["ok"], (kind, rep, plan.describe(), r)
+
+
+def test_packed_batched_and_misaligned(g):
+    """A strided batch through the padded copies (one item at a time), and an
+    operand that is not copied but starts off a 16-byte boundary: the plan then
+    takes its scalar fallback."""
+    M, N, K, nb = 200, 136, 77, 3
+    plan = g.Plan(M, N, K, "bf16", batch_hint=nb)
+    assert int(_describe(plan)["packed"]) == 1
+    As = torch.stack([gc.inputs(M, N, K, "bf16", 730 + 2 * b)[0] for b in range(nb)])
+    Bs = torch.stack([gc.inputs(M, N, K, "bf16", 730 + 2 * b)[1] for b in range(nb)])
+    dev = torch.device("cuda")
+    Cs = plan.run_batched(As.to(dev), Bs.to(dev))
+    torch.cuda.synchronize()
+    for b in range(nb):
+        r = gc.check_full(Cs[b].cpu(), As[b], Bs[b], "bf16")
+        assert r["ok"], (b, r)
+    # B (rows aligned, not copied) one element past a 16-byte boundary
+    A, B = As[0], Bs[0]
+    Bbuf = torch.empty(K * N + 1, dtype=torch.bfloat16, device=dev)
+    Bbuf[1:] = B.reshape(-1).to(dev)
+    C = plan.run(A.to(dev), Bbuf[1:].view(K, N))
+    torch.cuda.synchronize()
+    r = gc.check_full(C.cpu(), A, B, "bf16")
+    assert r["ok"], r
+
+
 def test_repeat_shape_hits_cache(g):
     """A repeated shape is served from the exact-shape cache."""
     h0, m0, _ = g.cache_stats()
