@@ -22,6 +22,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libgemm15.so")
 
 F32, F16, BF16 = 0, 1, 2
+B_LAYOUT = {"kn": 0, "nk": 1}
 EPI_BIAS, EPI_GELU, EPI_RESID, EPI_SCALE = 1, 2, 4, 8
 _CODE = {"f32": F32, "f16": F16, "bf16": BF16}
 _TORCH = {F32: torch.float32, F16: torch.float16, BF16: torch.bfloat16}
@@ -60,6 +61,8 @@ _I64, _I32, _VP = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
 SIGNATURES = {
     "gemm_plan_create": (_VP, [_I64, _I64, _I64, _I32, ctypes.POINTER(Epilogue)]),
     "gemm_plan_create_ex": (_VP, [_I64, _I64, _I64, _I32, ctypes.POINTER(Epilogue), _I64, _I32]),
+    "gemm_plan_create_layout": (_VP, [_I64, _I64, _I64, _I32, ctypes.POINTER(Epilogue), _I64, _I32,
+                                      _I32]),
     "gemm_run": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "gemm_run_strided_batched": (ctypes.c_int, [_VP, _I64, _VP, _I64, _VP, _I64, _VP, _VP, _I64,
                                                 _VP, _I64, _VP]),
@@ -69,6 +72,9 @@ SIGNATURES = {
     "gemm_plan_describe": (ctypes.c_int, [_VP, ctypes.c_char_p, ctypes.c_size_t]),
     "gemm_select": (ctypes.c_int, [ctypes.POINTER(DeviceDesc), _I64, _I64, _I64, _I32,
                                    ctypes.POINTER(Epilogue), _I64, _I32, ctypes.POINTER(Choice)]),
+    "gemm_select_layout": (ctypes.c_int, [ctypes.POINTER(DeviceDesc), _I64, _I64, _I64, _I32,
+                                          ctypes.POINTER(Epilogue), _I64, _I32, _I32,
+                                          ctypes.POINTER(Choice)]),
     "gemm_config_count": (ctypes.c_int, []),
     "gemm_config_name": (ctypes.c_char_p, [_I32]),
     "gemm_cache_stats": (None, [ctypes.POINTER(ctypes.c_int64)] * 3),
@@ -119,12 +125,13 @@ def _epi(bias=False, gelu=False, resid=False, scale=None, out_dtype="f32") -> Ep
 
 
 def select(M, N, K, dtype, *, cu_count=256, lds_bytes=163840, batch_hint=1, aligned16=True,
-           **epi) -> Choice:
+           b_layout="kn", **epi) -> Choice:
     """Configuration the library would choose on a described device (no GPU needed)."""
     ch = Choice()
     e = _epi(**epi)
-    rc = lib.gemm_select(ctypes.byref(DeviceDesc(cu_count, lds_bytes)), M, N, K, _CODE[dtype],
-                         ctypes.byref(e), batch_hint, int(bool(aligned16)), ctypes.byref(ch))
+    rc = lib.gemm_select_layout(ctypes.byref(DeviceDesc(cu_count, lds_bytes)), M, N, K,
+                                _CODE[dtype], ctypes.byref(e), batch_hint, int(bool(aligned16)),
+                                B_LAYOUT[b_layout], ctypes.byref(ch))
     if rc != 0:
         raise GemmError(rc, "gemm_select")
     return ch
@@ -135,20 +142,25 @@ def _ptr(t):
 
 
 class Plan:
-    """A plan for C = epi(A x B); wraps gemm_plan_create_ex / gemm_run."""
+    """A plan for C = epi(A x B); wraps gemm_plan_create_layout / gemm_run.
+
+    b_layout="kn": B is [K, N]; b_layout="nk": the B passed to run() is Bt [N, K]
+    and C = epi(A Bt^T)."""
 
     def __init__(self, M: int, N: int, K: int, dtype: str, *, bias: bool = False,
                  gelu: bool = False, resid: bool = False, scale: float | None = None,
-                 out_dtype: str = "f32", batch_hint: int = 1, config: int | str = -1):
+                 out_dtype: str = "f32", batch_hint: int = 1, config: int | str = -1,
+                 b_layout: str = "kn"):
         if isinstance(config, str):
             config = config_index(config)
         self.M, self.N, self.K = M, N, K
         self.dtype, self.out_dtype = dtype, out_dtype
+        self.b_layout = b_layout
         self.flags = _epi(bias, gelu, resid, scale, out_dtype)
-        self._h = lib.gemm_plan_create_ex(M, N, K, _CODE[dtype], ctypes.byref(self.flags),
-                                          batch_hint, config)
+        self._h = lib.gemm_plan_create_layout(M, N, K, _CODE[dtype], ctypes.byref(self.flags),
+                                              batch_hint, config, B_LAYOUT[b_layout])
         if not self._h:
-            raise GemmError(lib.gemm_last_error(), "gemm_plan_create_ex")
+            raise GemmError(lib.gemm_last_error(), "gemm_plan_create_layout")
 
     def __del__(self):
         h = getattr(self, "_h", None)
@@ -183,7 +195,7 @@ class Plan:
         """C = epi(A x B) on the current (or given) stream; returns C."""
         M, N, K = self.M, self.N, self.K
         self._check(A, (M, K), self.dtype, "A")
-        self._check(B, (K, N), self.dtype, "B")
+        self._check(B, (K, N) if self.b_layout == "kn" else (N, K), self.dtype, "B")
         if out is None:
             out = torch.empty((M, N), dtype=_TORCH[_CODE[self.out_dtype]], device=A.device)
         self._check(out, (M, N), self.out_dtype, "C")
@@ -202,7 +214,7 @@ class Plan:
         M, N, K = self.M, self.N, self.K
         nb = A.shape[0]
         self._check(A, (nb, M, K), self.dtype, "A")
-        self._check(B, (nb, K, N), self.dtype, "B")
+        self._check(B, (nb, K, N) if self.b_layout == "kn" else (nb, N, K), self.dtype, "B")
         if out is None:
             out = torch.empty((nb, M, N), dtype=_TORCH[_CODE[self.out_dtype]], device=A.device)
         self._check(out, (nb, M, N), self.out_dtype, "C")

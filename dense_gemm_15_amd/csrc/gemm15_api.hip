@@ -37,6 +37,7 @@ struct gemm_plan {
   void* workspace;
   int64_t workspace_bytes;
   int split;
+  int b_nk;         // 1: B is given transposed, Bt [N x K] row-major
   int packed;       // bit 0: A rows padded into pack_a; bit 1: B rows into pack_b
   int64_t lda_p;    // padded row lengths (elements) of pack_a and pack_b
   int64_t ldb_p;
@@ -59,6 +60,8 @@ struct Registry {
     n = mfma16_pipe_entries(&p);
     all.insert(all.end(), p, p + n);
     n = mfma16_dlds_entries(&p);
+    all.insert(all.end(), p, p + n);
+    n = mfma16_nt_entries(&p);
     all.insert(all.end(), p, p + n);
     n = f32_entries(&p);
     all.insert(all.end(), p, p + n);
@@ -105,6 +108,13 @@ const EffRow kEff[] = {
     {"m16d_bf16_128x128x64_w2x2_a3", 0.79}, {"m16d_f16_128x128x64_w2x2_a3", 0.79},
     {"m16d_bf16_128x128x64_w2x2_a4", 0.67}, {"m16d_f16_128x128x64_w2x2_a4", 0.67},
     {"m16d_bf16_64x128", 0.62}, {"m16d_f16_64x128", 0.62},
+    {"m16n_bf16_256x256x64_w4x2", 1.04}, {"m16n_f16_256x256x64_w4x2", 1.04},
+    {"m16n_bf16_256x256x64_w2x4", 1.02}, {"m16n_f16_256x256x64_w2x4", 1.02},
+    {"m16n_bf16_128x256", 0.92}, {"m16n_f16_128x256", 0.92},
+    {"m16n_bf16_256x128", 0.86}, {"m16n_f16_256x128", 0.86},
+    {"m16n_bf16_128x128x64_w2x2_a2_b2", 0.86}, {"m16n_f16_128x128x64_w2x2_a2_b2", 0.86},
+    {"m16n_bf16_128x128x64_w2x2_a3_b3", 0.85}, {"m16n_f16_128x128x64_w2x2_a3_b3", 0.85},
+    {"m16n_bf16_64x128", 0.66}, {"m16n_f16_64x128", 0.66},
     {"m16p_bf16_256x256x64_w2x2", 0.68}, {"m16p_f16_256x256x64_w2x2", 0.68},
     {"m16p_bf16_256x256x64_w2x4", 0.62}, {"m16p_f16_256x256x64_w2x4", 0.62},
     {"m16p_bf16_128x128", 0.48}, {"m16p_f16_128x128", 0.48},
@@ -130,7 +140,7 @@ const EffRow kEff[] = {
 struct TunedRow {
   bool f32;
   int64_t M, N, K, batch;
-  const char* config;
+  const char* config;  // an "m16n" configuration answers problems with a transposed B
 };
 const TunedRow kTuned[] = {
     {false, 4096, 4096, 4096, 1, "m16d_{t}_256x256x64_w4x2_a3_b4_r1"},
@@ -141,6 +151,11 @@ const TunedRow kTuned[] = {
     {false, 8192, 3072, 768, 1, "m16d_{t}_128x256x64_w2x4_a3_b4_r1"},  // encoder FFN, first GEMM
     {false, 8192, 768, 3072, 1, "m16d_{t}_128x256x64_w2x4_a3_b4_r1"},  // encoder FFN, second GEMM
     {false, 512, 512, 64, 96, "m16d_{t}_128x128x64_w2x2_a3_b4_r1"},    // 96 heads of Q K^T
+    {false, 4096, 4096, 4096, 1, "m16n_{t}_256x256x64_w4x2_a3_b2"},
+    {false, 2048, 2048, 2048, 1, "m16n_{t}_128x128x64_w2x2_a3_b3"},
+    {false, 8192, 3072, 768, 1, "m16n_{t}_256x256x64_w4x2_a3_b2"},
+    {false, 8192, 768, 3072, 1, "m16n_{t}_128x256x64_w2x4_a3_b3"},
+    {false, 512, 512, 64, 96, "m16n_{t}_128x128x64_w2x2_a2_b2"},
     {true, 4096, 4096, 4096, 1, "f32d_256x256x16_w4x2_a3"},
     {true, 8192, 8192, 8192, 1, "f32d_256x256x16_w4x2_a3"},
     {true, 2048, 2048, 2048, 1, "f32d_128x128x16_w2x2_a3"},
@@ -165,8 +180,9 @@ int cfg_occupancy(const KernelEntry& k, const gemm_device_desc& dev) {
 }
 
 bool cfg_fits(const KernelEntry& k, int dtype, bool vec_a, bool vec_b, const gemm_device_desc& dev,
-              int64_t M, int64_t N, int64_t K, int out_dtype) {
+              int64_t M, int64_t N, int64_t K, int out_dtype, bool b_nk = false) {
   if (k.in_dtype != -1 && k.in_dtype != dtype) return false;
+  if ((k.b_nk != 0) != b_nk) return false;
   if (k.buf32) {
     const int64_t lim = int64_t(1) << 31;
     const int64_t es = elem_bytes(dtype), oe = elem_bytes(out_dtype);
@@ -231,12 +247,13 @@ double cfg_cost(const KernelEntry& k, int64_t M, int64_t N, int64_t K, int64_t b
 }
 
 int tuned_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dtype,
-                 int64_t batch) {
+                 int64_t batch, bool b_nk) {
   if (dev.cu_count != 256 || dev.lds_bytes < 163840) return -1;
   const auto& all = registry().all;
   for (const TunedRow& r : kTuned) {
     if (r.f32 != (dtype == GEMM_F32) || r.M != M || r.N != N || r.K != K || r.batch != batch)
       continue;
+    if ((std::strncmp(r.config, "m16n_", 5) == 0) != b_nk) continue;
     std::string name(r.config);
     const size_t at = name.find("{t}");
     if (at != std::string::npos) name.replace(at, 3, dtype == GEMM_BF16 ? "bf16" : "f16");
@@ -259,11 +276,11 @@ int64_t round_up8(int64_t x) { return (x + 7) / 8 * 8; }
 bool is_m16d(const KernelEntry& k) { return std::strncmp(k.name, "m16d_", 5) == 0; }
 
 Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dtype,
-                        const gemm_epilogue& epi, int64_t batch, bool aligned16) {
+                        const gemm_epilogue& epi, int64_t batch, bool aligned16, bool b_nk) {
   const auto& all = registry().all;
   const int es = elem_bytes(dtype);
   const bool vec_a = aligned16 && (K * es) % 16 == 0;
-  const bool vec_b = aligned16 && (N * es) % 16 == 0;
+  const bool vec_b = aligned16 && ((b_nk ? K : N) * es) % 16 == 0;
   // best configuration by the cost model on problem (M, N, K) (ld dims kp, np
   // for the fit of 32-bit offsets), among those `use` accepts
   auto best_for = [&](bool va, bool vb, int64_t kp, int64_t np, auto use, double* cost) {
@@ -272,7 +289,7 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
     for (int i = 0; i < static_cast<int>(all.size()); ++i) {
       const KernelEntry& k = all[i];
       if (k.kind == KIND_GEMV || !use(k)) continue;
-      if (!cfg_fits(k, dtype, va, vb, dev, M, np, kp, epi.out_dtype)) continue;
+      if (!cfg_fits(k, dtype, va, vb, dev, M, np, kp, epi.out_dtype, b_nk)) continue;
       const double c = cfg_cost(k, M, N, K, batch, dev);
       if (best < 0 || c < best_cost * 0.999) {
         best = i;
@@ -288,15 +305,15 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
   // A few rows (M <= 8): the product is a stream over B, served by the
   // split-K few-row kernel with the fewest rows that covers M (DeepGEMM page,
   // section 4.3: small shapes get their own small-block kernel).
-  for (int i = 0; i < static_cast<int>(all.size()); ++i) {
+  for (int i = 0; i < static_cast<int>(all.size()) && !b_nk; ++i) {
     const KernelEntry& k = all[i];
     if (k.kind != KIND_GEMV || !cfg_fits(k, dtype, vec_a, vec_b, dev, M, N, K, epi.out_dtype))
       continue;
     if (s.config < 0 || k.bm < all[s.config].bm) s.config = i;
   }
   if (s.config >= 0) return s;
-  const int tuned = tuned_config(dev, M, N, K, dtype, batch);
-  if (tuned >= 0 && cfg_fits(all[tuned], dtype, vec_a, vec_b, dev, M, N, K, epi.out_dtype)) {
+  const int tuned = tuned_config(dev, M, N, K, dtype, batch, b_nk);
+  if (tuned >= 0 && cfg_fits(all[tuned], dtype, vec_a, vec_b, dev, M, N, K, epi.out_dtype, b_nk)) {
     s.config = tuned;
     return s;
   }
@@ -304,13 +321,14 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
   s.config = best_for(vec_a, vec_b, K, N, any, &cost);
   // 16-bit rows that are not 16-byte multiples: rather than a scalar-load kernel,
   // copy the offending operand into zero-padded rows (plan workspace) and run a
-  // 16-byte-load kernel, when the product is big enough to repay the copy.
-  const bool pa = (K * es) % 16 != 0, pb = (N * es) % 16 != 0;
-  if (dtype != GEMM_F32 && aligned16 && (pa || pb) && M > 8 &&
-      static_cast<double>(M) * N * K >= double(1 << 20)) {
+  // 16-byte-load kernel, when the product is big enough to repay the copy (always
+  // for a transposed B, which has no scalar-load kernel).
+  const bool pa = (K * es) % 16 != 0, pb = ((b_nk ? K : N) * es) % 16 != 0;
+  if (dtype != GEMM_F32 && aligned16 && (pa || pb) &&
+      (b_nk || (M > 8 && static_cast<double>(M) * N * K >= double(1 << 20)))) {
     double pcost = 0;
-    const int pk = best_for(true, true, pa ? round_up8(K) : K, pb ? round_up8(N) : N,
-                            is_m16d, &pcost);
+    const int pk = best_for(true, true, pa ? round_up8(K) : K, (pb && !b_nk) ? round_up8(N) : N,
+                            [&](const KernelEntry& k) { return b_nk || is_m16d(k); }, &pcost);
     if (pk >= 0 && (s.config < 0 || pcost < cost)) {
       s.config = pk;
       s.packed = (pa ? 1 : 0) | (pb ? 2 : 0);
@@ -321,10 +339,11 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
 
 struct CacheKey {
   int64_t M, N, K, batch;
-  int dtype, flags, out_dtype, aligned, cu, lds;
+  int dtype, flags, out_dtype, aligned, cu, lds, b_nk;
   bool operator<(const CacheKey& o) const {
-    return std::tie(M, N, K, batch, dtype, flags, out_dtype, aligned, cu, lds) <
-           std::tie(o.M, o.N, o.K, o.batch, o.dtype, o.flags, o.out_dtype, o.aligned, o.cu, o.lds);
+    return std::tie(M, N, K, batch, dtype, flags, out_dtype, aligned, cu, lds, b_nk) <
+           std::tie(o.M, o.N, o.K, o.batch, o.dtype, o.flags, o.out_dtype, o.aligned, o.cu, o.lds,
+                    o.b_nk);
   }
 };
 
@@ -350,9 +369,9 @@ int forced_config() {
 
 // Cached choice for (shape, types, device facts).
 Selection choose(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dtype,
-                 const gemm_epilogue& epi, int64_t batch, bool aligned16) {
+                 const gemm_epilogue& epi, int64_t batch, bool aligned16, bool b_nk) {
   CacheKey key{M, N, K, batch, dtype, static_cast<int>(epi.flags), epi.out_dtype,
-               aligned16 ? 1 : 0, dev.cu_count, dev.lds_bytes};
+               aligned16 ? 1 : 0, dev.cu_count, dev.lds_bytes, b_nk ? 1 : 0};
   Cache& c = cache();
   {
     std::lock_guard<std::mutex> lk(c.mu);
@@ -362,7 +381,7 @@ Selection choose(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, i
       return it->second;
     }
   }
-  const Selection sel = select_config(dev, M, N, K, dtype, epi, batch, aligned16);
+  const Selection sel = select_config(dev, M, N, K, dtype, epi, batch, aligned16, b_nk);
   std::lock_guard<std::mutex> lk(c.mu);
   ++c.misses;
   c.map[key] = sel;
@@ -421,7 +440,8 @@ int run_packed(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, con
     const char* Bz = static_cast<const char*>(B) + z * sB * ie;
     if ((p->packed & 1) && pack_rows16(Az, p->M, p->K, p->pack_a, p->lda_p, s) != hipSuccess)
       return GEMM_ERR_HIP;
-    if ((p->packed & 2) && pack_rows16(Bz, p->K, p->N, p->pack_b, p->ldb_p, s) != hipSuccess)
+    if ((p->packed & 2) && pack_rows16(Bz, p->b_nk ? p->N : p->K, p->b_nk ? p->K : p->N, p->pack_b,
+                                       p->ldb_p, s) != hipSuccess)
       return GEMM_ERR_HIP;
     LaunchArgs la;
     la.M = p->M;
@@ -445,7 +465,7 @@ int run_packed(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, con
     la.workspace_bytes = 0;
     la.split = 1;
     la.lda = p->lda_p;
-    la.ldb = p->ldb_p;
+    la.ldb = p->ldb_p;  // padded, or the unpadded row length
     la.ldc = p->N;
     la.c_vec = (c16 && p->N % 8 == 0) ? 1 : 0;
     if (k.launch(la, s) != hipSuccess) return GEMM_ERR_HIP;
@@ -457,11 +477,15 @@ int run_packed(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, con
 
 extern "C" {
 
-gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
-                               const gemm_epilogue* epi_in, int64_t batch_hint, int32_t config) {
+gemm_plan* gemm_plan_create_layout(int64_t M, int64_t N, int64_t K, int32_t dtype,
+                                   const gemm_epilogue* epi_in, int64_t batch_hint, int32_t config,
+                                   int32_t b_layout) {
   const gemm_epilogue epi = norm_epi(epi_in);
   int rc = check_problem(M, N, K, dtype, epi, batch_hint);
   if (rc) return fail(rc);
+  if (b_layout != GEMM_B_KN && b_layout != GEMM_B_NK) return fail(GEMM_ERR_ARG);
+  const bool b_nk = b_layout == GEMM_B_NK;
+  if (b_nk && dtype == GEMM_F32) return fail(GEMM_ERR_DTYPE);
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(GEMM_ERR_NO_DEVICE);
   int dev = 0;
@@ -478,17 +502,19 @@ gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
     if (forced >= static_cast<int>(all.size())) return fail(GEMM_ERR_CONFIG);
     const KernelEntry& k = all[forced];
     const int es = elem_bytes(dtype);
-    if (!cfg_fits(k, dtype, (K * es) % 16 == 0, (N * es) % 16 == 0, desc, M, N, K, epi.out_dtype))
+    if (!cfg_fits(k, dtype, (K * es) % 16 == 0, ((b_nk ? K : N) * es) % 16 == 0, desc, M, N, K,
+                  epi.out_dtype, b_nk))
       return fail(GEMM_ERR_CONFIG);
     sel.config = forced;
     sel.fallback = forced;
     if (k.vec_a || k.vec_b)
-      sel.fallback = select_config(desc, M, N, K, dtype, epi, batch_hint, false).config;
+      sel.fallback = select_config(desc, M, N, K, dtype, epi, batch_hint, false, b_nk).config;
   } else {
-    sel = choose(desc, M, N, K, dtype, epi, batch_hint, true);
+    sel = choose(desc, M, N, K, dtype, epi, batch_hint, true, b_nk);
   }
   const int cfg = sel.config, fb = sel.fallback;
-  if (cfg < 0 || fb < 0) return fail(GEMM_ERR_CONFIG);
+  // a transposed B has no scalar-load kernel: unaligned pointers are an error at run time
+  if (cfg < 0 || (fb < 0 && !b_nk)) return fail(GEMM_ERR_CONFIG);
 
   gemm_plan* p = new (std::nothrow) gemm_plan();
   if (!p) return fail(GEMM_ERR_NOMEM);
@@ -504,16 +530,18 @@ gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
   p->workspace = nullptr;
   p->workspace_bytes = 0;
   p->split = 1;
+  p->b_nk = b_nk ? 1 : 0;
   p->packed = sel.packed;
   p->lda_p = (sel.packed & 1) ? round_up8(K) : K;
-  p->ldb_p = (sel.packed & 2) ? round_up8(N) : N;
+  p->ldb_p = b_nk ? ((sel.packed & 2) ? round_up8(K) : K) : ((sel.packed & 2) ? round_up8(N) : N);
   p->pack_a = nullptr;
   p->pack_b = nullptr;
   if (sel.packed) {
     const int64_t es = elem_bytes(dtype);
     const bool ok =
         (!(sel.packed & 1) || hipMalloc(&p->pack_a, static_cast<size_t>(M * p->lda_p * es)) == hipSuccess) &&
-        (!(sel.packed & 2) || hipMalloc(&p->pack_b, static_cast<size_t>(K * p->ldb_p * es)) == hipSuccess);
+        (!(sel.packed & 2) ||
+         hipMalloc(&p->pack_b, static_cast<size_t>((b_nk ? N : K) * p->ldb_p * es)) == hipSuccess);
     if (!ok) {
       (void)hipGetLastError();
       if (p->pack_a) (void)hipFree(p->pack_a);
@@ -535,9 +563,14 @@ gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
   return p;
 }
 
+gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
+                               const gemm_epilogue* epi, int64_t batch_hint, int32_t config) {
+  return gemm_plan_create_layout(M, N, K, dtype, epi, batch_hint, config, GEMM_B_KN);
+}
+
 gemm_plan* gemm_plan_create(int64_t M, int64_t N, int64_t K, int32_t dtype,
                             const gemm_epilogue* epi) {
-  return gemm_plan_create_ex(M, N, K, dtype, epi, 1, -1);
+  return gemm_plan_create_layout(M, N, K, dtype, epi, 1, -1, GEMM_B_KN);
 }
 
 int gemm_run_strided_batched(const gemm_plan* p, int64_t batch, const void* A, int64_t sA,
@@ -571,7 +604,9 @@ int gemm_run_strided_batched(const gemm_plan* p, int64_t batch, const void* A, i
     if (a_ok && b_ok) return run_packed(p, batch, A, sA, B, sB, bias, resid, sR, C, sC, c16,
                                         static_cast<hipStream_t>(stream));
   }
-  const KernelEntry& k = all[a16 && !p->packed ? p->config : p->fallback];
+  const int ci = a16 && !p->packed ? p->config : p->fallback;
+  if (ci < 0) return GEMM_ERR_ALIGN;  // transposed B: 16-byte aligned operands required
+  const KernelEntry& k = all[ci];
 
   const int64_t tiles = ((p->M + k.bm - 1) / k.bm) * ((p->N + k.bn - 1) / k.bn);
   if (tiles > 0x7fffffff) return GEMM_ERR_SHAPE;
@@ -598,7 +633,7 @@ int gemm_run_strided_batched(const gemm_plan* p, int64_t batch, const void* A, i
   la.workspace_bytes = p->workspace_bytes;
   la.split = p->split;
   la.lda = p->K;
-  la.ldb = p->N;
+  la.ldb = p->b_nk ? p->K : p->N;
   la.ldc = p->N;
   la.c_vec = (a16 && p->N % 8 == 0) ? 1 : 0;
   const hipError_t err = k.launch(la, static_cast<hipStream_t>(stream));
@@ -646,10 +681,10 @@ int gemm_plan_describe(const gemm_plan* p, char* buf, size_t len) {
   const int n = std::snprintf(
       tmp, sizeof(tmp),
       "config=%s id=%d tile=%dx%dx%d threads=%d lds=%d workgroups=%lld split=%d packed=%d "
-      "fallback=%s",
+      "b=%s fallback=%s",
       k.name, p->config, k.bm, k.bn, k.bk, k.threads, k.lds_bytes,
       static_cast<long long>(cfg_workgroups(k, p->M, p->N, p->split, p->batch_hint)), p->split,
-      p->packed, all[p->fallback].name);
+      p->packed, p->b_nk ? "nk" : "kn", p->fallback >= 0 ? all[p->fallback].name : "none");
   if (buf && len > 0) {
     std::strncpy(buf, tmp, len - 1);
     buf[len - 1] = '\0';
@@ -657,15 +692,18 @@ int gemm_plan_describe(const gemm_plan* p, char* buf, size_t len) {
   return n;
 }
 
-int gemm_select(const gemm_device_desc* dev, int64_t M, int64_t N, int64_t K, int32_t dtype,
-                const gemm_epilogue* epi_in, int64_t batch_hint, int32_t aligned16,
-                gemm_choice* out) {
+int gemm_select_layout(const gemm_device_desc* dev, int64_t M, int64_t N, int64_t K,
+                       int32_t dtype, const gemm_epilogue* epi_in, int64_t batch_hint,
+                       int32_t aligned16, int32_t b_layout, gemm_choice* out) {
   if (!dev || !out) return GEMM_ERR_NULL;
+  if (b_layout != GEMM_B_KN && b_layout != GEMM_B_NK) return GEMM_ERR_ARG;
+  const bool b_nk = b_layout == GEMM_B_NK;
+  if (b_nk && dtype == GEMM_F32) return GEMM_ERR_DTYPE;
   if (dev->cu_count < 1 || dev->lds_bytes < 1) return GEMM_ERR_ARG;
   const gemm_epilogue epi = norm_epi(epi_in);
   const int rc = check_problem(M, N, K, dtype, epi, batch_hint);
   if (rc) return rc;
-  const Selection sel = choose(*dev, M, N, K, dtype, epi, batch_hint, aligned16 != 0);
+  const Selection sel = choose(*dev, M, N, K, dtype, epi, batch_hint, aligned16 != 0, b_nk);
   const int cfg = sel.config;
   if (cfg < 0) return GEMM_ERR_CONFIG;
   const KernelEntry& k = registry().all[cfg];
@@ -680,6 +718,12 @@ int gemm_select(const gemm_device_desc* dev, int64_t M, int64_t N, int64_t K, in
   out->workgroups = cfg_workgroups(k, M, N, out->split, batch_hint);
   out->packed = sel.packed;
   return GEMM_OK;
+}
+
+int gemm_select(const gemm_device_desc* dev, int64_t M, int64_t N, int64_t K, int32_t dtype,
+                const gemm_epilogue* epi, int64_t batch_hint, int32_t aligned16,
+                gemm_choice* out) {
+  return gemm_select_layout(dev, M, N, K, dtype, epi, batch_hint, aligned16, GEMM_B_KN, out);
 }
 
 int gemm_config_count(void) { return static_cast<int>(registry().all.size()); }

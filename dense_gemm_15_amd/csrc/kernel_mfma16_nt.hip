@@ -1,0 +1,235 @@
+// kernel_mfma16_nt.hip -- bf16 / fp16 matrix-core GEMM with the right operand
+// given transposed: C = epi(A x Bt^T), A [M x K] and Bt [N x K] row-major (a
+// linear layer's weight in [out, in] order, or K of attention scores Q K^T).
+//
+// Same tiling and schedule as kernel_mfma16_dlds.hip (DeepGEMM page, sections
+// 2.2 and 3.1; prefetch of the SGEMM page, section 2.3), but both operands now
+// arrive k-contiguous, which is what the matrix core reads: Bt slices go global
+// -> LDS directly (buffer_load ... lds) exactly like A, into their own ring, and
+// B fragments are read like A fragments. No register staging, no transpose, no
+// LDS stores in the main loop.
+//
+// LDS: an A ring of SA slices and a B ring of SB slices (BM x 128 and BN x 128
+// bytes per slice). With SB = SA - 1 (the 256 x 256 tile, whose rings would not
+// fit otherwise) B is fetched one slice ahead, A two; the B loads of a slice are
+// issued before its A loads so the wait at the slice boundary can leave the
+// newest A loads in flight.
+#include "m16_common.hpp"
+
+namespace g15 {
+namespace {
+
+template <typename T, int BM, int BN, int WGM, int WGN, int SA, int SB>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a) {
+  constexpr int BK = 64;
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int AI = BM / 8 / NW;  // direct A loads per wave per slice (8 rows each)
+  constexpr int BI = BN / 8 / NW;  // direct B loads per wave per slice
+  constexpr int A_STAGE = BM * 8;  // 16-byte chunks per A slice
+  constexpr int B_STAGE = BN * 8;
+  static_assert(BM % (8 * NW) == 0 && AI >= 1, "A rows must split evenly over the waves");
+  static_assert(BN % (8 * NW) == 0 && BI >= 1, "B rows must split evenly over the waves");
+  static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 block");
+  static_assert(SB >= 2 && (SA == SB || SA == SB + 1), "rings: SA = SB or SA = SB + 1");
+  static_assert(BK / 16 == 4, "the K loop below is written for four k-steps per slice");
+  constexpr int RING = SA * A_STAGE + SB * B_STAGE;
+  constexpr int STG = (NW * 32 * (WTN + 8) * 4 + 15) / 16;  // epilogue staging, 16-byte units
+  __shared__ u32x4 lds[RING > STG ? RING : STG];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  // wave index as a scalar: LDS slot addresses derived from it stay in SGPRs
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), K = static_cast<int>(a.K);
+  const int LDA = static_cast<int>(a.lda), LDB = static_cast<int>(a.ldb);
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  int tm, tn;
+  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int64_t z = blockIdx.y;
+
+  // 16-byte chunk c of an LDS row sits at c ^ (row & 7) ^ ((row >> 3) & 3) in both
+  // rings (conflict-free fragment reads). Instruction i of a wave fills 8 rows
+  // r0 .. r0+7 (lane l -> slot r0*8 + l), so lane l fetches logical chunk
+  // (l & 7) ^ (l >> 3) ^ ((r0 >> 3) & 3) of row r0 + (l >> 3).
+  const uint16_t* Abase = static_cast<const uint16_t*>(a.A) + z * a.sA;
+  const uint16_t* Bbase = static_cast<const uint16_t*>(a.B) + z * a.sB;
+  int a_chk[AI], b_chk[BI];
+  uint32_t a_voff[AI], b_voff[BI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    a_chk[i] = (lane & 7) ^ (lane >> 3) ^ ((wave * AI + i) & 3);
+    const int gm = m0 + (wave * AI + i) * 8 + (lane >> 3);
+    a_voff[i] = gm < M ? static_cast<uint32_t>(gm * LDA + a_chk[i] * 8) * 2u : OOB;
+  }
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    b_chk[i] = (lane & 7) ^ (lane >> 3) ^ ((wave * BI + i) & 3);
+    const int gn = n0 + (wave * BI + i) * 8 + (lane >> 3);
+    b_voff[i] = gn < N ? static_cast<uint32_t>(gn * LDB + b_chk[i] * 8) * 2u : OOB;
+  }
+  // One operand's slice k0 into ring slot `slot`. TAIL: the slice may reach past K
+  // (chunks past K are masked and their slots zeroed, since an out-of-range
+  // direct load leaves its LDS slot untouched); otherwise the issue is branch-free.
+  auto issue = [&](const uint16_t* base, int rows, int ld, const uint32_t* voff,
+                   const int* chk, u32x4* ring, int per_wave, int k0, int slot, auto TailC,
+                   auto NC) {
+    constexpr bool TAIL = decltype(TailC)::value;
+    constexpr int NI = decltype(NC)::value;
+    const int64_t left = static_cast<int64_t>(rows) * ld - k0;
+    const auto r = rsrc(base + k0, static_cast<uint32_t>(left > 0 ? left * 2 : 0));
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const bool kin = !TAIL || k0 + chk[i] * 8 < K;  // k past K inside a row would read the next row
+      const uint32_t off = kin ? voff[i] : OOB;
+      u32x4* dst = ring + slot * (per_wave * NW * 64) + (wave * per_wave + i) * 64;
+      if (TAIL && !kin) dst[lane] = u32x4{0u, 0u, 0u, 0u};
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
+    }
+  };
+  u32x4* const ringA = lds;
+  u32x4* const ringB = lds + SA * A_STAGE;
+  auto issue_a = [&](int k0, int slot, auto TailC) {
+    issue(Abase, M, LDA, a_voff, a_chk, ringA, AI, k0, slot, TailC,
+          std::integral_constant<int, AI>{});
+  };
+  auto issue_b = [&](int k0, int slot, auto TailC) {
+    issue(Bbase, N, LDB, b_voff, b_chk, ringB, BI, k0, slot, TailC,
+          std::integral_constant<int, BI>{});
+  };
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int nk = (K + BK - 1) / BK;
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  // fragment rows: A row wm*WTM + 32 i + lrow, B row wn*WTN + 32 j + lrow; the
+  // chunk permutation depends on the row modulo 32 only
+  const int a_base = (wm * WTM + lrow) * 8, b_base = (wn * WTN + lrow) * 8;
+  const int perm = (lrow & 7) ^ ((lrow >> 3) & 3);
+  auto frags = [&](const u32x4* LA, const u32x4* LB, int s, u32x4 (&fa)[FM], u32x4 (&fb)[FN]) {
+    const int c = (2 * s + lhalf) ^ perm;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[i] = LA[a_base + i * 256 + c];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = LB[b_base + j * 256 + c];
+  };
+  auto mmas = [&](const u32x4 (&fa)[FM], const u32x4 (&fb)[FN], int i0, int i1) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      if (i < i0 || i >= i1) continue;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) acc[i][j] = mma<T>(fa[i], fb[j], acc[i][j]);
+    }
+  };
+
+  // Prologue: B slices 0 .. SB-2 and A slices 0 .. SA-2 (B of a slice before its A).
+  for (int s = 0; s < SA - 1; ++s) {
+    if (s < SB - 1) issue_b(s * BK, s, std::true_type{});
+    issue_a(s * BK, s, std::true_type{});
+  }
+  wait_vm<0>();
+  lds_barrier();
+  u32x4 f0a[FM], f0b[FN], f1a[FM], f1b[FN];
+  frags(ringA, ringB, 0, f0a, f0b);
+
+  // loads left in flight at a slice boundary: everything issued after B(kt+1)
+  constexpr int PER = AI + BI;
+  constexpr int WAITN = SA == SB ? PER * (SA - 2) : PER * (SB - 2) + AI;
+  constexpr int HALF = FM / 2;
+  int ca = 0, cb = 0;  // ring slots of A(kt), B(kt)
+  auto slice = [&](auto TailC, int kt) {
+    const int na = ca + 1 == SA ? 0 : ca + 1, nb = cb + 1 == SB ? 0 : cb + 1;
+    const int fa = ca == 0 ? SA - 1 : ca - 1;  // slot of A(kt-1), refilled with A(kt+SA-1)
+    const int fb = cb == 0 ? SB - 1 : cb - 1;  // slot of B(kt-1), refilled with B(kt+SB-1)
+    const u32x4* LA = ringA + ca * A_STAGE;
+    const u32x4* LB = ringB + cb * B_STAGE;
+
+    frags(LA, LB, 1, f1a, f1b);
+    mmas(f0a, f0b, 0, FM);
+    plan_slice<0, FM * FN, FM + FN, 0, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+
+    frags(LA, LB, 2, f0a, f0b);
+    issue_b((kt + SB - 1) * BK, fb, TailC);
+    issue_a((kt + SA - 1) * BK, fa, TailC);
+    mmas(f1a, f1b, 0, FM);
+    plan_slice<0, FM * FN, FM + FN, 0, PER>();
+    __builtin_amdgcn_sched_barrier(0);
+
+    frags(LA, LB, 3, f1a, f1b);
+    mmas(f0a, f0b, 0, FM);
+    plan_slice<0, FM * FN, FM + FN, 0, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+
+    mmas(f1a, f1b, 0, HALF);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vm<WAITN>();
+    lds_barrier();
+    frags(ringA + na * A_STAGE, ringB + nb * B_STAGE, 0, f0a, f0b);
+    mmas(f1a, f1b, HALF, FM);
+    plan_slice<0, (FM - HALF) * FN, FM + FN, 0, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    ca = na;
+    cb = nb;
+  };
+  // Slices whose issues (A(kt + SA - 1), B(kt + SB - 1)) lie wholly inside K run
+  // the branch-free issue; the last few take the masked one.
+  int kt = 0;
+  for (; kt < nk && (kt + SA) * BK <= K; ++kt) slice(std::false_type{}, kt);
+  for (; kt < nk; ++kt) slice(std::true_type{}, kt);
+
+  wait_vm<0>();
+  lds_barrier();  // every wave is done with the rings; LDS is free
+  store_tile<FM, FN, WTM, WTN, NW, static_cast<int>(sizeof(lds))>(
+      a, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, wave, lane, z);
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, int SA, int SB>
+hipError_t launch_m16n(const LaunchArgs& a, hipStream_t s) {
+  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
+  dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(a.batch));
+  hipLaunchKernelGGL((gemm_m16n_kernel<T, BM, BN, WGM, WGN, SA, SB>), grid, dim3(64 * WGM * WGN),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+#define G15_M16N(T, TN, BM, BN, WGM, WGN, SA, SB)                                                 \
+  {"m16n_" TN "_" #BM "x" #BN "x64_w" #WGM "x" #WGN "_a" #SA "_b" #SB, KIND_MFMA16, T::code, BM,   \
+   BN, 64, 64 * WGM * WGN,                                                                        \
+   static_cast<int>(sizeof(u32x4)) *                                                              \
+       ((SA * BM + SB * BN) * 8 > (WGM * WGN * 32 * (BN / WGN + 8) * 4 + 15) / 16                  \
+            ? (SA * BM + SB * BN) * 8                                                             \
+            : (WGM * WGN * 32 * (BN / WGN + 8) * 4 + 15) / 16),                                   \
+   1, 1, launch_m16n<T, BM, BN, WGM, WGN, SA, SB>, 1, 1}
+
+#define G15_M16N_ALL(T, TN)                     \
+  G15_M16N(T, TN, 256, 256, 4, 2, 3, 2),        \
+  G15_M16N(T, TN, 256, 256, 2, 4, 3, 2),        \
+  G15_M16N(T, TN, 256, 128, 2, 2, 3, 3),        \
+  G15_M16N(T, TN, 128, 256, 2, 4, 3, 3),        \
+  G15_M16N(T, TN, 128, 128, 2, 2, 3, 3),        \
+  G15_M16N(T, TN, 128, 128, 2, 2, 2, 2),        \
+  G15_M16N(T, TN, 64, 128, 2, 2, 4, 4)
+
+const KernelEntry kM16N[] = {
+    G15_M16N_ALL(bf16_t, "bf16"),
+    G15_M16N_ALL(f16_t, "f16"),
+};
+
+}  // namespace
+
+int mfma16_nt_entries(const KernelEntry** out) {
+  *out = kM16N;
+  return static_cast<int>(sizeof(kM16N) / sizeof(kM16N[0]));
+}
+
+}  // namespace g15

@@ -55,6 +55,7 @@ struct KernelEntry {
   int vec_b;      // 1: needs 16-byte aligned B rows
   LaunchFn launch;
   int buf32 = 0;  // 1: addresses A, B, C with 32-bit byte offsets (each must be < 2 GiB)
+  int b_nk = 0;   // 1: B is given transposed, Bt [N x K] row-major (row stride ldb)
 };
 
 // Each kernel file appends its instantiations.
@@ -62,6 +63,7 @@ int simple_entries(const KernelEntry** out);
 int mfma16_entries(const KernelEntry** out);
 int mfma16_pipe_entries(const KernelEntry** out);
 int mfma16_dlds_entries(const KernelEntry** out);
+int mfma16_nt_entries(const KernelEntry** out);
 int f32_entries(const KernelEntry** out);
 int f32_dlds_entries(const KernelEntry** out);
 int gemv_entries(const KernelEntry** out);

@@ -81,6 +81,13 @@ typedef enum gemm_status {
   GEMM_ERR_ARG = -10       /* another invalid argument (batch < 1, a bad stride, ...) */
 } gemm_status;
 
+/* Storage of the right operand B. */
+enum {
+  GEMM_B_KN = 0, /* B is K x N row-major (C = A B) */
+  GEMM_B_NK = 1  /* B is given transposed: Bt is N x K row-major, C = A Bt^T (a linear
+                    layer's weight in [out, in] order, or K of attention scores Q K^T) */
+};
+
 typedef struct gemm_plan gemm_plan;
 
 /*
@@ -107,9 +114,26 @@ gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
                                const gemm_epilogue* epi, int64_t batch_hint, int32_t config);
 
 /*
+ * As gemm_plan_create_ex, with the storage of B: GEMM_B_KN (B is K x N row-major,
+ * as for gemm_plan_create) or GEMM_B_NK (the B argument of gemm_run* is then Bt,
+ * N x K row-major, and the plan computes C = epi(A Bt^T)). This is the operand
+ * order of a linear layer whose weight is stored [out, in] (tutorial page,
+ * section 2: Y = X W^T + b) and of attention scores Q K^T with K stored [S x D],
+ * so no transposed copy is needed. With GEMM_B_NK both operands are K-contiguous,
+ * as the matrix core reads them, and both stream straight into LDS.
+ * GEMM_B_NK needs a 16-bit dtype (GEMM_ERR_DTYPE otherwise) and 16-byte aligned
+ * A, Bt and C base pointers and batch strides at run time (GEMM_ERR_ALIGN
+ * otherwise); when K is not a multiple of 8 the plan copies A and Bt into
+ * zero-padded rows before each run. GEMM_ERR_ARG for another b_layout.
+ */
+gemm_plan* gemm_plan_create_layout(int64_t M, int64_t N, int64_t K, int32_t dtype,
+                                   const gemm_epilogue* epi, int64_t batch_hint, int32_t config,
+                                   int32_t b_layout);
+
+/*
  * Enqueue C = epi(A x B) on `stream`.
  *  A      device, M x K row-major, plan dtype
- *  B      device, K x N row-major, plan dtype
+ *  B      device, K x N row-major, plan dtype (N x K row-major for a GEMM_B_NK plan)
  *  bias   device, N FP32 values; required iff GEMM_EPI_BIAS, else ignored
  *  resid  device, M x N row-major of out_dtype; required iff GEMM_EPI_RESID, else
  *         ignored. resid may equal C (each element is read before it is written).
@@ -181,6 +205,11 @@ typedef struct gemm_choice {
 int gemm_select(const gemm_device_desc* dev, int64_t M, int64_t N, int64_t K, int32_t dtype,
                 const gemm_epilogue* epi, int64_t batch_hint, int32_t aligned16,
                 gemm_choice* out);
+
+/* gemm_select for a given storage of B (GEMM_B_KN or GEMM_B_NK). */
+int gemm_select_layout(const gemm_device_desc* dev, int64_t M, int64_t N, int64_t K,
+                       int32_t dtype, const gemm_epilogue* epi, int64_t batch_hint,
+                       int32_t aligned16, int32_t b_layout, gemm_choice* out);
 
 /* Number of configurations compiled into the library. */
 int gemm_config_count(void);

@@ -172,6 +172,21 @@ def test_select_few_rows_split_k(dtype, M):
     assert not g.config_names()[g.select(9, 4096, 4096, dtype, **MI355X).config].startswith("gemv")
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_select_transposed_b(dtype):
+    """A transposed B (Bt [N x K]) takes the both-operands-K-contiguous kernels;
+    K not a multiple of 8 copies both operands; fp32 has no such kernel."""
+    for M, N, K in [(4096, 4096, 4096), (512, 512, 64), (1, 4096, 4096), (300, 264, 200)]:
+        ch = g.select(M, N, K, dtype, b_layout="nk", **MI355X)
+        assert g.config_names()[ch.config].startswith(f"m16n_{dtype}_") and ch.packed == 0
+    ch = g.select(127, 1000, 771, dtype, b_layout="nk", **MI355X)
+    assert g.config_names()[ch.config].startswith("m16n") and ch.packed == 3
+    # the plain layout never takes a transposed-B kernel
+    assert not g.config_names()[g.select(4096, 4096, 4096, dtype, **MI355X).config].startswith("m16n")
+    with pytest.raises(g.GemmError):
+        g.select(64, 64, 64, "f32", b_layout="nk", **MI355X)
+
+
 def test_exact_shape_cache_hit():
     h0, m0, e0 = g.cache_stats()
     g.select(777, 555, 333, "bf16", **MI355X)

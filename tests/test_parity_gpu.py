@@ -53,7 +53,8 @@ def _dtype_of(name):
 
 
 CONFIGS = _configs()
-TILE_CONFIGS = [c for c in CONFIGS if not c.startswith("gemv")]
+TILE_CONFIGS = [c for c in CONFIGS if not c.startswith("gemv") and not c.startswith("m16n")]
+NT_CONFIGS = [c for c in CONFIGS if c.startswith("m16n")]
 GEMV_CONFIGS = [c for c in CONFIGS if c.startswith("gemv")]
 
 
@@ -298,6 +299,88 @@ def test_workload_odd_shapes(g, name):
     C = gc.run_gpu(plan, A, B)
     r = gc.check_full(C, A, B, w["dtype"])
     assert r["ok"], r
+
+
+def _run_nt(plan, A, B, bias=None, resid=None, batched=False):
+    """Run a transposed-B plan: the kernel gets Bt = B^T (contiguous); the oracle
+    keeps using B."""
+    dev = torch.device("cuda")
+    Bt = B.transpose(-1, -2).contiguous()
+    fn = plan.run_batched if batched else plan.run
+    out = fn(A.to(dev), Bt.to(dev), None if bias is None else bias.to(dev),
+             None if resid is None else resid.to(dev))
+    torch.cuda.synchronize()
+    return out.cpu()
+
+
+@pytest.mark.parametrize("name", NT_CONFIGS)
+def test_each_nt_config_ragged(g, name):
+    """Every transposed-B configuration (B given as Bt [N x K]) on shapes spanning
+    several tiles with ragged M/N/K tails, the exact tile size and one row."""
+    dtype = _dtype_of(name)
+    idx = g.config_index(name)
+    dims = list(map(int, [p for p in name.split("_") if "x" in p and p[0].isdigit()][0].split("x")))
+    bm, bn, bk = dims
+    shapes = [(2 * bm + 3, bn + 8, 2 * bk + 8), (bm, bn, bk), (1, 8, 8), (bm + 5, 2 * bn + 3, 3 * bk)]
+    for si, (M, N, K) in enumerate(shapes):
+        say(f"[{name}] M={M} N={N} K={K}")
+        plan = g.Plan(M, N, K, dtype, config=idx, b_layout="nk")
+        assert plan.config_name == name
+        for kind in ("uniform", "int"):
+            A, B = gc.inputs(M, N, K, dtype, 3000 + 17 * si, kind)
+            C = _run_nt(plan, A, B)
+            r = gc.check_full(C, A, B, dtype, exact=(kind == "int"))
+            assert r["ok"], (name, M, N, K, kind, r)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_nt_epilogue_packed_and_errors(g, dtype):
+    """Transposed B with bias + GELU to 16-bit output, with residual, with K not a
+    multiple of 8 (A and Bt copied into padded rows), and the alignment error."""
+    cases = [(300, 264, 200, dict(bias=True, gelu=True, out_dtype="bf16"), 0),
+             (257, 130, 192, dict(bias=True, resid=True, out_dtype=dtype), 0),
+             (200, 136, 77, dict(), 3)]
+    for ci, (M, N, K, epi, packed) in enumerate(cases):
+        plan = g.Plan(M, N, K, dtype, b_layout="nk", **epi)
+        d = _describe(plan)
+        say(f"[nt] {plan.describe()}")
+        assert d["b"] == "nk" and int(d["packed"]) == packed
+        A, B = gc.inputs(M, N, K, dtype, 810 + ci)
+        od = epi.get("out_dtype", "f32")
+        bias = synth.normal(820 + ci, (N,), 0.5, "f32") if epi.get("bias") else None
+        resid = synth.uniform(830 + ci, (M, N), od) if epi.get("resid") else None
+        C = _run_nt(plan, A, B, bias, resid)
+        r = gc.check_full(C, A, B, dtype, od, bias, resid, None, epi.get("gelu", False))
+        assert r["ok"], (ci, r)
+    # an operand off a 16-byte boundary: transposed B has no scalar-load kernel
+    import ctypes
+    M, N, K = 64, 64, 64
+    plan = g.Plan(M, N, K, dtype, b_layout="nk")
+    dev = torch.device("cuda")
+    buf = torch.zeros(M * K + 8, dtype=gc.TORCH[dtype], device=dev)
+    C = torch.empty(M, N, device=dev)
+    rc = g.lib.gemm_run(plan._h, ctypes.c_void_p(buf.data_ptr() + 2), ctypes.c_void_p(buf.data_ptr()),
+                        None, None, ctypes.c_void_p(C.data_ptr()), None)
+    assert rc == -4
+
+
+def test_workload_qk_nt(g):
+    """96 attention-score GEMMs with K as stored ([S x D] per head, no transposed
+    copy): C = Q K^T through a transposed-B plan, every element of every head."""
+    import oracle
+    Q, Kt = synth.qk_inputs()
+    Kmat = Kt.transpose(1, 2).contiguous()  # [96 x 512 x 64]
+    nb, S, D = Q.shape
+    plan = g.Plan(S, S, D, "bf16", batch_hint=nb, b_layout="nk")
+    say("[qk-nt]", plan.describe())
+    dev = torch.device("cuda")
+    Sc = plan.run_batched(Q.to(dev), Kmat.to(dev))
+    torch.cuda.synchronize()
+    Sc = Sc.cpu()
+    for b in range(nb):
+        ref, s = oracle.gemm(synth.bits(Q[b]), synth.bits(Kt[b]), "bf16")
+        r = oracle.check(synth.bits(Sc[b]), ref, s)
+        assert r["ok"], (b, r)
 
 
 PACKED_CASES = [
