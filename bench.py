@@ -120,22 +120,25 @@ def time_graph(fn, reps=20, replays=7):
     return sorted(ts)[len(ts) // 2]
 
 
-def gemm_workload(g, name, steps, warmup, graph=False):
+def gemm_workload(g, name, steps, warmup, graph=False, b_layout="kn"):
     import torch
     import synth
     w = synth.WORKLOADS[name]
     A, B = synth.gemm_inputs(name)
+    if b_layout == "nk":
+        B = B.t().contiguous()  # the same product with B stored transposed (Bt [N x K])
     dev = torch.device("cuda")
     A, B = A.to(dev), B.to(dev)
     M, N, K = w["M"], w["N"], w["K"]
-    plan = g.Plan(M, N, K, w["dtype"])
+    plan = g.Plan(M, N, K, w["dtype"], b_layout=b_layout)
     C = torch.empty((M, N), dtype=torch.float32, device=dev)
     run = lambda: plan.run(A, B, out=C)  # noqa: E731
     med, mean, wall = time_calls(run, steps, warmup)
     flops = 2 * M * N * K
     es = 4 if w["dtype"] == "f32" else 2
     byts = (M * K + K * N) * es + M * N * 4
-    r = dict(workload=name, M=M, N=N, K=K, dtype=w["dtype"], config=plan.config_name,
+    r = dict(workload=name + ("_nt" if b_layout == "nk" else ""), M=M, N=N, K=K, dtype=w["dtype"],
+             config=plan.config_name, b_layout=b_layout,
              median_ms=med, mean_ms=mean, wall_s=wall, flops=flops, bytes=byts,
              tflops=flops / (med * 1e-3) / 1e12,
              tflops_mean=flops / (mean * 1e-3) / 1e12,
@@ -148,49 +151,58 @@ def gemm_workload(g, name, steps, warmup, graph=False):
     return r
 
 
-def ffn_workload(g, steps, warmup):
+def ffn_workload(g, steps, warmup, b_layout="kn"):
+    """The encoder FFN pair; b_layout="nk" keeps the weights in [out, in] order."""
     import torch
     import synth
     X, W1, b1, W2, b2 = synth.ffn_inputs()
+    T, Hd, F = X.shape[0], X.shape[1], W1.shape[1]
+    if b_layout == "nk":
+        W1, W2 = W1.t().contiguous(), W2.t().contiguous()
     dev = torch.device("cuda")
     X, W1, b1, W2, b2 = (t.to(dev) for t in (X, W1, b1, W2, b2))
-    T, Hd, F = X.shape[0], X.shape[1], W1.shape[1]
-    p1 = g.Plan(T, F, Hd, "bf16", bias=True, gelu=True, out_dtype="bf16")
-    p2 = g.Plan(T, Hd, F, "bf16", bias=True, resid=True, out_dtype="bf16")
+    p1 = g.Plan(T, F, Hd, "bf16", bias=True, gelu=True, out_dtype="bf16", b_layout=b_layout)
+    p2 = g.Plan(T, Hd, F, "bf16", bias=True, resid=True, out_dtype="bf16", b_layout=b_layout)
     H = torch.empty((T, F), dtype=torch.bfloat16, device=dev)
     Y = torch.empty((T, Hd), dtype=torch.bfloat16, device=dev)
     out = {}
+    sfx = "_nt" if b_layout == "nk" else ""
     for tag, fn, fl, by in (
-        ("ffn1", lambda: p1.run(X, W1, bias=b1, out=H), 2 * T * F * Hd,
+        ("ffn1" + sfx, lambda: p1.run(X, W1, bias=b1, out=H), 2 * T * F * Hd,
          (T * Hd + Hd * F + T * F) * 2 + F * 4),
-        ("ffn2", lambda: p2.run(H, W2, bias=b2, resid=X, out=Y), 2 * T * F * Hd,
+        ("ffn2" + sfx, lambda: p2.run(H, W2, bias=b2, resid=X, out=Y), 2 * T * F * Hd,
          (T * F + F * Hd + 2 * T * Hd) * 2 + Hd * 4),
     ):
         med, mean, wall = time_calls(fn, steps, warmup)
         gms = time_graph(fn)
         out[tag] = dict(workload=tag, median_ms=med, mean_ms=mean, flops=fl, bytes=by,
-                        config=(p1 if tag == "ffn1" else p2).config_name,
+                        config=(p1 if tag.startswith("ffn1") else p2).config_name,
                         tflops=fl / (med * 1e-3) / 1e12, gbs=by / (med * 1e-3) / 1e9,
                         frac_peak=fl / (mean * 1e-3) / 1e12 / PEAK_TFLOPS["bf16"],
                         graph_ms=gms, graph_tflops=fl / (gms * 1e-3) / 1e12)
     return out
 
 
-def qk_workload(g, steps, warmup):
+def qk_workload(g, steps, warmup, b_layout="kn"):
+    """96 heads of Q K^T; "kn" takes the materialised K^T [64 x 512] per head,
+    "nk" takes K as stored [512 x 64] (no transposed copy)."""
     import torch
     import synth
     Q, Kt = synth.qk_inputs()
+    if b_layout == "nk":
+        Kt = Kt.transpose(1, 2).contiguous()
     dev = torch.device("cuda")
     Q, Kt = Q.to(dev), Kt.to(dev)
     nb, S, D = Q.shape
-    plan = g.Plan(S, S, D, "bf16", batch_hint=nb)
+    plan = g.Plan(S, S, D, "bf16", batch_hint=nb, b_layout=b_layout)
     out = torch.empty((nb, S, S), dtype=torch.float32, device=dev)
     run = lambda: plan.run_batched(Q, Kt, out=out)  # noqa: E731
     med, mean, wall = time_calls(run, steps, warmup)
     gms = time_graph(run)
     fl = 2 * nb * S * S * D
     by = nb * (2 * S * D * 2 + S * S * 4)
-    return dict(workload="qk_96x512x512x64", median_ms=med, mean_ms=mean, flops=fl, bytes=by,
+    return dict(workload="qk_96x512x512x64" + ("_nt" if b_layout == "nk" else ""), median_ms=med,
+                mean_ms=mean, flops=fl, bytes=by,
                 config=plan.config_name, tflops=fl / (med * 1e-3) / 1e12,
                 gbs=by / (med * 1e-3) / 1e9, frac_hbm=by / (mean * 1e-3) / 1e9 / PEAK_HBM_GBS,
                 graph_ms=gms, graph_tflops=fl / (gms * 1e-3) / 1e12,
@@ -231,6 +243,10 @@ def symbol_to_config(sym: str):
     if m:
         t, bm, bn, wm, wn, sa, kr, r = m.groups()
         return f"m16d_{t}_{bm}x{bn}x64_w{wm}x{wn}_a{sa}_b{kr}_r{r}"
+    m = re.search(r"gemm_m16n_kernel<g15::(\w+)_t, (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)>", sym)
+    if m:
+        t, bm, bn, wm, wn, sa, sb = m.groups()
+        return f"m16n_{t}_{bm}x{bn}x64_w{wm}x{wn}_a{sa}_b{sb}"
     m = re.search(r"gemm_f32d_kernel<(\d+), (\d+), (\d+), (\d+), (\d+)>", sym)
     if m:
         bm, bn, wm, wn, sa = m.groups()
@@ -333,6 +349,15 @@ def main():
               file=sys.stderr, flush=True)
         extra["qk"] = qk_workload(g, args.steps, args.warmup)
         print(f"[bench] {json.dumps(extra['qk'])}", file=sys.stderr, flush=True)
+        # the same products with B stored transposed (weights [out, in], K as stored)
+        extra["bf16_4096_nt"] = gemm_workload(g, "bf16_4096", args.steps, args.warmup,
+                                              b_layout="nk")
+        print(f"[bench] {json.dumps(extra['bf16_4096_nt'])}", file=sys.stderr, flush=True)
+        extra.update(ffn_workload(g, args.steps, args.warmup, b_layout="nk"))
+        print(f"[bench] ffn_nt {json.dumps(extra['ffn1_nt'])} {json.dumps(extra['ffn2_nt'])}",
+              file=sys.stderr, flush=True)
+        extra["qk_nt"] = qk_workload(g, args.steps, args.warmup, b_layout="nk")
+        print(f"[bench] {json.dumps(extra['qk_nt'])}", file=sys.stderr, flush=True)
 
     cpu = None
     if not args.no_cpu:
