@@ -108,8 +108,11 @@ const EffRow kEff[] = {
     {"m16d_bf16_128x128x64_w2x2_a3", 0.79}, {"m16d_f16_128x128x64_w2x2_a3", 0.79},
     {"m16d_bf16_128x128x64_w2x2_a4", 0.67}, {"m16d_f16_128x128x64_w2x2_a4", 0.67},
     {"m16d_bf16_64x128", 0.62}, {"m16d_f16_64x128", 0.62},
-    {"m16n_bf16_256x256x64_w4x2", 1.04}, {"m16n_f16_256x256x64_w4x2", 1.04},
-    {"m16n_bf16_256x256x64_w2x4", 1.02}, {"m16n_f16_256x256x64_w2x4", 1.02},
+    {"m16n_bf16_256x256x64_w2x4", 1.05}, {"m16n_f16_256x256x64_w2x4", 1.05},
+    {"m16n_bf16_256x256x64_w4x2", 1.01}, {"m16n_f16_256x256x64_w4x2", 1.01},
+    {"m16t_bf16_256x256", 0.97}, {"m16t_f16_256x256", 0.97},
+    {"m16t_bf16_128x128x64_w2x2_a2_b2", 0.78}, {"m16t_f16_128x128x64_w2x2_a2_b2", 0.78},
+    {"m16t_bf16_", 0.75}, {"m16t_f16_", 0.75},
     {"m16n_bf16_128x256", 0.92}, {"m16n_f16_128x256", 0.92},
     {"m16n_bf16_256x128", 0.86}, {"m16n_f16_256x128", 0.86},
     {"m16n_bf16_128x128x64_w2x2_a2_b2", 0.86}, {"m16n_f16_128x128x64_w2x2_a2_b2", 0.86},
@@ -151,9 +154,9 @@ const TunedRow kTuned[] = {
     {false, 8192, 3072, 768, 1, "m16d_{t}_128x256x64_w2x4_a3_b4_r1"},  // encoder FFN, first GEMM
     {false, 8192, 768, 3072, 1, "m16d_{t}_128x256x64_w2x4_a3_b4_r1"},  // encoder FFN, second GEMM
     {false, 512, 512, 64, 96, "m16d_{t}_128x128x64_w2x2_a3_b4_r1"},    // 96 heads of Q K^T
-    {false, 4096, 4096, 4096, 1, "m16n_{t}_256x256x64_w4x2_a3_b2"},
+    {false, 4096, 4096, 4096, 1, "m16n_{t}_256x256x64_w2x4_a3_b2"},
     {false, 2048, 2048, 2048, 1, "m16n_{t}_128x128x64_w2x2_a3_b3"},
-    {false, 8192, 3072, 768, 1, "m16n_{t}_256x256x64_w4x2_a3_b2"},
+    {false, 8192, 3072, 768, 1, "m16n_{t}_256x256x64_w2x4_a3_b2"},
     {false, 8192, 768, 3072, 1, "m16n_{t}_128x256x64_w2x4_a3_b3"},
     {false, 512, 512, 64, 96, "m16n_{t}_128x128x64_w2x2_a2_b2"},
     {true, 4096, 4096, 4096, 1, "f32d_256x256x16_w4x2_a3"},

@@ -1,6 +1,11 @@
-// kernel_mfma16_nt.hip -- bf16 / fp16 matrix-core GEMM with the right operand
-// given transposed: C = epi(A x Bt^T), A [M x K] and Bt [N x K] row-major (a
-// linear layer's weight in [out, in] order, or K of attention scores Q K^T).
+// kernel_mfma16_nt.hip -- bf16 / fp16 matrix-core GEMMs with both operands
+// streamed global -> LDS directly:
+//  * m16n: the right operand given transposed, C = epi(A x Bt^T), A [M x K] and
+//    Bt [N x K] row-major (a linear layer's weight in [out, in] order, or K of
+//    attention scores Q K^T);
+//  * m16t: the plain layout, B [K x N] row-major, with B slices stored in LDS as
+//    they come (k rows of n) and B fragments read with the gfx950 transposing
+//    LDS read (ds_read_b64_tr_b16), two per fragment.
 //
 // Same tiling and schedule as kernel_mfma16_dlds.hip (DeepGEMM page, sections
 // 2.2 and 3.1; prefetch of the SGEMM page, section 2.3), but both operands now
@@ -8,6 +13,13 @@
 // -> LDS directly (buffer_load ... lds) exactly like A, into their own ring, and
 // B fragments are read like A fragments. No register staging, no transpose, no
 // LDS stores in the main loop.
+//
+// For m16t the transposing read returns, in lane i of each group of 16 lanes, 4
+// consecutive k of column n0 + i when source lane t of the group addresses row
+// k0 + t / 4, columns n0 + 4 (t % 4) .. +3; a fragment (8 k of one column per
+// lane) takes two such reads. B rows of 2 BN bytes permute 16-byte chunk c to
+// c ^ (4 (k & 3)), which keeps those reads free of bank conflicts (measured 2.9
+// cycles per read, like an untransposed 8-byte read).
 //
 // LDS: an A ring of SA slices and a B ring of SB slices (BM x 128 and BN x 128
 // bytes per slice). With SB = SA - 1 (the 256 x 256 tile, whose rings would not
@@ -19,7 +31,11 @@
 namespace g15 {
 namespace {
 
-template <typename T, int BM, int BN, int WGM, int WGN, int SA, int SB>
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+template <typename T, int BM, int BN, int WGM, int WGN, int SA, int SB, bool BROW>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a) {
   constexpr int BK = 64;
   constexpr int NW = WGM * WGN;
@@ -34,6 +50,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 block");
   static_assert(SB >= 2 && (SA == SB || SA == SB + 1), "rings: SA = SB or SA = SB + 1");
   static_assert(BK / 16 == 4, "the K loop below is written for four k-steps per slice");
+  // B row-major (m16t): a slice is 64 rows of BN/8 chunks; one load fills RPI rows
+  constexpr int CPR_B = BN / 8, RPI = 64 / CPR_B;
+  static_assert(!BROW || (CPR_B >= 16 && 64 % CPR_B == 0), "m16t: BN of 128 or 256");
   constexpr int RING = SA * A_STAGE + SB * B_STAGE;
   constexpr int STG = (NW * 32 * (WTN + 8) * 4 + 15) / 16;  // epilogue staging, 16-byte units
   __shared__ u32x4 lds[RING > STG ? RING : STG];
@@ -65,11 +84,23 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
     const int gm = m0 + (wave * AI + i) * 8 + (lane >> 3);
     a_voff[i] = gm < M ? static_cast<uint32_t>(gm * LDA + a_chk[i] * 8) * 2u : OOB;
   }
+  int b_row[BI];  // m16t: the slice row this lane fills in load i
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
-    b_chk[i] = (lane & 7) ^ (lane >> 3) ^ ((wave * BI + i) & 3);
-    const int gn = n0 + (wave * BI + i) * 8 + (lane >> 3);
-    b_voff[i] = gn < N ? static_cast<uint32_t>(gn * LDB + b_chk[i] * 8) * 2u : OOB;
+    if constexpr (!BROW) {
+      b_chk[i] = (lane & 7) ^ (lane >> 3) ^ ((wave * BI + i) & 3);
+      const int gn = n0 + (wave * BI + i) * 8 + (lane >> 3);
+      b_voff[i] = gn < N ? static_cast<uint32_t>(gn * LDB + b_chk[i] * 8) * 2u : OOB;
+      b_row[i] = 0;
+    } else {
+      // load q = wave BI + i fills rows q RPI .. +RPI-1; lane l -> row q RPI + l / CPR_B,
+      // slot chunk l % CPR_B, which holds logical chunk (l % CPR_B) ^ (4 (row & 3))
+      const int row = (wave * BI + i) * RPI + lane / CPR_B;
+      const int gn = n0 + ((lane % CPR_B) ^ (4 * (row & 3))) * 8;
+      b_row[i] = row;
+      b_chk[i] = 0;
+      b_voff[i] = gn < N ? static_cast<uint32_t>(row * LDB + gn) * 2u : OOB;
+    }
   }
   // One operand's slice k0 into ring slot `slot`. TAIL: the slice may reach past K
   // (chunks past K are masked and their slots zeroed, since an out-of-range
@@ -97,8 +128,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
           std::integral_constant<int, AI>{});
   };
   auto issue_b = [&](int k0, int slot, auto TailC) {
-    issue(Bbase, N, LDB, b_voff, b_chk, ringB, BI, k0, slot, TailC,
-          std::integral_constant<int, BI>{});
+    if constexpr (!BROW) {
+      issue(Bbase, N, LDB, b_voff, b_chk, ringB, BI, k0, slot, TailC,
+            std::integral_constant<int, BI>{});
+    } else {
+      // rows past K fall beyond the slice's descriptor extent (read as zeros; the
+      // tail zeroes their slots, which such a load leaves untouched)
+      constexpr bool TAIL = decltype(TailC)::value;
+      const int64_t left = static_cast<int64_t>(K - k0) * LDB;
+      const auto r = rsrc(Bbase + static_cast<int64_t>(k0) * LDB,
+                          static_cast<uint32_t>(left > 0 ? left * 2 : 0));
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+        u32x4* dst = ringB + slot * B_STAGE + (wave * BI + i) * 64;
+        if (TAIL && k0 + b_row[i] >= K) dst[lane] = u32x4{0u, 0u, 0u, 0u};
+        // (an array element written straight into the builtin's arguments makes the
+        // host compilation drop this kernel's launch stub; go through a local)
+        const uint32_t off = b_voff[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)dst, 16, off, 0, 0, 0);
+      }
+    }
   };
 
   f32x16 acc[FM][FN];
@@ -115,12 +164,43 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
   // chunk permutation depends on the row modulo 32 only
   const int a_base = (wm * WTM + lrow) * 8, b_base = (wn * WTN + lrow) * 8;
   const int perm = (lrow & 7) ^ ((lrow >> 3) & 3);
+  // m16t: byte offset in a B slice of this lane's first transposing read of block
+  // j at k-step 0 (group g = lane / 16, t = lane % 16: row 8 (g / 2) + t / 4,
+  // column wn WTN + 32 j + 16 (g % 2) + 4 (t % 4)); k-step s adds 16 s rows, the
+  // second read of a fragment 4 rows, neither of which changes row & 3
+  int btr[FN];
+  {
+    const int g = lane >> 4, t = lane & 15;
+    const int kr = 8 * (g >> 1) + (t >> 2);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = wn * WTN + 32 * j + 16 * (g & 1) + 4 * (t & 3);
+      btr[j] = kr * (BN * 2) + (((n >> 3) ^ (4 * (kr & 3))) << 4) + (n & 7) * 2;
+    }
+  }
   auto frags = [&](const u32x4* LA, const u32x4* LB, int s, u32x4 (&fa)[FM], u32x4 (&fb)[FN]) {
     const int c = (2 * s + lhalf) ^ perm;
 #pragma unroll
     for (int i = 0; i < FM; ++i) fa[i] = LA[a_base + i * 256 + c];
+    if constexpr (!BROW) {
 #pragma unroll
-    for (int j = 0; j < FN; ++j) fb[j] = LB[b_base + j * 256 + c];
+      for (int j = 0; j < FN; ++j) fb[j] = LB[b_base + j * 256 + c];
+    } else {
+      // address the LDS array itself (an address-space cast of a derived generic
+      // pointer is not available in the host compilation of this kernel)
+      const int boff = static_cast<int>(LB - lds) * 16 + 16 * s * (BN * 2);
+      const lds_char* Lb = (const lds_char*)lds + boff;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Lb + btr[j]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4*)(Lb + btr[j] + 4 * (BN * 2)));
+        fb[j] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                      __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                      __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                      __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
+      }
+    }
   };
   auto mmas = [&](const u32x4 (&fa)[FM], const u32x4 (&fb)[FN], int i0, int i1) {
 #pragma unroll
@@ -193,23 +273,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
       a, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, wave, lane, z);
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, int SA, int SB>
+template <typename T, int BM, int BN, int WGM, int WGN, int SA, int SB, bool BROW>
 hipError_t launch_m16n(const LaunchArgs& a, hipStream_t s) {
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(a.batch));
-  hipLaunchKernelGGL((gemm_m16n_kernel<T, BM, BN, WGM, WGN, SA, SB>), grid, dim3(64 * WGM * WGN),
-                     0, s, a);
+  hipLaunchKernelGGL((gemm_m16n_kernel<T, BM, BN, WGM, WGN, SA, SB, BROW>), grid,
+                     dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }
 
-#define G15_M16N(T, TN, BM, BN, WGM, WGN, SA, SB)                                                 \
-  {"m16n_" TN "_" #BM "x" #BN "x64_w" #WGM "x" #WGN "_a" #SA "_b" #SB, KIND_MFMA16, T::code, BM,   \
+#define G15_M16N(T, TN, BM, BN, WGM, WGN, SA, SB) G15_M16X(T, TN, "m16n_", false, BM, BN, WGM, WGN, SA, SB)
+#define G15_M16T(T, TN, BM, BN, WGM, WGN, SA, SB) G15_M16X(T, TN, "m16t_", true, BM, BN, WGM, WGN, SA, SB)
+#define G15_M16X(T, TN, PFX, BROW, BM, BN, WGM, WGN, SA, SB)                                      \
+  {PFX TN "_" #BM "x" #BN "x64_w" #WGM "x" #WGN "_a" #SA "_b" #SB, KIND_MFMA16, T::code, BM,       \
    BN, 64, 64 * WGM * WGN,                                                                        \
    static_cast<int>(sizeof(u32x4)) *                                                              \
        ((SA * BM + SB * BN) * 8 > (WGM * WGN * 32 * (BN / WGN + 8) * 4 + 15) / 16                  \
             ? (SA * BM + SB * BN) * 8                                                             \
             : (WGM * WGN * 32 * (BN / WGN + 8) * 4 + 15) / 16),                                   \
-   1, 1, launch_m16n<T, BM, BN, WGM, WGN, SA, SB>, 1, 1}
+   1, 1, launch_m16n<T, BM, BN, WGM, WGN, SA, SB, BROW>, 1, BROW ? 0 : 1}
 
 #define G15_M16N_ALL(T, TN)                     \
   G15_M16N(T, TN, 256, 256, 4, 2, 3, 2),        \
@@ -220,9 +302,17 @@ hipError_t launch_m16n(const LaunchArgs& a, hipStream_t s) {
   G15_M16N(T, TN, 128, 128, 2, 2, 2, 2),        \
   G15_M16N(T, TN, 64, 128, 2, 2, 4, 4)
 
+#define G15_M16T_ALL(T, TN)                     \
+  G15_M16T(T, TN, 256, 256, 4, 2, 3, 2),        \
+  G15_M16T(T, TN, 256, 256, 2, 4, 3, 2),        \
+  G15_M16T(T, TN, 256, 128, 2, 2, 3, 3),        \
+  G15_M16T(T, TN, 128, 256, 2, 4, 3, 3),        \
+  G15_M16T(T, TN, 128, 128, 2, 2, 3, 3),        \
+  G15_M16T(T, TN, 128, 128, 2, 2, 2, 2)
+
 const KernelEntry kM16N[] = {
-    G15_M16N_ALL(bf16_t, "bf16"),
-    G15_M16N_ALL(f16_t, "f16"),
+    G15_M16N_ALL(bf16_t, "bf16"), G15_M16N_ALL(f16_t, "f16"),
+    G15_M16T_ALL(bf16_t, "bf16"), G15_M16T_ALL(f16_t, "f16"),
 };
 
 }  // namespace
