@@ -58,6 +58,15 @@ def test_plan_create_without_device():
     assert e.value.status == -5
 
 
+def test_layout_plan_errors_without_device():
+    """gemm_plan_create_layout validates its layout before looking for a device."""
+    e = g.Epilogue(0, 1.0, g.F32)
+    assert not g.lib.gemm_plan_create_layout(64, 64, 64, g.BF16, ctypes.byref(e), 1, -1, 7)
+    assert g.lib.gemm_last_error() == -10  # GEMM_ERR_ARG
+    assert not g.lib.gemm_plan_create_layout(64, 64, 64, g.F32, ctypes.byref(e), 1, -1, 1)
+    assert g.lib.gemm_last_error() == -2  # GEMM_ERR_DTYPE: no transposed-B fp32 kernel
+
+
 def test_null_plan_rejected():
     assert g.lib.gemm_run(None, None, None, None, None, None, None) == -7
     assert g.lib.gemm_plan_describe(None, None, 0) == -7

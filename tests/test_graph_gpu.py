@@ -30,6 +30,9 @@ CASES = [
     (1024, 1024, 512, "f32", dict()),
     (2, 1000, 3000, "bf16", dict(bias=True, out_dtype="f32")),  # few-row kernel, split K
     (1, 4096, 4096, "f16", dict()),
+    (300, 261, 203, "f16", dict()),                     # padded copies of A and B, element-wise C
+    (512, 512, 256, "bf16", dict(b_layout="nk")),       # B given transposed
+    (200, 136, 77, "bf16", dict(b_layout="nk")),        # transposed B with padded copies
 ]
 
 
@@ -38,12 +41,14 @@ def test_graph_replay_matches_eager(g, case):
     M, N, K, dtype, epi = CASES[case]
     print(f"[graph] {M}x{N}x{K} {dtype} {epi}", file=sys.stderr, flush=True)
     plan = g.Plan(M, N, K, dtype, **epi)
+    nk = epi.get("b_layout") == "nk"
     dev = torch.device("cuda")
-    sets = []
+    sets, Bref = [], []
     for seed in (901, 905, 909):
         A, B = gc.inputs(M, N, K, dtype, seed)
+        Bref.append(B)
         bias = synth.normal(seed + 2, (N,), 0.5, "f32").to(dev) if epi.get("bias") else None
-        sets.append((A.to(dev), B.to(dev), bias))
+        sets.append((A.to(dev), (B.t().contiguous() if nk else B).to(dev), bias))
     eager = [plan.run(A, B, bias=b).clone() for A, B, b in sets]
     torch.cuda.synchronize()
 
@@ -74,7 +79,7 @@ def test_graph_replay_matches_eager(g, case):
                            eager[i].view(torch.int16 if out.element_size() == 2 else torch.int32)), \
             (case, rep, i, plan.describe())
     # the eager results themselves are right
-    A, B, b = sets[0]
-    r = gc.check_full(eager[0].cpu(), A.cpu(), B.cpu(), dtype, epi.get("out_dtype", "f32"),
+    A, _, b = sets[0]
+    r = gc.check_full(eager[0].cpu(), A.cpu(), Bref[0], dtype, epi.get("out_dtype", "f32"),
                       None if b is None else b.cpu(), gelu=epi.get("gelu", False))
     assert r["ok"], r
