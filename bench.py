@@ -281,20 +281,21 @@ def summarize(db_dir: str, kind: str) -> None:
         d = sqlite3.connect(db)
         for name, cn, val in d.execute("select kernel_name, counter_name, value from counters_collection"):
             acc[(name, cn)].append(val)
-    print(f"{'kernel':96s} {'counter':12s} {'n':>4s} {'KiB/dispatch':>14s}")
+    print(f"{'kernel':96s} {'counter':24s} {'n':>4s} {'per dispatch':>16s}")
     for (name, cn), v in sorted(acc.items()):
-        print(f"{name[:96]:96s} {cn:12s} {len(v):4d} {sum(v) / len(v):14.1f}")
+        print(f"{name[:96]:96s} {cn:24s} {len(v):4d} {sum(v) / len(v):16.1f}")
     # update the traffic file with the scale of each counter on the 256 MiB copy
     t = {"kernels": {}}
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-    copy = {cn: sum(v) / len(v) for (name, cn), v in acc.items() if "copyBuffer" in name}
+    copy = {cn: sum(v) / len(v) for (name, cn), v in acc.items()
+            if "copyBuffer" in name and cn in ("FETCH_SIZE", "WRITE_SIZE")}
     for cn, kib in copy.items():
         t.setdefault("scale", {})[cn] = 262144.0 / kib
     for (name, cn), v in acc.items():
         cfg = symbol_to_config(name)
-        if cfg is None:
+        if cfg is None or cn not in ("FETCH_SIZE", "WRITE_SIZE"):
             continue
         t["kernels"].setdefault(cfg, {})[cn + "_kib"] = sum(v) / len(v)
     sc = t.get("scale", {})
