@@ -34,7 +34,8 @@ struct LaunchArgs {
   // Row strides in elements. Every kernel handles lda = K, ldb = N, ldc = N;
   // only the m16d kernels take other strides (operands packed into padded rows).
   int64_t lda, ldb, ldc;
-  int c_vec;            // 1: C (and resid) rows and base are 16-byte aligned (m16d reads it)
+  int c_vec;            // 1: C (and resid) base and rows 16-byte aligned, N % 8 == 0
+                        // (read by the 16-bit staged epilogue of the m16 kernels)
 };
 
 // Copy a rows x cols matrix of 16-bit elements (row stride cols) into rows of

@@ -1,7 +1,7 @@
 // m16_common.hpp -- pieces shared by the bf16 / fp16 matrix-core kernels that
 // stream operands global -> LDS (kernel_mfma16_dlds.hip, kernel_mfma16_nt.hip):
 // buffer descriptors, the 32x32x16 MFMA, wait and barrier helpers, instruction
-// grouping, the XCD-aware tile order and the LDS-staged epilogue.
+// grouping, the XCD-aware tile order and the epilogue.
 #pragma once
 
 #include <type_traits>
@@ -77,28 +77,25 @@ __device__ __forceinline__ void tile_of(int wid, int tiles_m, int tiles_n, int& 
 
 // Epilogue of a wave's WTM x WTN sub-tile (FM x FN blocks of 32 x 32) of the tile
 // at (m0, n0). In the accumulators lane l holds C[row][col] of block (i, j) with
-// col = l % 32 and row = 8 (r / 4) + 4 (l / 32) + r % 4: one column per lane, so
-// direct stores would write 2 or 4 bytes per lane. Instead scale, bias and GELU
-// are applied there (the bias is one value per lane and block column), then each
-// 32-row block row of the sub-tile goes through the wave's own LDS area and comes
-// back as 8 consecutive columns per lane: residual loads and C stores move 16 or
-// 32 contiguous bytes per lane. That needs a.c_vec: N a multiple of 8 (a chunk of
-// 8 columns is all inside or all outside the matrix) and 16-byte aligned rows;
-// otherwise each lane moves single elements. lds_f is the workgroup's LDS
-// (LDS_BYTES bytes); every wave must have finished with its previous contents.
+// col = l % 32 and row = 8 (r / 4) + 4 (l / 32) + r % 4. Scale, bias and GELU are
+// applied there (the bias is one value per lane and block column); the residual is
+// added and the result rounded where it is stored. Three store forms, measured:
+//  * fp32 output: straight from the registers. One register of a block is 32
+//    consecutive columns of two rows, two whole 128-byte spans per store, and
+//    regrouping would only add work (also for rows of any alignment).
+//  * 16-bit output with a.c_vec (N a multiple of 8, 16-byte aligned rows): each
+//    32-row block row goes through the wave's own LDS area and comes back as 8
+//    consecutive columns per lane, 16-byte residual loads and C stores.
+//  * other 16-bit output: straight from the registers, two columns per lane
+//    after one exchange between neighbouring lanes (even LDC), else one.
+// lds_f is the workgroup's LDS (LDS_BYTES bytes); every wave must have finished
+// with its previous contents.
 template <int FM, int FN, int WTM, int WTN, int NW, int LDS_BYTES>
 __device__ __forceinline__ void store_tile(const LaunchArgs& a, f32x16 (&acc)[FM][FN], float* lds_f,
                                            int m0, int n0, int wm, int wn, int wave, int lane,
                                            int64_t z) {
   const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), LDC = static_cast<int>(a.ldc);
   const int lrow = lane & 31, lhalf = lane >> 5;
-  constexpr int EP = WTN + 8;  // floats per staged row: rows 4 apart land 32 banks apart
-  constexpr int CPR = WTN / 8;  // 8-column chunks per row
-  constexpr int RPP = 64 / CPR;  // rows per pass
-  constexpr int PASSES = 32 / RPP;
-  static_assert(NW * 32 * EP * 4 <= LDS_BYTES, "staging must fit in LDS");
-  static_assert(64 % CPR == 0 && 32 % RPP == 0, "staging passes");
-  float* stg = lds_f + wave * 32 * EP;
 
   const Epi& e = a.epi;
   const int ob = e.out_dtype == DT_F32 ? 4 : 2;
@@ -113,6 +110,105 @@ __device__ __forceinline__ void store_tile(const LaunchArgs& a, f32x16 (&acc)[FM
     const int col = n0 + wn * WTN + j * 32 + lrow;
     bj[j] = ((e.flags & EPI_BIAS) && col < N) ? e.bias[col] : 0.f;
   }
+  auto epi = [&](float v, int j) {
+    if (e.flags & EPI_SCALE) v *= e.scale;
+    if (e.flags & EPI_BIAS) v += bj[j];
+    if (e.flags & EPI_GELU) v = gelu(v);
+    return v;
+  };
+
+  if (e.out_dtype == DT_F32) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int cl = n0 + wn * WTN + 32 * j + lrow;
+        const int rb = m0 + wm * WTM + 32 * i + 4 * lhalf;
+        uint32_t off[16];
+        float rv[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rb + 8 * (r >> 2) + (r & 3);
+          off[r] = (row < M && cl < N) ? static_cast<uint32_t>(row * LDC + cl) * 4u : OOB;
+          if (has_r)  // the block's residual loads all in flight at once
+            rv[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rR, off[r], 0, 0));
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = epi(acc[i][j][r], j);
+          if (has_r) v += rv[r];
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rC, off[r], 0, 0);
+        }
+      }
+    return;
+  }
+
+  const bool bf = e.out_dtype == DT_BF16;
+  auto narrow = [&](float x) { return bf ? narrow_bf16(x) : narrow_f16(x); };
+  auto widen16 = [&](uint32_t h) {
+    return bf ? widen(bf16_t{}, static_cast<uint16_t>(h)) : widen(f16_t{}, static_cast<uint16_t>(h));
+  };
+
+  if (!a.c_vec) {
+    // Registers 2p and 2p+1 of a block are rows R and R+1 of one column per lane
+    // and lanes l, l^1 hold neighbouring columns: after one exchange the even lane
+    // has columns (c, c+1) of row R and the odd lane columns (c-1, c) of row R+1,
+    // 4 bytes per lane (4-byte aligned when LDC and N are even).
+    const bool odd = (lane & 1) != 0;
+    const bool pairs = ((LDC | N) & 1) == 0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int cl = n0 + wn * WTN + 32 * j + lrow;
+        const int rb = m0 + wm * WTM + 32 * i + 4 * lhalf;
+        float v[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) v[r] = epi(acc[i][j][r], j);
+        if (pairs) {
+          const int ce = cl & ~1;
+          uint32_t off[8], res[8];
+#pragma unroll
+          for (int p = 0; p < 8; ++p) {
+            const int row = rb + 8 * (p >> 1) + 2 * (p & 1) + (odd ? 1 : 0);
+            off[p] = (row < M && ce < N) ? static_cast<uint32_t>(row * LDC + ce) * 2u : OOB;
+            if (has_r) res[p] = __builtin_amdgcn_raw_buffer_load_b32(rR, off[p], 0, 0);
+          }
+#pragma unroll
+          for (int p = 0; p < 8; ++p) {
+            // DPP quad_perm [1, 0, 3, 2]: each lane receives its neighbour's value
+            const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(
+                __float_as_int(odd ? v[2 * p] : v[2 * p + 1]), 0xB1, 0xF, 0xF, false));
+            float lo = odd ? recv : v[2 * p];
+            float hi = odd ? v[2 * p + 1] : recv;
+            if (has_r) {
+              lo += widen16(res[p] & 0xffffu);
+              hi += widen16(res[p] >> 16);
+            }
+            const uint32_t w = static_cast<uint32_t>(narrow(lo)) | (static_cast<uint32_t>(narrow(hi)) << 16);
+            __builtin_amdgcn_raw_buffer_store_b32(w, rC, off[p], 0, 0);
+          }
+        } else {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int row = rb + 8 * (r >> 2) + (r & 3);
+            const uint32_t o = (row < M && cl < N) ? static_cast<uint32_t>(row * LDC + cl) * 2u : OOB;
+            float x = v[r];
+            if (has_r) x += widen16(__builtin_amdgcn_raw_buffer_load_b16(rR, o, 0, 0));
+            __builtin_amdgcn_raw_buffer_store_b16(narrow(x), rC, o, 0, 0);
+          }
+        }
+      }
+    return;
+  }
+
+  constexpr int EP = WTN + 8;    // floats per staged row: rows 4 apart land 32 banks apart
+  constexpr int CPR = WTN / 8;   // 8-column chunks per row
+  constexpr int RPP = 64 / CPR;  // rows per pass
+  constexpr int PASSES = 32 / RPP;
+  static_assert(NW * 32 * EP * 4 <= LDS_BYTES, "staging must fit in LDS");
+  static_assert(64 % CPR == 0 && 32 % RPP == 0, "staging passes");
+  float* stg = lds_f + wave * 32 * EP;
   const int q = lane % CPR;  // this lane's chunk within a staged row
   const int col = n0 + wn * WTN + 8 * q;
 #pragma unroll
@@ -120,82 +216,36 @@ __device__ __forceinline__ void store_tile(const LaunchArgs& a, f32x16 (&acc)[FM
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float v = acc[i][j][r];
-        if (e.flags & EPI_SCALE) v *= e.scale;
-        if (e.flags & EPI_BIAS) v += bj[j];
-        if (e.flags & EPI_GELU) v = gelu(v);
-        stg[(8 * (r >> 2) + 4 * lhalf + (r & 3)) * EP + 32 * j + lrow] = v;
-      }
+      for (int r = 0; r < 16; ++r)
+        stg[(8 * (r >> 2) + 4 * lhalf + (r & 3)) * EP + 32 * j + lrow] = epi(acc[i][j][r], j);
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's staging writes are done
 
-    if (!a.c_vec) {
-      // C rows not 16-byte aligned: the lanes take consecutive columns of one row
-      // and move one element each (coalesced, no vector access)
-      for (int rr = 0; rr < 32; ++rr) {
-        const int row = m0 + wm * WTM + 32 * i + rr;
-#pragma unroll
-        for (int cc = lane; cc < WTN; cc += 64) {
-          const int cl = n0 + wn * WTN + cc;
-          if (row < M && cl < N) {
-            const int64_t idx = static_cast<int64_t>(row) * LDC + cl;
-            float v = stg[rr * EP + cc];
-            if (has_r) v += load_out_elem(Rz, e.out_dtype, idx);
-            store_out_elem(Cz, e.out_dtype, idx, v);
-          }
-        }
-      }
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      continue;
-    }
-
     uint32_t off[PASSES];
-    u32x4 res[PASSES][2];
+    u32x4 res[PASSES];
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const int row = m0 + wm * WTM + 32 * i + p * RPP + lane / CPR;
-      off[p] = (row < M && col < N) ? static_cast<uint32_t>(row * LDC + col) * ob : OOB;
-      if (has_r) {  // every residual load of the block row in flight at once
-        res[p][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rR, off[p], 0, 0));
-        if (ob == 4)
-          res[p][1] = __builtin_bit_cast(
-              u32x4, __builtin_amdgcn_raw_buffer_load_b128(rR, off[p] + 16u, 0, 0));
-      }
+      off[p] = (row < M && col < N) ? static_cast<uint32_t>(row * LDC + col) * 2u : OOB;
+      if (has_r)  // every residual load of the block row in flight at once
+        res[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rR, off[p], 0, 0));
     }
 #pragma unroll
     for (int p = 0; p < PASSES; ++p) {
       const float* src = stg + (p * RPP + lane / CPR) * EP + 8 * q;
       const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
       const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
-      float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-      if (ob == 4) {
-        if (has_r)
+      const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      uint32_t w[4];
 #pragma unroll
-          for (int t = 0; t < 8; ++t) v[t] += __uint_as_float(res[p][t >> 2][t & 3]);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]),
-                                                     __float_as_uint(v[2]), __float_as_uint(v[3])},
-                                               rC, off[p], 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{__float_as_uint(v[4]), __float_as_uint(v[5]),
-                                                     __float_as_uint(v[6]), __float_as_uint(v[7])},
-                                               rC, off[p] + 16u, 0, 0);
-      } else {
-        const bool bf = e.out_dtype == DT_BF16;
-        uint32_t w[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          float x0 = v[2 * t], x1 = v[2 * t + 1];
-          if (has_r) {
-            const uint32_t rr = res[p][0][t];
-            const uint16_t r0 = static_cast<uint16_t>(rr & 0xffffu), r1 = static_cast<uint16_t>(rr >> 16);
-            x0 += bf ? widen(bf16_t{}, r0) : widen(f16_t{}, r0);
-            x1 += bf ? widen(bf16_t{}, r1) : widen(f16_t{}, r1);
-          }
-          const uint16_t h0 = bf ? narrow_bf16(x0) : narrow_f16(x0);
-          const uint16_t h1 = bf ? narrow_bf16(x1) : narrow_f16(x1);
-          w[t] = static_cast<uint32_t>(h0) | (static_cast<uint32_t>(h1) << 16);
+      for (int t = 0; t < 4; ++t) {
+        float x0 = v[2 * t], x1 = v[2 * t + 1];
+        if (has_r) {
+          x0 += widen16(res[p][t] & 0xffffu);
+          x1 += widen16(res[p][t] >> 16);
         }
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, rC, off[p], 0, 0);
+        w[t] = static_cast<uint32_t>(narrow(x0)) | (static_cast<uint32_t>(narrow(x1)) << 16);
       }
+      __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, rC, off[p], 0, 0);
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next block row
   }

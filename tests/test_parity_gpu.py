@@ -389,6 +389,9 @@ PACKED_CASES = [
     (300, 261, 200, "f16", "f32", dict(), 2),                         # B (and C) rows unaligned
     (517, 1003, 77, "bf16", "bf16", dict(bias=True, resid=True), 3),  # both, 16-bit C, residual
     (257, 777, 130, "f16", "f16", dict(bias=True, gelu=True), 3),
+    # even N that is not a multiple of 8: 16-bit C stored two columns per lane
+    (300, 266, 200, "bf16", "bf16", dict(bias=True, resid=True), 2),
+    (129, 1002, 64, "f16", "f16", dict(), 2),
 ]
 
 
@@ -396,7 +399,7 @@ PACKED_CASES = [
 def test_packed_operands(g, case):
     """16-bit operands whose rows are not 16-byte multiples are copied into
     zero-padded rows and run through a 16-byte-load kernel; C rows that are not
-    16-byte multiples are stored element by element. Every element, float and
+    16-byte multiples are stored one or two elements per lane. Every element, float and
     small-integer inputs, two runs of the same plan."""
     M, N, K, dtype, out_dtype, epi, bits = PACKED_CASES[case]
     plan = g.Plan(M, N, K, dtype, out_dtype=out_dtype, **epi)
