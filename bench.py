@@ -7,8 +7,9 @@ fraction of the gfx950 dense bf16 matrix peak; the same 4096^3 product with
 fp32 inputs (SGEMM) is measured beside it against the fp32 peak. Inputs are
 seeded synthetic uniform[-1, 1) matrices already resident in HBM.
 
-Protocol: W untimed warm-up calls, then K timed calls, each bracketed by a pair
-of HIP events recorded on the stream the kernel runs on; per-call time is the
+Protocol: W untimed warm-up calls (continued until the product has run for at
+least SETTLE_S seconds, so the clocks have left their idle state), then K timed
+calls, each bracketed by a pair of HIP events recorded on the stream the kernel runs on; per-call time is the
 median (throughput) and the mean (roofline: average launch duration). The
 whole timed region is also bracketed by device synchronisation.
 
@@ -27,6 +28,12 @@ import time
 
 PEAK_TFLOPS = {"bf16": 2516.6, "f16": 2516.6, "f32": 157.3}  # 256 CU x 2.4 GHz x {4096, 256}
 PEAK_HBM_GBS = 8000.0
+# Minimum length of the untimed warm-up. Coming out of idle the GPU's clocks take
+# tens of milliseconds to settle: at 4096^3 bf16 the per-call median after 10 calls
+# (1.3 ms) is 127-131 us, after 0.05 s of calls 121 us, and it stays there up to
+# 3 s (the vendor library's product goes 120 -> 106 us alike). The timed calls are
+# meant to see the steady state, so the warm-up lasts W calls and at least this long.
+SETTLE_S = 0.25
 ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
@@ -69,12 +76,20 @@ def parse():
     return ap.parse_args()
 
 
-def time_calls(fn, steps, warmup):
-    """Median and mean per-call milliseconds over `steps` event-bracketed calls."""
+def time_calls(fn, steps, warmup, settle_s=None):
+    """Median and mean per-call milliseconds over `steps` event-bracketed calls,
+    after `warmup` untimed calls that continue until the GPU has run the product
+    for `settle_s` seconds (see SETTLE_S)."""
     import torch
+    settle_s = SETTLE_S if settle_s is None else settle_s
+    t_warm = time.perf_counter()
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
+    while time.perf_counter() - t_warm < settle_s:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
     st = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(steps)]
@@ -372,6 +387,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warmup_min_s": SETTLE_S,
         "ms_per_step": round(head["median_ms"], 5),
         "higher_is_better": True,
         "scaling": "weak",
