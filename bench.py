@@ -258,10 +258,12 @@ def symbol_to_config(sym: str):
     if m:
         t, bm, bn, wm, wn, sa, kr, r = m.groups()
         return f"m16d_{t}_{bm}x{bn}x64_w{wm}x{wn}_a{sa}_b{kr}_r{r}"
-    m = re.search(r"gemm_m16n_kernel<g15::(\w+)_t, (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)>", sym)
+    m = re.search(r"gemm_m16n_kernel<g15::(\w+)_t, (\d+), (\d+), (\d+), (\d+), (\d+), (\d+),"
+                  r" (true|false)>", sym)
     if m:
-        t, bm, bn, wm, wn, sa, sb = m.groups()
-        return f"m16n_{t}_{bm}x{bn}x64_w{wm}x{wn}_a{sa}_b{sb}"
+        t, bm, bn, wm, wn, sa, sb, brow = m.groups()
+        kind = "m16t" if brow == "true" else "m16n"
+        return f"{kind}_{t}_{bm}x{bn}x64_w{wm}x{wn}_a{sa}_b{sb}"
     m = re.search(r"gemm_f32d_kernel<(\d+), (\d+), (\d+), (\d+), (\d+)>", sym)
     if m:
         bm, bn, wm, wn, sa = m.groups()

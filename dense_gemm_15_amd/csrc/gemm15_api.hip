@@ -148,15 +148,15 @@ struct TunedRow {
 const TunedRow kTuned[] = {
     {false, 4096, 4096, 4096, 1, "m16d_{t}_256x256x64_w4x2_a3_b4_r1"},
     {false, 8192, 8192, 8192, 1, "m16d_{t}_256x256x64_w4x2_a3_b4_r1"},
-    {false, 2048, 2048, 2048, 1, "m16d_{t}_128x128x64_w2x2_a3_b4_r2"},
+    {false, 2048, 2048, 2048, 1, "m16d_{t}_128x128x64_w2x2_a3_b4_r1"},
     {false, 1024, 1024, 1024, 1, "m16d_{t}_64x128x64_w2x2_a4_b4_r2"},
     {false, 512, 512, 512, 1, "m16d_{t}_64x128x64_w2x2_a4_b4_r2"},
-    {false, 8192, 3072, 768, 1, "m16d_{t}_128x256x64_w2x4_a3_b4_r1"},  // encoder FFN, first GEMM
+    {false, 8192, 3072, 768, 1, "m16t_{t}_128x128x64_w2x2_a2_b2"},     // encoder FFN, first GEMM
     {false, 8192, 768, 3072, 1, "m16d_{t}_128x256x64_w2x4_a3_b4_r1"},  // encoder FFN, second GEMM
-    {false, 512, 512, 64, 96, "m16d_{t}_128x128x64_w2x2_a3_b4_r1"},    // 96 heads of Q K^T
+    {false, 512, 512, 64, 96, "m16d_{t}_128x256x64_w2x4_a3_b4_r1"},    // 96 heads of Q K^T
     {false, 4096, 4096, 4096, 1, "m16n_{t}_256x256x64_w2x4_a3_b2"},
     {false, 2048, 2048, 2048, 1, "m16n_{t}_128x128x64_w2x2_a3_b3"},
-    {false, 8192, 3072, 768, 1, "m16n_{t}_256x256x64_w2x4_a3_b2"},
+    {false, 8192, 3072, 768, 1, "m16n_{t}_128x128x64_w2x2_a2_b2"},
     {false, 8192, 768, 3072, 1, "m16n_{t}_128x256x64_w2x4_a3_b3"},
     {false, 512, 512, 64, 96, "m16n_{t}_128x128x64_w2x2_a2_b2"},
     {true, 4096, 4096, 4096, 1, "f32d_256x256x16_w4x2_a3"},
