@@ -113,17 +113,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16d_kernel(LaunchArgs a)
   };
 
   // B: thread block b covers KR rows (k) x 8 columns (n) of the slice. KR = 8:
-  // (kb, nb) = (b & 7, b >> 3). KR = 4: nb = (b & 7) | (b >> 7) << 3 and
-  // kq = (b >> 3) & 15, so eight neighbouring lanes read 128 contiguous bytes of
-  // one row. The block is transposed in registers and stored n-major.
+  // (kb, nb) = (b & 7, b >> 3). KR = 4 (one block per thread): the bits of b, from
+  // the lowest, give nb bits 0-1, kq bit 0, kq bit 3, the other nb bits, kq bits
+  // 1-2 (kq = k / 4). The transposed store of column c writes row 8 nb + c at chunk
+  // kq / 2 (permuted by nb & 3), half kq & 1; gfx950's LDS takes 16 lanes of an
+  // 8-byte store per pass over 32 banks, and these 16 lanes then hit 16 different
+  // (chunk, half) slots: no bank conflicts (nb & 7 on the low lanes had 2-way
+  // conflicts in every store). Each load still reads 256 contiguous bytes of a row
+  // with 16 lanes. The block is transposed in registers and stored n-major.
   u32x4 rb[NSB][NB][KR];
+  constexpr int NBH = BN == 256 ? 3 : BN == 128 ? 2 : 1;  // nb bits above the lowest two
+  static_assert(KR == 8 || BN / 32 == (1 << NBH), "KR = 4 mapping: BN of 64, 128 or 256");
   auto b_coords = [&](int b, int& kr0, int& nb) {
     if constexpr (KR == 8) {
       kr0 = (b & 7) * 8;
       nb = b >> 3;
     } else {
-      kr0 = ((b >> 3) & 15) * 4;
-      nb = (b & 7) | ((b >> 7) << 3);
+      const int kq = ((b >> 2) & 1) | (((b >> 3) & 1) << 3) | (((b >> (4 + NBH)) & 3) << 1);
+      kr0 = kq * 4;
+      nb = (b & 3) | (((b >> 4) & ((1 << NBH) - 1)) << 2);
     }
   };
   uint32_t b_voff[NB][KR];
