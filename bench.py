@@ -16,7 +16,7 @@ whole timed region is also bracketed by device synchronisation.
 ``cpu_baseline`` times the fp64 host oracle on a bounded row-block of the same
 product on the host's cores.
 
-Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--all] [--no-cpu]
+Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--all] [--no-cpu] [--vendor]
 """
 from __future__ import annotations
 
@@ -71,6 +71,9 @@ def parse():
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr + json)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--json-out", default=None, help="write per-workload results here")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time torch.mm (the vendor library) and this library on the "
+                         "4096^3 bf16 product with bf16 output, for context")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -164,6 +167,27 @@ def gemm_workload(g, name, steps, warmup, graph=False, b_layout="kn"):
         r.update(graph_ms=gms, graph_tflops=flops / (gms * 1e-3) / 1e12,
                  graph_gbs=byts / (gms * 1e-3) / 1e9)
     return r
+
+
+def vendor_reference(g, steps, warmup):
+    """4096^3 bf16 with bf16 output: torch.mm (the vendor library) and this library,
+    timed alike, one after the other on the same inputs. Context only."""
+    import torch
+    import synth
+    A, B = synth.gemm_inputs("bf16_4096")
+    dev = torch.device("cuda")
+    A, B = A.to(dev), B.to(dev)
+    n = A.shape[0]
+    C = torch.empty((n, n), dtype=torch.bfloat16, device=dev)
+    plan = g.Plan(n, n, n, "bf16", out_dtype="bf16")
+    flops = 2 * n * n * n
+    out = {}
+    for tag, fn in (("torch_mm", lambda: torch.mm(A, B, out=C)),
+                    ("gemm15", lambda: plan.run(A, B, out=C))):
+        med, mean, _ = time_calls(fn, steps, warmup)
+        out[tag] = dict(median_ms=med, mean_ms=mean, tflops=flops / (med * 1e-3) / 1e12)
+    out["gemm15"]["config"] = plan.config_name
+    return out
 
 
 def ffn_workload(g, steps, warmup, b_layout="kn"):
@@ -349,6 +373,9 @@ def main():
     print(f"[bench] {json.dumps(f32)}", file=sys.stderr, flush=True)
 
     extra = {}
+    if args.vendor:
+        extra["vendor_bf16_out"] = vendor_reference(g, args.steps, args.warmup)
+        print(f"[bench] vendor {json.dumps(extra['vendor_bf16_out'])}", file=sys.stderr, flush=True)
     if args.copy_calibration:
         import torch as _t
         src = _t.empty(64 * 2**20, dtype=_t.float32, device="cuda")  # 256 MiB
