@@ -17,6 +17,7 @@ whole timed region is also bracketed by device synchronisation.
 product on the host's cores.
 
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--all] [--no-cpu] [--vendor]
+       [--ladder]
 """
 from __future__ import annotations
 
@@ -71,6 +72,9 @@ def parse():
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr + json)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--json-out", default=None, help="write per-workload results here")
+    ap.add_argument("--ladder", action="store_true",
+                    help="also time the optimisation ladder V0..V4 on the 4096^3 fp16 product "
+                         "and the fp16-accumulation variant")
     ap.add_argument("--vendor", action="store_true",
                     help="also time torch.mm (the vendor library) and this library on the "
                          "4096^3 bf16 product with bf16 output, for context")
@@ -167,6 +171,57 @@ def gemm_workload(g, name, steps, warmup, graph=False, b_layout="kn"):
         r.update(graph_ms=gms, graph_tflops=flops / (gms * 1e-3) / 1e12,
                  graph_gbs=byts / (gms * 1e-3) / 1e9)
     return r
+
+
+# The optimisation ladder of the DeepGEMM page (section 4.1) on this chip: V0 one
+# thread per element, V1 LDS tiles, V2 register tiles, V3 padded LDS rows (and
+# V3a, padding that keeps 16-byte rows: section 5.2), V4 matrix instructions on
+# the same 64 x 64 tile, then this library's own choice.
+LADDER = [("V0 one thread per element", "ladder_v0_f16_16x16"),
+          ("V1 LDS tiles", "ladder_v1_f16_16x16x16"),
+          ("V2 register tiles", "ladder_v2_f16_64x64x16"),
+          ("V3 padded LDS rows (65 floats)", "ladder_v3_f16_64x64x16"),
+          ("V3a aligned padding (68 floats)", "ladder_v3a_f16_64x64x16"),
+          ("V4 matrix instructions", "mfma16_f16_64x64_w2x2"),
+          ("this library", None)]
+
+
+def ladder_workload(g, steps):
+    """Each rung on the 4096^3 fp16 product (fp32 accumulation, fp32 C), with as
+    many calls as fit about half a second (at least 3, at most `steps`); then the
+    fp16-accumulating rung and its maximum absolute difference from this
+    library's fp32-accumulating result on the same inputs (DeepGEMM page, section
+    3.4)."""
+    import torch
+    import synth
+    A, B = synth.gemm_inputs("fp16_4096")
+    dev = torch.device("cuda")
+    A, B = A.to(dev), B.to(dev)
+    n = A.shape[0]
+    flops = 2 * n * n * n
+    rungs = []
+    outs = {}
+    for tag, cfg in LADDER + [("V3, fp16 accumulator", "ladder_v3acc16_f16_64x64x16")]:
+        plan = g.Plan(n, n, n, "f16", config=cfg if cfg else -1)
+        C = torch.empty((n, n), dtype=torch.float32, device=dev)
+        run = lambda: plan.run(A, B, out=C)  # noqa: E731
+        t0 = time.perf_counter()
+        run()
+        torch.cuda.synchronize()
+        first = time.perf_counter() - t0
+        k = max(3, min(steps, int(0.5 / max(first, 1e-6))))
+        med, mean, _ = time_calls(run, k, 1, settle_s=min(SETTLE_S, 10 * first))
+        rungs.append(dict(rung=tag, config=plan.config_name, calls=k, median_ms=med,
+                          tflops=flops / (med * 1e-3) / 1e12,
+                          frac_peak=flops / (med * 1e-3) / 1e12 / PEAK_TFLOPS["f16"]))
+        print(f"[bench] ladder {json.dumps(rungs[-1])}", file=sys.stderr, flush=True)
+        if cfg is None or "acc16" in (cfg or ""):
+            outs[tag] = C
+    ref = outs["this library"].double()
+    err16 = (outs["V3, fp16 accumulator"].double() - ref).abs().max().item()
+    return dict(rungs=rungs, fp16_accumulation_max_abs_diff=err16,
+                note="fp16-accumulator result against this library's fp32-accumulating "
+                     "result on the same 4096^3 fp16 inputs")
 
 
 def vendor_reference(g, steps, warmup):
@@ -373,6 +428,10 @@ def main():
     print(f"[bench] {json.dumps(f32)}", file=sys.stderr, flush=True)
 
     extra = {}
+    if args.ladder:
+        extra["ladder"] = ladder_workload(g, args.steps)
+        print(f"[bench] ladder fp16-accumulation max abs diff "
+              f"{extra['ladder']['fp16_accumulation_max_abs_diff']:.4g}", file=sys.stderr, flush=True)
     if args.vendor:
         extra["vendor_bf16_out"] = vendor_reference(g, args.steps, args.warmup)
         print(f"[bench] vendor {json.dumps(extra['vendor_bf16_out'])}", file=sys.stderr, flush=True)

@@ -69,6 +69,8 @@ struct Registry {
     all.insert(all.end(), p, p + n);
     n = gemv_entries(&p);
     all.insert(all.end(), p, p + n);
+    n = ladder_entries(&p);
+    all.insert(all.end(), p, p + n);
   }
 };
 
@@ -291,7 +293,7 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
     double best_cost = 0;
     for (int i = 0; i < static_cast<int>(all.size()); ++i) {
       const KernelEntry& k = all[i];
-      if (k.kind == KIND_GEMV || !use(k)) continue;
+      if (k.kind == KIND_GEMV || k.kind == KIND_LADDER || !use(k)) continue;
       if (!cfg_fits(k, dtype, va, vb, dev, M, np, kp, epi.out_dtype, b_nk)) continue;
       const double c = cfg_cost(k, M, N, K, batch, dev);
       if (best < 0 || c < best_cost * 0.999) {

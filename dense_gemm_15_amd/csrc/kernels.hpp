@@ -14,6 +14,7 @@ enum KernelKind : int {
   KIND_MFMA16 = 1,  // bf16 / fp16 MFMA kernel
   KIND_F32 = 2,     // fp32 MFMA kernel
   KIND_GEMV = 3,    // few-row split-K kernel (M small)
+  KIND_LADDER = 4,  // optimisation-ladder rungs: run only when forced by name
 };
 
 // One launch: a strided batch of row-major products C = epi(A x B).
@@ -68,5 +69,6 @@ int mfma16_nt_entries(const KernelEntry** out);
 int f32_entries(const KernelEntry** out);
 int f32_dlds_entries(const KernelEntry** out);
 int gemv_entries(const KernelEntry** out);
+int ladder_entries(const KernelEntry** out);
 
 }  // namespace g15

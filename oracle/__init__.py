@@ -72,6 +72,7 @@ def load(path: str | None = None):
                                 vp, i32]
     lib.oracle_gemm_at.argtypes = [i64, i64, i64, i32, vp, vp, ctypes.c_uint, dp, vp, i32, vp,
                                    i64, vp, vp, vp, vp]
+    lib.oracle_gemm_f16acc.argtypes = [i64, i64, i64, vp, vp, vp]
     lib.oracle_threads.restype = i32
     if path is None:
         _lib = lib
@@ -155,6 +156,24 @@ def gemm(A, B, dtype, flags: int = 0, scale: float = 1.0, bias=None, resid=None,
     if rc != 0:
         raise ValueError(f"oracle_gemm rejected its arguments (code {rc})")
     return ref, s
+
+
+def gemm_f16acc(A, B, lib=None):
+    """fp16 A [M,K], B [K,N] (bit patterns) with every accumulator held in fp16:
+    one round-to-nearest-even per k of acc + a*b (DeepGEMM page, section 3.4's
+    FP16-accumulation variant). Exact for inputs on the 2^-10 grid in [-1, 1].
+    Returns [M,N] float64 (fp16 values)."""
+    lib = lib or load()
+    A = _buf(A, "f16")
+    B = _buf(B, "f16")
+    M, K = A.shape
+    K2, N = B.shape
+    assert K == K2, "inner dimensions differ"
+    ref = np.empty((M, N), np.float64)
+    rc = lib.oracle_gemm_f16acc(M, N, K, A.ctypes.data, B.ctypes.data, ref.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_gemm_f16acc rejected its arguments (code {rc})")
+    return ref
 
 
 def gemm_at(A, B, dtype, rows, cols, flags: int = 0, scale: float = 1.0, bias=None, resid=None,

@@ -256,6 +256,32 @@ int oracle_gemm_at(int64_t M, int64_t N, int64_t K, int dtype, const void* A, co
   return 0;
 }
 
+/*
+ * FP16 accumulation (DeepGEMM page, section 3.4: the variant it warns against,
+ * "run one version accumulating in FP16 and one in FP32 on the same random
+ * inputs and compare the maximum absolute error"). fp16 A and B, no epilogue:
+ * for each element the accumulator is an fp16 value, and each k in sequence
+ * replaces it by RNE16(acc + a*b), the sum formed exactly and rounded once (a
+ * fused multiply-add in fp16). acc + a*b is formed in double, which is exact
+ * when it fits 53 bits: always for inputs that are multiples of 2^-10 in
+ * [-1, 1] (every quantity is then a multiple of 2^-20 below 2^16). ref receives
+ * the final accumulators (fp16 values, as doubles).
+ */
+int oracle_gemm_f16acc(int64_t M, int64_t N, int64_t K, const void* A, const void* B,
+                       double* ref) {
+  if (M < 1 || N < 1 || K < 1 || !A || !B || !ref) return -1;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int64_t i = 0; i < M; ++i)
+    for (int64_t j = 0; j < N; ++j) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k)
+        acc = round_fmt(acc + dec_one(OR_F16, A, i * K + k) * dec_one(OR_F16, B, k * N + j), 11,
+                        -14, 15);
+      ref[i * N + j] = acc;
+    }
+  return 0;
+}
+
 /* Number of OpenMP threads a parallel region here would use. */
 int oracle_threads(void) {
 #ifdef _OPENMP

@@ -52,6 +52,13 @@ def small_int(seed: int, shape, dtype: str, lo: int = -8, hi: int = 8) -> torch.
     return _cast(rng.integers(lo, hi + 1, size=tuple(shape)).astype(np.float64), dtype)
 
 
+def grid(seed: int, shape, dtype: str, step: float = 2.0 ** -10) -> torch.Tensor:
+    """Multiples of ``step`` uniform in [-1, 1] (exact in fp16 for step 2^-10)."""
+    rng = np.random.default_rng(seed)
+    n = int(round(1.0 / step))
+    return _cast(rng.integers(-n, n + 1, size=tuple(shape)).astype(np.float64) * step, dtype)
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """The raw element bits of a CPU tensor as a numpy array.
 

@@ -321,4 +321,45 @@ def pin_check_logic(lib):
     assert not oracle.check(off, ref, s, exact=True, lib=lib)["ok"]
 
 
+def pin_f16acc_stepwise(lib):
+    """FP16 accumulation (DeepGEMM page, section 3.4) against a step-by-step numpy
+    model: the exact acc + a*b in float64, rounded to float16 by numpy's own
+    conversion (round to nearest even) at every k. Inputs on the 2^-10 grid, where
+    the float64 sum is exact."""
+    r = _rng(41)
+    for M, N, K in [(3, 4, 1), (5, 7, 33), (2, 3, 257)]:
+        A = (r.integers(-1024, 1025, (M, K)) / 1024).astype(np.float16)
+        B = (r.integers(-1024, 1025, (K, N)) / 1024).astype(np.float16)
+        got = oracle.gemm_f16acc(A.view(np.uint16), B.view(np.uint16), lib=lib)
+        want = np.zeros((M, N))
+        for i in range(M):
+            for j in range(N):
+                acc = np.float16(0)
+                for k in range(K):
+                    acc = np.float16(np.float64(acc) + np.float64(A[i, k]) * np.float64(B[k, j]))
+                want[i, j] = acc
+        assert np.array_equal(got, want), (M, N, K)
+
+
+def pin_f16acc_closed_forms(lib):
+    """FP16 accumulation: B = I returns A exactly; K = 1 returns RNE16(a b); with
+    K = 2048 random products the fp16 accumulator is off the exact sum by far more
+    than fp32 accumulation would be (the error the page warns about)."""
+    r = _rng(42)
+    A = (r.integers(-1024, 1025, (6, 9)) / 1024).astype(np.float16)
+    I = np.eye(9, dtype=np.float16)
+    assert np.array_equal(oracle.gemm_f16acc(A.view(np.uint16), I.view(np.uint16), lib=lib),
+                          A.astype(np.float64))
+    a = (r.integers(-1024, 1025, (8, 1)) / 1024).astype(np.float16)
+    b = (r.integers(-1024, 1025, (1, 8)) / 1024).astype(np.float16)
+    want = (a.astype(np.float64) @ b.astype(np.float64)).astype(np.float16).astype(np.float64)
+    assert np.array_equal(oracle.gemm_f16acc(a.view(np.uint16), b.view(np.uint16), lib=lib), want)
+    A = (r.integers(-1024, 1025, (4, 2048)) / 1024).astype(np.float16)
+    B = (r.integers(-1024, 1025, (2048, 4)) / 1024).astype(np.float16)
+    exact = A.astype(np.float64) @ B.astype(np.float64)
+    err16 = np.abs(oracle.gemm_f16acc(A.view(np.uint16), B.view(np.uint16), lib=lib) - exact).max()
+    err32 = np.abs((A.astype(np.float32) @ B.astype(np.float32)).astype(np.float64) - exact).max()
+    assert err16 > 1e-3 and err16 > 100 * err32, (err16, err32)
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -55,6 +55,10 @@ MUTANTS = [
     ("no_overflow_to_inf", "if (r >= ldexp(1.0, emax + 1)) r = INFINITY;", ""),
     ("ulp_off_by_one", "return ldexp(1.0, lead - (p - 1));", "return ldexp(1.0, lead - p);"),
     ("a_row_stride_N", "arow[k] = dec_one(dtype, A, i * K + k)", "arow[k] = dec_one(dtype, A, i * N + k)"),
+    ("f16acc_not_rounded", "acc = round_fmt(acc + dec_one(OR_F16, A, i * K + k) * dec_one(OR_F16, B, k * N + j), 11,\n                        -14, 15);",
+     "acc = acc + dec_one(OR_F16, A, i * K + k) * dec_one(OR_F16, B, k * N + j);"),
+    ("f16acc_bf16_rounding", "11,\n                        -14, 15);", "8,\n                        -126, 127);"),
+    ("f16acc_transposed_B", "dec_one(OR_F16, B, k * N + j)", "dec_one(OR_F16, B, j * K + k)"),
 ]
 
 RUNNER = r"""

@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 import synth
 from tests import gpu_cases as gc
 
@@ -53,7 +54,8 @@ def _dtype_of(name):
 
 
 CONFIGS = _configs()
-TILE_CONFIGS = [c for c in CONFIGS if not c.startswith("gemv") and not c.startswith("m16n")]
+TILE_CONFIGS = [c for c in CONFIGS if not c.startswith("gemv") and not c.startswith("m16n")
+                and "acc16" not in c]
 NT_CONFIGS = [c for c in CONFIGS if c.startswith("m16n")]
 GEMV_CONFIGS = [c for c in CONFIGS if c.startswith("gemv")]
 
@@ -63,7 +65,7 @@ def test_each_config_ragged(g, name):
     """Every compiled configuration on shapes spanning several tiles with ragged tails."""
     dtype = _dtype_of(name)
     idx = g.config_index(name)
-    vec = "scalar" not in name and not name.startswith("simple")
+    vec = "scalar" not in name and not name.startswith(("simple", "ladder"))
     parts = name.split("_")
     tile = [p for p in parts if "x" in p and p[0].isdigit()][0] if not name.startswith("simple") \
         else "64x64"
@@ -147,6 +149,59 @@ def test_gemv_epilogue_and_batch(g, dtype):
     for b in range(nb):
         r = gc.check_full(Cs[b], As[b], Bs[b], dtype)
         assert r["ok"], (b, r)
+
+
+def test_ladder_fp16_accumulation_exact(g):
+    """The fp16-accumulating rung of the optimisation ladder equals the oracle's
+    fp16-accumulation mode bit for bit (one RNE to fp16 per k of acc + a*b) on
+    inputs of the 2^-10 grid, on shapes spanning several 64x64 tiles with ragged
+    edges, also strided-batched."""
+    name = "ladder_v3acc16_f16_64x64x16"
+    for si, (M, N, K) in enumerate([(130, 70, 300), (64, 64, 16), (1, 3, 1000)]):
+        say(f"[{name}] M={M} N={N} K={K}")
+        A = synth.grid(900 + si, (M, K), "f16")
+        B = synth.grid(910 + si, (K, N), "f16")
+        plan = g.Plan(M, N, K, "f16", config=name)
+        C = gc.run_gpu(plan, A, B).double().numpy()
+        ref = oracle.gemm_f16acc(synth.bits(A), synth.bits(B))
+        assert np.array_equal(C, ref), (M, N, K, np.abs(C - ref).max())
+    M, N, K, nb = 70, 90, 130, 3
+    As = torch.stack([synth.grid(920 + b, (M, K), "f16") for b in range(nb)])
+    Bs = torch.stack([synth.grid(930 + b, (K, N), "f16") for b in range(nb)])
+    plan = g.Plan(M, N, K, "f16", config=name, batch_hint=nb)
+    dev = torch.device("cuda")
+    Cs = plan.run_batched(As.to(dev), Bs.to(dev))
+    torch.cuda.synchronize()
+    for b in range(nb):
+        ref = oracle.gemm_f16acc(synth.bits(As[b]), synth.bits(Bs[b]))
+        assert np.array_equal(Cs[b].cpu().double().numpy(), ref), b
+
+
+def test_accumulation_error_study(g):
+    """DeepGEMM page, section 3.4: the same random fp16 inputs through the fp32- and
+    the fp16-accumulating rung; against the fp64 product the fp16 accumulator's
+    maximum absolute error is orders of magnitude larger (here: > 100x), while the
+    fp32 one is within the parity tolerance."""
+    M, N, K = 256, 192, 4096
+    A, B = gc.inputs(M, N, K, "f16", 940)
+    ref, s = oracle.gemm(synth.bits(A), synth.bits(B), "f16")
+    errs = {}
+    for name in ("ladder_v3_f16_64x64x16", "ladder_v3acc16_f16_64x64x16"):
+        C = gc.run_gpu(g.Plan(M, N, K, "f16", config=name), A, B).double().numpy()
+        errs[name] = np.abs(C - ref).max()
+        if "acc16" not in name:
+            r = oracle.check(C.astype(np.float32), ref, s, "f32")
+            assert r["ok"], r
+    say(f"[accumulation] max abs error fp32-acc {errs['ladder_v3_f16_64x64x16']:.3e}, "
+        f"fp16-acc {errs['ladder_v3acc16_f16_64x64x16']:.3e}")
+    assert errs["ladder_v3acc16_f16_64x64x16"] > 100 * errs["ladder_v3_f16_64x64x16"]
+
+
+def test_ladder_never_chosen_automatically(g):
+    """The ladder rungs run only when forced by name."""
+    for M, N, K in [(4096, 4096, 4096), (127, 1000, 771), (1, 3, 5), (300, 264, 200)]:
+        for dt in ("f16", "bf16", "f32"):
+            assert not g.Plan(M, N, K, dt).config_name.startswith("ladder")
 
 
 EPI_CASES = [
