@@ -39,12 +39,29 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 
 
-def kernel_source_hash() -> str:
-    """Hash of the device sources; counter data taken from other sources is stale."""
+# Sources each measured kernel is built from (its file and the headers it
+# includes): its counter data are stale once any of them changes.
+_COMMON = ["kernels.hpp", "device_common.hpp"]
+KERNEL_SOURCES = {
+    "m16d": ["kernel_mfma16_dlds.hip", "m16_common.hpp"] + _COMMON,
+    "m16n": ["kernel_mfma16_nt.hip", "m16_common.hpp"] + _COMMON,
+    "m16t": ["kernel_mfma16_nt.hip", "m16_common.hpp"] + _COMMON,
+    "f32d": ["kernel_f32_dlds.hip"] + _COMMON,
+    "gemv": ["kernel_gemv.hip"] + _COMMON,
+}
+
+
+def kernel_source_hash(config: str | None = None) -> str:
+    """Hash of the device sources of configuration `config` (all of them when the
+    configuration's family is not listed)."""
     import glob
     import hashlib
+    csrc = os.path.join(ROOT, "dense_gemm_15_amd", "csrc")
+    names = KERNEL_SOURCES.get((config or "").split("_")[0])
+    files = ([os.path.join(csrc, n) for n in names] if names
+             else sorted(glob.glob(os.path.join(csrc, "*"))))
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "dense_gemm_15_amd", "csrc", "*"))):
+    for f in files:
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + fh.read())
     return h.hexdigest()[:16]
@@ -52,16 +69,16 @@ def kernel_source_hash() -> str:
 
 def measured_traffic(kernel_config: str):
     """Bytes per launch from the committed FETCH_SIZE / WRITE_SIZE summary, or None
-    when it is missing or was taken from different kernel sources."""
+    when it is missing or was taken from other sources of that kernel."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_hash") != kernel_source_hash():
-        return None
     row = t.get("kernels", {}).get(kernel_config)
-    return None if row is None else row["traffic_bytes"]
+    if row is None or row.get("source_hash") != kernel_source_hash(kernel_config):
+        return None
+    return row.get("traffic_bytes")
 
 
 def parse():
@@ -393,13 +410,15 @@ def summarize(db_dir: str, kind: str) -> None:
         cfg = symbol_to_config(name)
         if cfg is None or cn not in ("FETCH_SIZE", "WRITE_SIZE"):
             continue
-        t["kernels"].setdefault(cfg, {})[cn + "_kib"] = sum(v) / len(v)
+        row = t["kernels"].setdefault(cfg, {})
+        row[cn + "_kib"] = sum(v) / len(v)
+        row["source_hash"] = kernel_source_hash(cfg)
     sc = t.get("scale", {})
     for cfg, row in t["kernels"].items():
         if "FETCH_SIZE_kib" in row and "WRITE_SIZE_kib" in row and sc:
             row["traffic_bytes"] = round(row["FETCH_SIZE_kib"] * 1024 * sc.get("FETCH_SIZE", 1.0)
                                          + row["WRITE_SIZE_kib"] * 1024 * sc.get("WRITE_SIZE", 1.0))
-    t["source_hash"] = kernel_source_hash()
+    t.pop("source_hash", None)
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(t, f, indent=1, sort_keys=True)
 
