@@ -429,8 +429,8 @@ def main():
         return
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the product shards by rows of A across GPUs, which is not measured here)",
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported: the product "
+              "would shard by rows of A across GPUs, and only one GPU's share is measured",
               file=sys.stderr)
         sys.exit(2)
     import torch
