@@ -320,6 +320,48 @@ def qk_workload(g, steps, warmup, b_layout="kn"):
                 graph_frac_hbm=by / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS)
 
 
+def attention_workload(g, steps, warmup):
+    """Attention continuation (tutorial page, section 2: Softmax(Q K^T) V) on the 96
+    heads of sequence 512, dimension 64: S = Q K^T (fp32), P = softmax(S) row by row
+    (bf16), O = P V (fp32), each stage timed alone and the chain as a whole. The
+    softmax is HBM-bound: its bytes are S read once and P written once."""
+    import torch
+    import synth
+    Q, Kt, V = synth.attention_inputs()
+    dev = torch.device("cuda")
+    Q, Kt, V = Q.to(dev), Kt.to(dev), V.to(dev)
+    nb, Sq, D = Q.shape
+    qk = g.Plan(Sq, Sq, D, "bf16", batch_hint=nb)
+    pv = g.Plan(Sq, D, Sq, "bf16", batch_hint=nb)
+    S = torch.empty((nb, Sq, Sq), dtype=torch.float32, device=dev)
+    P = torch.empty((nb, Sq, Sq), dtype=torch.bfloat16, device=dev)
+    O = torch.empty((nb, Sq, D), dtype=torch.float32, device=dev)
+    stages = {
+        "qk": (lambda: qk.run_batched(Q, Kt, out=S), 2 * nb * Sq * Sq * D,
+               nb * (2 * Sq * D * 2 + Sq * Sq * 4), qk.config_name),
+        "softmax": (lambda: g.softmax_rows(S, 1.0, "bf16", out=P), 0, nb * Sq * Sq * (4 + 2),
+                    "softmax_rows"),
+        "pv": (lambda: pv.run_batched(P, V, out=O), 2 * nb * Sq * Sq * D,
+               nb * (Sq * Sq * 2 + Sq * D * 2 + Sq * D * 4), pv.config_name),
+    }
+    out = {}
+    for name, (fn, fl, by, cfg) in stages.items():
+        med, mean, _ = time_calls(fn, steps, warmup)
+        gms = time_graph(fn)
+        out[name] = dict(config=cfg, median_ms=med, graph_ms=gms, flops=fl, bytes=by,
+                         gbs=by / (gms * 1e-3) / 1e9, frac_hbm=by / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                         tflops=fl / (gms * 1e-3) / 1e12)
+
+    def chain():
+        qk.run_batched(Q, Kt, out=S)
+        g.softmax_rows(S, 1.0, "bf16", out=P)
+        pv.run_batched(P, V, out=O)
+    med, mean, _ = time_calls(chain, steps, warmup)
+    gms = time_graph(chain)
+    out["chain"] = dict(median_ms=med, graph_ms=gms)
+    return dict(workload="attention_96x512x64", stages=out)
+
+
 def cpu_baseline(target_s=15.0):
     """The fp64 oracle on the 4096^3 bf16 product on all host cores: a row block
     sized to about `target_s` seconds, or the whole product repeated until that
@@ -472,6 +514,8 @@ def main():
               file=sys.stderr, flush=True)
         extra["qk"] = qk_workload(g, args.steps, args.warmup)
         print(f"[bench] {json.dumps(extra['qk'])}", file=sys.stderr, flush=True)
+        extra["attention"] = attention_workload(g, args.steps, args.warmup)
+        print(f"[bench] {json.dumps(extra['attention'])}", file=sys.stderr, flush=True)
         # the same products with B stored transposed (weights [out, in], K as stored)
         extra["bf16_4096_nt"] = gemm_workload(g, "bf16_4096", args.steps, args.warmup,
                                               b_layout="nk")

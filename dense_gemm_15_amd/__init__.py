@@ -67,6 +67,8 @@ SIGNATURES = {
     "gemm_run_strided_batched": (ctypes.c_int, [_VP, _I64, _VP, _I64, _VP, _I64, _VP, _VP, _I64,
                                                 _VP, _I64, _VP]),
     "gemm_plan_destroy": (None, [_VP]),
+    "gemm_softmax_rows": (ctypes.c_int, [_VP, _I64, _I64, _I64, ctypes.c_float, _VP, _I64, _I32,
+                                         _VP]),
     "gemm_last_error": (ctypes.c_int, []),
     "gemm_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "gemm_plan_describe": (ctypes.c_int, [_VP, ctypes.c_char_p, ctypes.c_size_t]),
@@ -228,3 +230,23 @@ class Plan:
         if rc != 0:
             raise GemmError(rc, "gemm_run_strided_batched")
         return out
+
+
+def softmax_rows(S, scale: float = 1.0, out_dtype: str = "bf16", out=None, stream=None):
+    """P = softmax(scale * S) over the last dimension of a contiguous fp32 cuda tensor
+    (gemm_softmax_rows); P has S's shape and type out_dtype."""
+    if S.device.type != "cuda" or S.dtype != torch.float32 or not S.is_contiguous():
+        raise ValueError("S must be a contiguous float32 cuda tensor")
+    cols = S.shape[-1]
+    rows = S.numel() // cols
+    if out is None:
+        out = torch.empty(S.shape, dtype=_TORCH[_CODE[out_dtype]], device=S.device)
+    elif (out.shape != S.shape or out.dtype != _TORCH[_CODE[out_dtype]] or not out.is_contiguous()
+          or out.device != S.device):
+        raise ValueError("out must be a contiguous tensor of S's shape and type out_dtype")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    rc = lib.gemm_softmax_rows(_ptr(S), rows, cols, cols, float(scale), _ptr(out), cols,
+                               _CODE[out_dtype], ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise GemmError(rc, "gemm_softmax_rows")
+    return out

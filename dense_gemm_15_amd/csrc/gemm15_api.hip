@@ -23,6 +23,7 @@
 
 #include "../../include/gemm15.h"
 #include "kernels.hpp"
+#include "softmax.hpp"
 
 using namespace g15;
 
@@ -576,6 +577,22 @@ gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
 gemm_plan* gemm_plan_create(int64_t M, int64_t N, int64_t K, int32_t dtype,
                             const gemm_epilogue* epi) {
   return gemm_plan_create_layout(M, N, K, dtype, epi, 1, -1, GEMM_B_KN);
+}
+
+int gemm_softmax_rows(const float* S, int64_t rows, int64_t cols, int64_t ld_s, float scale,
+                      void* P, int64_t ld_p, int32_t p_dtype, void* stream) {
+  if (rows < 1 || cols < 1 || (rows + 3) / 4 > 0x7fffffff) return GEMM_ERR_SHAPE;
+  if (ld_s < cols || ld_p < cols) return GEMM_ERR_ARG;
+  if (p_dtype != GEMM_F32 && p_dtype != GEMM_F16 && p_dtype != GEMM_BF16) return GEMM_ERR_DTYPE;
+  if (!S || !P) return GEMM_ERR_NULL;
+  if (!aligned_to(S, 4) || !aligned_to(P, elem_bytes(p_dtype))) return GEMM_ERR_ALIGN;
+  if (!std::isfinite(scale)) return GEMM_ERR_ARG;
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return GEMM_ERR_NO_DEVICE;
+  const int dt = p_dtype == GEMM_F32 ? DT_F32 : p_dtype == GEMM_BF16 ? DT_BF16 : DT_F16;
+  const hipError_t err = launch_softmax_rows(S, rows, cols, ld_s, scale, P, ld_p, dt,
+                                             static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
 int gemm_run_strided_batched(const gemm_plan* p, int64_t batch, const void* A, int64_t sA,

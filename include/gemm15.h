@@ -159,6 +159,30 @@ int gemm_run_strided_batched(const gemm_plan* plan, int64_t batch, const void* A
                              const void* resid, int64_t strideR, void* C, int64_t strideC,
                              void* stream);
 
+/*
+ * Row softmax between the two batched products of attention (tutorial page,
+ * section 2: attention is Q K^T, a softmax, then the product with V; DeepGEMM
+ * page, section 3.4: the softmax denominator must be accumulated in FP32):
+ *
+ *     P[r][c] = exp(scale*S[r][c] - m_r) / sum_c' exp(scale*S[r][c'] - m_r),
+ *     m_r = max_c scale*S[r][c]
+ *
+ * S      device, rows x cols FP32, row r at S + r*ld_s (ld_s >= cols, elements);
+ *        the scores as gemm_run_strided_batched leaves them (rows = batch * M)
+ * P      device, rows x cols of p_dtype (GEMM_F32, GEMM_F16 or GEMM_BF16), row r at
+ *        P + r*ld_p; computed in FP32 and rounded once (nearest, ties to even).
+ *        P must not overlap S.
+ * scale  a finite multiplier applied to S before the softmax (1 for the plain form)
+ * Enqueues one kernel on `stream` (a hipStream_t as void*; NULL = default) and
+ * returns GEMM_OK, or GEMM_ERR_SHAPE (rows or cols < 1), GEMM_ERR_ARG (ld_s or
+ * ld_p < cols, scale not finite), GEMM_ERR_DTYPE, GEMM_ERR_NULL, GEMM_ERR_ALIGN
+ * (S not 4-byte or P not element aligned), GEMM_ERR_NO_DEVICE, GEMM_ERR_HIP.
+ * Inputs are expected finite; a row whose scaled scores are all -inf has no
+ * softmax and yields NaN.
+ */
+int gemm_softmax_rows(const float* S, int64_t rows, int64_t cols, int64_t ld_s, float scale,
+                      void* P, int64_t ld_p, int32_t p_dtype, void* stream);
+
 /* Release a plan and its workspace. NULL is ignored. The caller must make sure no
  * enqueued run of the plan is still pending on a stream. */
 void gemm_plan_destroy(gemm_plan* plan);

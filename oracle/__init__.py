@@ -73,6 +73,7 @@ def load(path: str | None = None):
     lib.oracle_gemm_at.argtypes = [i64, i64, i64, i32, vp, vp, ctypes.c_uint, dp, vp, i32, vp,
                                    i64, vp, vp, vp, vp]
     lib.oracle_gemm_f16acc.argtypes = [i64, i64, i64, vp, vp, vp]
+    lib.oracle_softmax_rows.argtypes = [i64, i64, vp, i64, dp, vp]
     lib.oracle_threads.restype = i32
     if path is None:
         _lib = lib
@@ -174,6 +175,30 @@ def gemm_f16acc(A, B, lib=None):
     if rc != 0:
         raise ValueError(f"oracle_gemm_f16acc rejected its arguments (code {rc})")
     return ref
+
+
+def softmax_rows(S, scale: float = 1.0, lib=None):
+    """Row softmax of scale * S in double; S a 2-D float32 array. Returns float64."""
+    lib = lib or load()
+    S = np.ascontiguousarray(S, dtype=np.float32)
+    rows, cols = S.shape
+    ref = np.empty((rows, cols), np.float64)
+    rc = lib.oracle_softmax_rows(rows, cols, S.ctypes.data, cols, float(scale), ref.ctypes.data)
+    if rc != 0:
+        raise ValueError(f"oracle_softmax_rows rejected its arguments (code {rc})")
+    return ref
+
+
+def softmax_tolerance(S, ref, scale: float = 1.0, out_dtype: str = "f32", lib=None):
+    """Element-wise bound for an fp32 softmax against the double reference: the
+    exponent's argument carries ~2^-24 |scale x| of rounding and exp, the row sum and
+    the division a few fp32 ulps, so |P - p| <= p (4e-6 + 2^-22 max_c |scale S|) per
+    row; a 16-bit output adds half a 16-bit ulp of the (rounded-once) value."""
+    R = np.abs(float(scale) * np.asarray(S, np.float64)).max(axis=1, keepdims=True)
+    tol = ref * (4e-6 + 2.0 ** -22 * R)
+    if out_dtype != "f32":
+        tol = tol + 0.5 * ulp16(out_dtype, np.abs(ref) + tol, lib=lib)
+    return tol
 
 
 def gemm_at(A, B, dtype, rows, cols, flags: int = 0, scale: float = 1.0, bias=None, resid=None,

@@ -282,6 +282,30 @@ int oracle_gemm_f16acc(int64_t M, int64_t N, int64_t K, const void* A, const voi
   return 0;
 }
 
+/*
+ * Row softmax (tutorial page, section 2: attention is Q K^T, a softmax over each
+ * row of scores, then the product with V): for each row r of the fp32 matrix S
+ * (rows x cols, row stride ld),
+ *   P[r][c] = exp(scale*S[r][c] - m) / sum_c' exp(scale*S[r][c'] - m),
+ *   m = max_c scale*S[r][c],
+ * everything in double (subtracting m changes nothing mathematically and keeps
+ * exp from overflowing). ref receives rows x cols doubles.
+ */
+int oracle_softmax_rows(int64_t rows, int64_t cols, const float* S, int64_t ld, double scale,
+                        double* ref) {
+  if (rows < 1 || cols < 1 || ld < cols || !S || !ref) return -1;
+#pragma omp parallel for schedule(dynamic, 16)
+  for (int64_t r = 0; r < rows; ++r) {
+    const float* x = S + r * ld;
+    double m = -INFINITY;
+    for (int64_t c = 0; c < cols; ++c) m = fmax(m, scale * (double)x[c]);
+    double sum = 0.0;
+    for (int64_t c = 0; c < cols; ++c) sum += exp(scale * (double)x[c] - m);
+    for (int64_t c = 0; c < cols; ++c) ref[r * cols + c] = exp(scale * (double)x[c] - m) / sum;
+  }
+  return 0;
+}
+
 /* Number of OpenMP threads a parallel region here would use. */
 int oracle_threads(void) {
 #ifdef _OPENMP

@@ -84,6 +84,9 @@ WORKLOADS = {
     "ffn": dict(kind="ffn", tokens=8192, hidden=768, ffn=3072, seeds=(401, 402, 403, 404, 405)),
     # Attention scores: Q, K [96 x 512 x 64] bf16 ~N(0,1) (index = batch*12 + head); seeds 501, 502.
     "qk": dict(kind="qk", batch=96, seq=512, head_dim=64, seeds=(501, 502)),
+    # Attention continuation: V [96 x 512 x 64] bf16 ~N(0,1), seed 503; P = softmax(Q K^T)
+    # row by row (the tutorial page's Softmax(QK^T)V, no 1/sqrt(D) factor), O = P V.
+    "attention": dict(kind="attention", batch=96, seq=512, head_dim=64, seeds=(501, 502, 503)),
     "gemv_1x4096x4096": dict(kind="gemm", M=1, N=4096, K=4096, dtype="f16", seeds=(511, 512)),
     "odd_127x1000x771": dict(kind="gemm", M=127, N=1000, K=771, dtype="f16", seeds=(521, 522)),
     "odd_4095x4097x63": dict(kind="gemm", M=4095, N=4097, K=63, dtype="f16", seeds=(531, 532)),
@@ -111,6 +114,14 @@ def ffn_inputs():
     W2 = normal(s2, (F, H), 0.02, "bf16")
     b2 = normal(sb2, (H,), 0.02, "f32")
     return X, W1, b1, W2, b2
+
+
+def attention_inputs():
+    """Q [96 x 512 x 64], K^T [96 x 64 x 512] (as qk_inputs) and V [96 x 512 x 64], bf16."""
+    w = WORKLOADS["attention"]
+    Q, Kt = qk_inputs()
+    V = normal(w["seeds"][2], (w["batch"], w["seq"], w["head_dim"]), 1.0, "bf16")
+    return Q, Kt, V
 
 
 def qk_inputs():

@@ -362,4 +362,37 @@ def pin_f16acc_closed_forms(lib):
     assert err16 > 1e-3 and err16 > 100 * err32, (err16, err32)
 
 
+def pin_softmax_library(lib):
+    """Row softmax against scipy.special.softmax on random rows (a library routine),
+    with a scale; rows sum to 1; a two-element row is the logistic function."""
+    from scipy.special import softmax as sp_softmax
+    r = _rng(51)
+    for rows, cols, scale in [(3, 1, 1.0), (5, 7, 1.0), (4, 513, 0.125), (2, 64, 3.0)]:
+        S = (r.standard_normal((rows, cols)) * 4).astype(np.float32)
+        got = oracle.softmax_rows(S, scale, lib=lib)
+        want = sp_softmax(scale * S.astype(np.float64), axis=1)
+        assert np.allclose(got, want, rtol=1e-13, atol=1e-300), (rows, cols, scale)
+        assert np.allclose(got.sum(axis=1), 1.0, rtol=0, atol=1e-13 * cols)
+    x = np.array([[0.75, -1.5]], np.float32)
+    p0 = 1.0 / (1.0 + math.exp(-1.5 - 0.75))
+    got = oracle.softmax_rows(x, lib=lib)
+    assert abs(got[0, 0] - p0) <= 1e-15 and abs(got[0, 1] - (1 - p0)) <= 1e-15
+
+
+def pin_softmax_invariants(lib):
+    """Shift invariance, equal entries give 1/cols exactly, and scores of 1e4 do not
+    overflow (the row maximum gets all of the weight)."""
+    r = _rng(52)
+    S = (r.integers(-3072, 3073, (6, 40)) / 1024).astype(np.float32)
+    a = oracle.softmax_rows(S, lib=lib)
+    b = oracle.softmax_rows(S + np.float32(64.0), lib=lib)  # exact: S is on the 2^-10 grid
+    assert np.allclose(a, b, rtol=1e-12, atol=0)
+    eq = oracle.softmax_rows(np.full((2, 8), 3.5, np.float32), lib=lib)
+    assert np.array_equal(eq, np.full((2, 8), 0.125))
+    big = np.zeros((1, 5), np.float32)
+    big[0, 2] = 1e4
+    got = oracle.softmax_rows(big, lib=lib)
+    assert np.all(np.isfinite(got)) and got[0, 2] == 1.0 and got[0, 0] == 0.0
+
+
 PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

@@ -59,6 +59,11 @@ MUTANTS = [
      "acc = acc + dec_one(OR_F16, A, i * K + k) * dec_one(OR_F16, B, k * N + j);"),
     ("f16acc_bf16_rounding", "11,\n                        -14, 15);", "8,\n                        -126, 127);"),
     ("f16acc_transposed_B", "dec_one(OR_F16, B, k * N + j)", "dec_one(OR_F16, B, j * K + k)"),
+    ("softmax_no_max", "sum += exp(scale * (double)x[c] - m);", "sum += exp(scale * (double)x[c]);"),
+    ("softmax_scale_dropped", "ref[r * cols + c] = exp(scale * (double)x[c] - m) / sum;",
+     "ref[r * cols + c] = exp((double)x[c] - m) / sum;"),
+    ("softmax_last_column_dropped", "for (int64_t c = 0; c < cols; ++c) sum += exp",
+     "for (int64_t c = 0; c + 1 < cols; ++c) sum += exp"),
 ]
 
 RUNNER = r"""
