@@ -162,6 +162,8 @@ const TunedRow kTuned[] = {
     {false, 8192, 3072, 768, 1, "m16n_{t}_128x128x64_w2x2_a2_b2"},
     {false, 8192, 768, 3072, 1, "m16n_{t}_128x256x64_w2x4_a3_b3"},
     {false, 512, 512, 64, 96, "m16n_{t}_128x128x64_w2x2_a2_b2"},
+    {false, 512, 64, 512, 96, "m16t_{t}_128x128x64_w2x2_a2_b2"},  // 96 heads of P V
+    {false, 512, 64, 512, 96, "m16n_{t}_128x128x64_w2x2_a2_b2"},
     {true, 4096, 4096, 4096, 1, "f32d_256x256x16_w4x2_a3"},
     {true, 8192, 8192, 8192, 1, "f32d_256x256x16_w4x2_a3"},
     {true, 2048, 2048, 2048, 1, "f32d_128x128x16_w2x2_a3"},
