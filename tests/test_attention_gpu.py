@@ -45,12 +45,15 @@ def _check_softmax(P, S, scale, out_dtype):
 
 @pytest.mark.parametrize("out_dtype", ["f32", "bf16", "f16"])
 def test_softmax_rows_shapes(g, out_dtype):
-    """Rows of 1 to 4097 columns (vector and scalar paths, ragged tails), scales 1 and
-    1/8, scores up to |40|."""
+    """Rows of 1 to 4097 columns: register-held rows (multiples of 4 up to 1024,
+    with partly filled chunks), the two-pass vector and scalar paths; scales 1, 1/8,
+    2 and a negative one; scores up to |40|."""
     dev = torch.device("cuda")
     for i, (rows, cols, scale, std) in enumerate([(37, 1, 1.0, 1.0), (37, 3, 1.0, 3.0),
                                                   (64, 512, 1.0, 8.0), (5, 1000, 0.125, 8.0),
-                                                  (3, 4097, 1.0, 2.0), (9, 4096, 0.125, 40.0)]):
+                                                  (7, 1024, -0.5, 4.0), (11, 4, 2.0, 1.0),
+                                                  (6, 260, 1.0, 3.0), (3, 4097, 1.0, 2.0),
+                                                  (9, 4096, 0.125, 40.0)]):
         S = synth.normal(600 + i, (rows, cols), std, "f32")
         P = g.softmax_rows(S.to(dev), scale, out_dtype).cpu()
         torch.cuda.synchronize()
