@@ -62,9 +62,18 @@ def kernel_source_hash(config: str | None = None) -> str:
              else sorted(glob.glob(os.path.join(csrc, "*"))))
     h = hashlib.sha256()
     for f in files:
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode() + fh.read())
+        with open(f) as fh:
+            h.update(os.path.basename(f).encode() + code_only(fh.read()).encode())
     return h.hexdigest()[:16]
+
+
+def code_only(src: str) -> str:
+    """C++ source without comments, trailing blanks and empty lines: what a hash of
+    the code should see (editing a comment does not change the kernel)."""
+    import re
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", "", src)
+    return "\n".join(ln.rstrip() for ln in src.splitlines() if ln.strip())
 
 
 def measured_traffic(kernel_config: str):

@@ -11,9 +11,9 @@
 //    store instructions) into a ring of SA LDS buffers, issued SA-1 slices
 //    ahead of use;
 //  * B slices must be transposed (the matrix core wants k contiguous per lane,
-//    B is n contiguous), so they land in one of two register sets two slices
-//    ahead, are transposed 8 x 8 in registers one slice ahead and stored into
-//    one of two n-major LDS buffers;
+//    B is n contiguous), so they land in registers one or two slices ahead (one
+//    or two register sets), are transposed in registers per thread block of
+//    4 x 8 or 8 x 8 (k x n) and stored into one of two n-major LDS buffers;
 //  * a single barrier per slice; the wait before it only covers the loads
 //    issued two slices earlier, so two slices of loads stay in flight;
 //  * operand fragments of k-step s+1 are read while the matrix core runs k-step
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16d_kernel(LaunchArgs a)
   }
   if (kt < nk) slice(std::integral_constant<int, 0>{}, Tail{}, kt);
 
-  // ---- epilogue: staged through LDS (store_tile)
+  // ---- epilogue (store_tile)
   wait_vm<0>();
   lds_barrier();  // every wave is done with the operand ring; LDS is free
   store_tile<FM, FN, WTM, WTN, NW, static_cast<int>(sizeof(lds))>(
