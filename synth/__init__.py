@@ -59,6 +59,15 @@ def grid(seed: int, shape, dtype: str, step: float = 2.0 ** -10) -> torch.Tensor
     return _cast(rng.integers(-n, n + 1, size=tuple(shape)).astype(np.float64) * step, dtype)
 
 
+def device_uniform(seed: int, shape, dtype: str, device="cuda") -> torch.Tensor:
+    """U[-1, 1) drawn on the GPU by torch's generator seeded with ``seed``, in
+    ``dtype``: for operands too large to draw on the host."""
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    x = torch.rand(tuple(shape), generator=gen, device=device, dtype=torch.float32) * 2 - 1
+    return x.to(DTYPES[dtype])
+
+
 def bits(t: torch.Tensor) -> np.ndarray:
     """The raw element bits of a CPU tensor as a numpy array.
 

@@ -498,6 +498,45 @@ def test_packed_batched_and_misaligned(g):
     assert r["ok"], r
 
 
+def test_operands_past_2gib(g):
+    """Maximum sizes: an A of exactly 2 GiB (bf16, 2^20 x 1024) and an fp32 C of 2 GiB
+    (65536 x 8192) leave the kernels that address operands with 32-bit offsets; the
+    64-bit-addressed ones must produce the same products. Sampled rows, including the
+    last ones (past the 2 GiB mark), against the oracle."""
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(950)
+    # A of 2^31 bytes
+    M, N, K = 1 << 20, 64, 1024
+    A = synth.device_uniform(951, (M, K), "bf16")
+    B = synth.uniform(952, (K, N), "bf16")
+    plan = g.Plan(M, N, K, "bf16")
+    say(f"[2GiB A] {plan.describe()}")
+    assert not plan.config_name.startswith(("m16d", "m16n", "m16t", "m16p", "f32d", "gemv"))
+    C = plan.run(A, B.to(dev))
+    torch.cuda.synchronize()
+    rows = np.concatenate([rng.integers(0, M, 24), [M - 2, M - 1]])
+    Ar = A[torch.from_numpy(rows).to(dev)].cpu()
+    Cr = C[torch.from_numpy(rows).to(dev)].cpu()
+    r = gc.check_full(Cr, Ar, B, "bf16")
+    assert r["ok"], r
+    del A, C
+    torch.cuda.empty_cache()
+    # fp32 C of 2^31 bytes
+    M, N, K = 1 << 16, 1 << 13, 16
+    A = synth.uniform(953, (M, K), "f32")
+    B = synth.uniform(954, (K, N), "f32")
+    plan = g.Plan(M, N, K, "f32")
+    say(f"[2GiB C] {plan.describe()}")
+    C = plan.run(A.to(dev), B.to(dev))
+    torch.cuda.synchronize()
+    rows = np.concatenate([rng.integers(0, M, 8), [M - 1]])
+    Cr = C[torch.from_numpy(rows).to(dev)].cpu()
+    r = gc.check_full(Cr, A[torch.from_numpy(rows)], B, "f32")
+    assert r["ok"], r
+    del C
+    torch.cuda.empty_cache()
+
+
 def test_repeat_shape_hits_cache(g):
     """A repeated shape is served from the exact-shape cache."""
     h0, m0, _ = g.cache_stats()
