@@ -83,3 +83,47 @@ def test_graph_replay_matches_eager(g, case):
     r = gc.check_full(eager[0].cpu(), A.cpu(), Bref[0], dtype, epi.get("out_dtype", "f32"),
                       None if b is None else b.cpu(), gelu=epi.get("gelu", False))
     assert r["ok"], r
+
+
+def test_graph_replay_attention_chain(g):
+    """S = Q K^T, P = softmax(S), O = P V captured as one graph (three kernels on one
+    stream, the softmax through gemm_softmax_rows) and replayed with Q changed in
+    place between replays: every replay equals the eager chain bit for bit."""
+    nb, Sq, D = 4, 256, 64
+    dev = torch.device("cuda")
+    Qs = [synth.normal(960 + i, (nb, Sq, D), 1.0, "bf16").to(dev) for i in range(3)]
+    Kt = synth.normal(964, (nb, Sq, D), 1.0, "bf16").transpose(1, 2).contiguous().to(dev)
+    V = synth.normal(965, (nb, Sq, D), 1.0, "bf16").to(dev)
+    qk = g.Plan(Sq, Sq, D, "bf16", batch_hint=nb)
+    pv = g.Plan(Sq, D, Sq, "bf16", batch_hint=nb)
+    S = torch.empty((nb, Sq, Sq), dtype=torch.float32, device=dev)
+    P = torch.empty((nb, Sq, Sq), dtype=torch.bfloat16, device=dev)
+    O = torch.empty((nb, Sq, D), dtype=torch.float32, device=dev)
+    Q = Qs[0].clone()
+
+    def chain():
+        qk.run_batched(Q, Kt, out=S)
+        g.softmax_rows(S, 1.0, "bf16", out=P)
+        pv.run_batched(P, V, out=O)
+
+    eager = []
+    for q in Qs:
+        Q.copy_(q)
+        chain()
+        eager.append(O.clone())
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        chain()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        chain()
+    for rep in range(5):
+        Q.copy_(Qs[rep % 3])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(O, eager[rep % 3]), rep
