@@ -195,6 +195,9 @@ bool cfg_fits(const KernelEntry& k, int dtype, bool vec_a, bool vec_b, const gem
     const int64_t lim = int64_t(1) << 31;
     const int64_t es = elem_bytes(dtype), oe = elem_bytes(out_dtype);
     if (M * K * es >= lim || K * N * es >= lim || M * N * oe >= lim) return false;
+    // the tiled kernels address row-major B from the current K slice: the offsets of
+    // its bk rows (bk row lengths past the slice start) must stay 32-bit as well
+    if (k.kind != KIND_GEMV && !b_nk && static_cast<int64_t>(k.bk) * N * es >= lim) return false;
   }
   if (k.vec_a && !vec_a) return false;
   if (k.vec_b && !vec_b) return false;

@@ -146,6 +146,19 @@ def test_select_batch_hint_changes_tiles():
     assert many.workgroups >= 256
 
 
+def test_select_keeps_slice_offsets_32bit():
+    """A 32-bit-offset tiled kernel reads a K slice of row-major B at offsets up to
+    bk row lengths: a B row of 2^24 16-bit elements (64 rows = 2 GiB) goes to the
+    64-bit kernels, one row shorter stays on the fast ones; the few-row kernels
+    address B from its start and keep any width under the 2 GiB total."""
+    wide = g.select(16, 1 << 24, 16, "bf16", **MI355X)
+    assert not g.config_names()[wide.config].startswith(("m16d", "m16t", "m16n", "m16p", "f32d"))
+    fits = g.select(16, (1 << 24) - 8, 16, "bf16", **MI355X)
+    assert g.config_names()[fits.config].startswith("m16d")
+    few = g.select(1, 1 << 24, 16, "bf16", **MI355X)
+    assert g.config_names()[few.config].startswith("gemv")
+
+
 TUNED = [
     ((4096, 4096, 4096), 1, "bf16", "m16d_bf16_256x256x64_w4x2_a3_b4_r1"),
     ((8192, 3072, 768), 1, "bf16", "m16t_bf16_128x128x64_w2x2_a2_b2"),

@@ -537,6 +537,29 @@ def test_operands_past_2gib(g):
     torch.cuda.empty_cache()
 
 
+def test_wide_b_rows(g):
+    """Row-major B rows of 2^24 - 8 and 2^24 bf16 elements with a short K: the first
+    stays on the 32-bit-offset kernel (a 64-row slice of B spans just under 2 GiB of
+    offsets, rows past K still out of range), the second goes to a 64-bit-addressed
+    one. Sampled columns, including the last ones, against the oracle."""
+    dev = torch.device("cuda")
+    rng = np.random.default_rng(960)
+    M, K = 16, 16
+    for N, fast in (((1 << 24) - 8, True), (1 << 24, False)):
+        A = synth.uniform(961, (M, K), "bf16")
+        B = synth.device_uniform(962, (K, N), "bf16")
+        plan = g.Plan(M, N, K, "bf16")
+        say(f"[wide B N={N}] {plan.describe()}")
+        assert plan.config_name.startswith("m16d") == fast, plan.config_name
+        C = plan.run(A.to(dev), B)
+        torch.cuda.synchronize()
+        cols = torch.from_numpy(np.concatenate([rng.integers(0, N, 56), np.arange(N - 8, N)])).to(dev)
+        r = gc.check_full(C[:, cols].cpu(), A, B[:, cols].cpu(), "bf16")
+        assert r["ok"], (N, r)
+        del B, C
+        torch.cuda.empty_cache()
+
+
 def test_repeat_shape_hits_cache(g):
     """A repeated shape is served from the exact-shape cache."""
     h0, m0, _ = g.cache_stats()
