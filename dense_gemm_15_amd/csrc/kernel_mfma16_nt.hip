@@ -312,15 +312,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
       mmas(f0a, f0b, 0, FM);
       plan_slice<0, FM * FN, FM + FN, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
+      // the B fragments of k-step 3 are read here too, before the slice's direct
+      // loads: the compiler makes a transposing LDS read that follows a direct load
+      // wait for every load in flight (plain reads it lets through)
+      u32x4 f3b[FN];
       frags(LA, LB, 2, f0a, f0b);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) read_frag(LA, LB, 3, 1 + j, f1a, f3b);
 #pragma unroll
       for (int v = 0; v < NV; ++v) dma(v);
       mmas(f1a, f1b, 0, FM);
-      plan_slice<0, FM * FN, FM + FN, 0, NV>();
+      plan_slice<0, FM * FN, FM + 2 * FN, 0, NV>();
       __builtin_amdgcn_sched_barrier(0);
-      frags(LA, LB, 3, f1a, f1b);
+#pragma unroll
+      for (int r = 0; r < FM + FN; ++r)
+        if (r == 0 || r > FN) read_frag(LA, LB, 3, r, f1a, f1b);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) f1b[j] = f3b[j];
       mmas(f0a, f0b, 0, FM);
-      plan_slice<0, FM * FN, FM + FN, 0, 0>();
+      plan_slice<0, FM * FN, FM, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
       mmas(f1a, f1b, 0, HALF);
       __builtin_amdgcn_sched_barrier(0);
