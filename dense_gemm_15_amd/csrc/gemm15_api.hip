@@ -149,7 +149,7 @@ struct TunedRow {
   const char* config;  // an "m16n" configuration answers problems with a transposed B
 };
 const TunedRow kTuned[] = {
-    {false, 4096, 4096, 4096, 1, "m16d_{t}_256x256x64_w4x2_a3_b4_r1"},
+    {false, 4096, 4096, 4096, 1, "m16t_{t}_256x256x64_w2x4_a3_b2"},
     {false, 8192, 8192, 8192, 1, "m16d_{t}_256x256x64_w4x2_a3_b4_r1"},
     {false, 2048, 2048, 2048, 1, "m16d_{t}_128x128x64_w2x2_a3_b4_r1"},
     {false, 1024, 1024, 1024, 1, "m16d_{t}_64x128x64_w2x2_a4_b4_r2"},

@@ -160,7 +160,9 @@ def test_select_keeps_slice_offsets_32bit():
 
 
 TUNED = [
-    ((4096, 4096, 4096), 1, "bf16", "m16d_bf16_256x256x64_w4x2_a3_b4_r1"),
+    ((4096, 4096, 4096), 1, "bf16", "m16t_bf16_256x256x64_w2x4_a3_b2"),
+    ((4096, 4096, 4096), 1, "f16", "m16t_f16_256x256x64_w2x4_a3_b2"),
+    ((8192, 8192, 8192), 1, "bf16", "m16d_bf16_256x256x64_w4x2_a3_b4_r1"),
     ((8192, 3072, 768), 1, "bf16", "m16t_bf16_128x128x64_w2x2_a2_b2"),
     ((8192, 768, 3072), 1, "bf16", "m16d_bf16_128x256x64_w2x4_a3_b4_r1"),
     ((512, 512, 64), 96, "bf16", "m16d_bf16_128x256x64_w2x4_a3_b4_r1"),

@@ -27,10 +27,11 @@ def test_symbol_to_config():
 
 def test_committed_traffic_matches_sources():
     """The committed FETCH_SIZE / WRITE_SIZE figures belong to the current sources of
-    the two headline kernels (re-collect them after changing those kernels)."""
+    the headline kernels (re-collect them after changing those kernels)."""
     with open(bench.TRAFFIC_FILE) as f:
         t = json.load(f)
-    for cfg in ("m16d_bf16_256x256x64_w4x2_a3_b4_r1", "f32d_256x256x16_w4x2_a3"):
+    for cfg in ("m16t_bf16_256x256x64_w2x4_a3_b2", "m16d_bf16_256x256x64_w4x2_a3_b4_r1",
+                "f32d_256x256x16_w4x2_a3"):
         assert t["kernels"][cfg]["source_hash"] == bench.kernel_source_hash(cfg), cfg
         v = bench.measured_traffic(cfg)
         assert v is not None and v > 134e6, (cfg, v)  # at least A + B + C once
