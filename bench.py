@@ -46,6 +46,7 @@ KERNEL_SOURCES = {
     "m16d": ["kernel_mfma16_dlds.hip", "m16_common.hpp"] + _COMMON,
     "m16n": ["kernel_mfma16_nt.hip", "m16_common.hpp"] + _COMMON,
     "m16t": ["kernel_mfma16_nt.hip", "m16_common.hpp"] + _COMMON,
+    "m16s": ["kernel_mfma16_k1.hip", "m16_common.hpp"] + _COMMON,
     "f32d": ["kernel_f32_dlds.hip"] + _COMMON,
     "gemv": ["kernel_gemv.hip"] + _COMMON,
 }
@@ -411,6 +412,10 @@ def symbol_to_config(sym: str):
         t, bm, bn, wm, wn, sa, sb, brow = m.groups()
         kind = "m16t" if brow == "true" else "m16n"
         return f"{kind}_{t}_{bm}x{bn}x64_w{wm}x{wn}_a{sa}_b{sb}"
+    m = re.search(r"gemm_m16s_kernel<g15::(\w+)_t, (\d+), (\d+), (\d+), (\d+)>", sym)
+    if m:
+        t, bm, bn, wm, wn = m.groups()
+        return f"m16s_{t}_{bm}x{bn}x64_w{wm}x{wn}"
     m = re.search(r"gemm_f32d_kernel<(\d+), (\d+), (\d+), (\d+), (\d+)>", sym)
     if m:
         bm, bn, wm, wn, sa = m.groups()

@@ -72,6 +72,8 @@ struct Registry {
     all.insert(all.end(), p, p + n);
     n = ladder_entries(&p);
     all.insert(all.end(), p, p + n);
+    n = mfma16_k1_entries(&p);
+    all.insert(all.end(), p, p + n);
   }
 };
 
@@ -156,7 +158,7 @@ const TunedRow kTuned[] = {
     {false, 512, 512, 512, 1, "m16d_{t}_64x128x64_w2x2_a4_b4_r2"},
     {false, 8192, 3072, 768, 1, "m16t_{t}_128x128x64_w2x2_a2_b2"},     // encoder FFN, first GEMM
     {false, 8192, 768, 3072, 1, "m16d_{t}_128x256x64_w2x4_a3_b4_r1"},  // encoder FFN, second GEMM
-    {false, 512, 512, 64, 96, "m16d_{t}_128x256x64_w2x4_a3_b4_r1"},    // 96 heads of Q K^T
+    {false, 512, 512, 64, 96, "m16s_{t}_256x128x64_w4x2"},             // 96 heads of Q K^T
     {false, 4096, 4096, 4096, 1, "m16n_{t}_256x256x64_w2x4_a3_b2"},
     {false, 2048, 2048, 2048, 1, "m16n_{t}_128x128x64_w2x2_a3_b3"},
     {false, 8192, 3072, 768, 1, "m16n_{t}_128x128x64_w2x2_a2_b2"},
@@ -203,6 +205,7 @@ bool cfg_fits(const KernelEntry& k, int dtype, bool vec_a, bool vec_b, const gem
   if (k.vec_b && !vec_b) return false;
   if (k.lds_bytes > dev.lds_bytes) return false;
   if (k.kind == KIND_GEMV && (M > k.bm || K > static_cast<int64_t>(k.bk) * 65535)) return false;
+  if (k.kind == KIND_K1 && K > k.bk) return false;
   return true;
 }
 
@@ -221,6 +224,12 @@ int gemv_split(const KernelEntry& k, int64_t N, int64_t K, int64_t batch,
   return static_cast<int>(s);
 }
 
+// Resident workgroups of a K1 configuration: every CU full, a multiple of 8 so
+// each XCD runs the same number.
+int k1_workgroups(const KernelEntry& k, const gemm_device_desc& dev) {
+  return (dev.cu_count * cfg_occupancy(k, dev) + 7) / 8 * 8;
+}
+
 // fp32 partial sums [split][bm][N].
 int64_t gemv_workspace_bytes(const KernelEntry& k, int64_t N, int split) {
   return split <= 1 ? 0 : static_cast<int64_t>(split) * k.bm * N * 4;
@@ -229,6 +238,7 @@ int64_t gemv_workspace_bytes(const KernelEntry& k, int64_t N, int split) {
 // Workgroups of one launch (one batch item for the GEMV kind, which loops).
 int64_t cfg_workgroups(const KernelEntry& k, int64_t M, int64_t N, int split, int64_t batch) {
   const int64_t tiles = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn);
+  if (k.kind == KIND_K1) return tiles * batch < split ? (tiles * batch + 7) / 8 * 8 : split;
   return k.kind == KIND_GEMV ? tiles * split : tiles * batch;
 }
 
@@ -299,7 +309,7 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
     double best_cost = 0;
     for (int i = 0; i < static_cast<int>(all.size()); ++i) {
       const KernelEntry& k = all[i];
-      if (k.kind == KIND_GEMV || k.kind == KIND_LADDER || !use(k)) continue;
+      if (k.kind == KIND_GEMV || k.kind == KIND_LADDER || k.kind == KIND_K1 || !use(k)) continue;
       if (!cfg_fits(k, dtype, va, vb, dev, M, np, kp, epi.out_dtype, b_nk)) continue;
       const double c = cfg_cost(k, M, N, K, batch, dev);
       if (best < 0 || c < best_cost * 0.999) {
@@ -561,6 +571,7 @@ gemm_plan* gemm_plan_create_layout(int64_t M, int64_t N, int64_t K, int32_t dtyp
     }
   }
   const KernelEntry& k = all[cfg];
+  if (k.kind == KIND_K1) p->split = k1_workgroups(k, desc);
   if (k.kind == KIND_GEMV) {
     p->split = gemv_split(k, N, K, batch_hint, desc);
     p->workspace_bytes = gemv_workspace_bytes(k, N, p->split);
@@ -741,7 +752,9 @@ int gemm_select_layout(const gemm_device_desc* dev, int64_t M, int64_t N, int64_
   out->bk = k.bk;
   out->threads = k.threads;
   out->lds_bytes = k.lds_bytes;
-  out->split = k.kind == KIND_GEMV ? gemv_split(k, N, K, batch_hint, *dev) : 1;
+  out->split = k.kind == KIND_GEMV ? gemv_split(k, N, K, batch_hint, *dev)
+               : k.kind == KIND_K1   ? k1_workgroups(k, *dev)
+                                     : 1;
   out->workgroups = cfg_workgroups(k, M, N, out->split, batch_hint);
   out->packed = sel.packed;
   return GEMM_OK;

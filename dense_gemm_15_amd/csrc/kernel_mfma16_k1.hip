@@ -1,0 +1,266 @@
+// kernel_mfma16_k1.hip -- bf16 / fp16 matrix-core GEMM for products whose K fits
+// one 64-deep slice: the attention scores S = Q K^T of heads of dimension 64 (the
+// tutorial page's attention, section 2: a batched Q K^T whose output the softmax
+// then reads). With K = 64 a 128 x 128 tile reads 32 KB of operands and writes
+// 64 KB of fp32 C, so the writes are the work: each workgroup walks a strided list
+// of tiles (batch items included) and keeps the next tile's operands loading while
+// it multiplies and stores the current one, instead of one tile per workgroup with
+// its loads, products and stores in sequence.
+//
+// Per tile: wait for its operands (and the previous tile's stores), barrier, read
+// every A fragment (16-byte LDS reads) and every B fragment (the transposing read
+// ds_read_b64_tr_b16, two per fragment) of the four 16-deep k-steps, issue the
+// direct-to-LDS loads of the next tile into the other slot, run the products, and
+// store C straight from the accumulators (DeepGEMM page, section 3.1: the tile's
+// accumulators leave once; the 16-bit forms without LDS staging, which would need
+// the slot being filled). All B fragments are read before the next tile's loads
+// go out because the compiler makes a transposing read that follows a direct load
+// wait for every load in flight.
+//
+// LDS (as in kernel_mfma16_nt.hip for m16t): an A slot is BM rows of 64 k, 16-byte
+// chunk c of row r at c ^ (r & 7) ^ ((r >> 3) & 3); a B slot is 64 rows (k) of BN
+// columns, chunk c of row k at c ^ (4 (k & 3)). Slots of k at or past K are zeroed
+// once (K is the same for every tile and the loads never write them); rows past M
+// and columns past N keep whatever the slot held, which only reaches outputs that
+// are not stored.
+//
+// Tile order: with 8 or more batch items, every tile of a batch item goes to one
+// XCD (workgroups reach the 8 XCDs round-robin), so each item's operands are
+// fetched into one L2; otherwise the tiles of the single product are strided over
+// the workgroups in the XCD-aware order of tile_of.
+#include "m16_common.hpp"
+
+namespace g15 {
+namespace {
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) char lds_char;
+
+template <typename T, int BM, int BN, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a) {
+  constexpr int BK = 64;
+  constexpr int NW = WGM * WGN;
+  constexpr int WTM = BM / WGM, WTN = BN / WGN;
+  constexpr int FM = WTM / 32, FN = WTN / 32;
+  constexpr int AI = BM / 8 / NW;                    // A loads per wave per tile (8 rows each)
+  constexpr int CPR_B = BN / 8, RPI = 64 / CPR_B;    // B: 16-byte chunks per row, rows per load
+  constexpr int BI = BN / 8 / NW;                    // B loads per wave per tile
+  constexpr int A_STAGE = BM * 8, B_STAGE = BN * 8;  // 16-byte chunks per slot
+  static_assert(BM % (8 * NW) == 0 && AI >= 1, "A rows must split evenly over the waves");
+  static_assert(BN % (8 * NW) == 0 && BI >= 1, "B chunks must split evenly over the waves");
+  static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 block");
+  static_assert(CPR_B >= 16 && 64 % CPR_B == 0, "B rows of 128 or 256 columns");
+  __shared__ u32x4 lds[2 * (A_STAGE + B_STAGE)];
+  u32x4* const ringA = lds;
+  u32x4* const ringB = lds + 2 * A_STAGE;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+  const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), K = static_cast<int>(a.K);
+  const int LDA = static_cast<int>(a.lda), LDB = static_cast<int>(a.ldb);
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+  const int64_t per_item = static_cast<int64_t>(tiles_m) * tiles_n;
+  const int64_t batch = a.batch;
+
+  // Tile-independent parts of this lane's load offsets. A: load i of the wave fills
+  // slot rows 8 (wave AI + i) .. +7, lane l row + l / 8, logical chunk a_chk[i].
+  // B: load i fills rows (wave BI + i) RPI .. +RPI-1, lane l row + l / CPR_B, slot
+  // chunk l % CPR_B, which holds logical chunk (l % CPR_B) ^ (4 (row & 3)).
+  int a_row[AI];
+  uint32_t a_koff[AI];
+  bool a_kin[AI];
+#pragma unroll
+  for (int i = 0; i < AI; ++i) {
+    const int chk = (lane & 7) ^ (lane >> 3) ^ ((wave * AI + i) & 3);
+    a_row[i] = (wave * AI + i) * 8 + (lane >> 3);
+    a_koff[i] = static_cast<uint32_t>(chk * 8);
+    a_kin[i] = chk * 8 < K;  // K is a multiple of 8: a chunk is wholly inside K or past it
+  }
+  int b_row[BI], b_col[BI];
+#pragma unroll
+  for (int i = 0; i < BI; ++i) {
+    const int row = (wave * BI + i) * RPI + lane / CPR_B;
+    b_row[i] = row;
+    b_col[i] = ((lane % CPR_B) ^ (4 * (row & 3))) * 8;
+  }
+  // k at or past K: zero those chunks of both slots once
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+#pragma unroll
+    for (int i = 0; i < AI; ++i)
+      if (!a_kin[i]) ringA[s * A_STAGE + (wave * AI + i) * 64 + lane] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int i = 0; i < BI; ++i)
+      if (b_row[i] >= K) ringB[s * B_STAGE + (wave * BI + i) * 64 + lane] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  // The q-th tile of this workgroup: batch item z and tile origin (m0, n0), or false
+  // past the end. Workgroup w runs on XCD w % 8.
+  const int64_t G = gridDim.x;
+  const bool by_item = batch >= 8 && G % 8 == 0;
+  auto tile = [&](int64_t q, int64_t& z, int& m0, int& n0) -> bool {
+    int64_t r;
+    if (by_item) {
+      // XCD x takes the items z = x, x + 8, ...; its G / 8 workgroups stride over the
+      // concatenated tiles of those items
+      const int64_t x = blockIdx.x % 8, gx = G / 8;
+      const int64_t u = blockIdx.x / 8 + q * gx;
+      const int64_t zi = u / per_item;
+      z = zi * 8 + x;
+      r = u - zi * per_item;
+      if (z >= batch) return false;
+    } else {
+      const int64_t t = blockIdx.x + q * G;
+      z = t / per_item;
+      r = t - z * per_item;
+      if (z >= batch) return false;
+    }
+    int tm, tn;
+    if (by_item) {
+      tm = static_cast<int>(r / tiles_n);
+      tn = static_cast<int>(r - static_cast<int64_t>(tm) * tiles_n);
+    } else {
+      tile_of(static_cast<int>(r), tiles_m, tiles_n, tm, tn);
+    }
+    m0 = tm * BM;
+    n0 = tn * BN;
+    return true;
+  };
+  // Direct-to-LDS loads of one tile into slot `slot`. A row past M, a column past N,
+  // a chunk or row past K get an offset past the extent (the slot is left as it is).
+  auto issue = [&](int64_t z, int m0, int n0, int slot) {
+    const uint16_t* Az = static_cast<const uint16_t*>(a.A) + z * a.sA;
+    const uint16_t* Bz = static_cast<const uint16_t*>(a.B) + z * a.sB;
+    const auto rA = rsrc(Az, static_cast<uint32_t>(static_cast<int64_t>(M) * LDA * 2));
+    const auto rB = rsrc(Bz, static_cast<uint32_t>(static_cast<int64_t>(K) * LDB * 2));
+#pragma unroll
+    for (int i = 0; i < AI; ++i) {
+      const int gm = m0 + a_row[i];
+      const uint32_t off =
+          (a_kin[i] && gm < M) ? static_cast<uint32_t>(gm * LDA) * 2u + a_koff[i] * 2u : OOB;
+      u32x4* dst = ringA + slot * A_STAGE + (wave * AI + i) * 64;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)dst, 16, off, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int gn = n0 + b_col[i];
+      const uint32_t off = (b_row[i] < K && gn < N)
+                               ? static_cast<uint32_t>(b_row[i] * LDB + gn) * 2u
+                               : OOB;
+      u32x4* dst = ringB + slot * B_STAGE + (wave * BI + i) * 64;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)dst, 16, off, 0, 0, 0);
+    }
+  };
+
+  // fragment addresses: A row wm*WTM + 32 i + (lane & 31), k chunk 2 s + lane / 32;
+  // B as in m16t (group g = lane / 16, t = lane % 16: row 8 (g / 2) + t / 4, column
+  // wn WTN + 32 j + 16 (g % 2) + 4 (t % 4); k-step s adds 16 s rows, the second read
+  // of a fragment 4 rows, neither of which changes row & 3)
+  const int lrow = lane & 31, lhalf = lane >> 5;
+  const int a_base = (wm * WTM + lrow) * 8;
+  const int perm = (lrow & 7) ^ ((lrow >> 3) & 3);
+  int btr[FN];
+  {
+    const int g = lane >> 4, t = lane & 15;
+    const int kr = 8 * (g >> 1) + (t >> 2);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int n = wn * WTN + 32 * j + 16 * (g & 1) + 4 * (t & 3);
+      btr[j] = kr * (BN * 2) + (((n >> 3) ^ (4 * (kr & 3))) << 4) + (n & 7) * 2;
+    }
+  }
+
+  LaunchArgs out = a;
+  out.c_vec = 0;  // 16-bit C straight from the registers: LDS holds the next tile's operands
+
+  f32x16 acc[FM][FN];
+  int64_t z;
+  int m0, n0;
+  bool have = tile(0, z, m0, n0);
+  if (have) issue(z, m0, n0, 0);
+  int slot = 0;
+  for (int64_t q = 0; have; ++q) {
+    int64_t zn;
+    int m0n, n0n;
+    const bool next = tile(q + 1, zn, m0n, n0n);
+    wait_vm<0>();  // this tile's operands (and the previous tile's stores) are complete
+    lds_barrier();  // every wave's loads have landed; every wave is done with the other slot
+
+    const u32x4* LA = ringA + slot * A_STAGE;
+    const int bslot = (static_cast<int>(ringB - lds) + slot * B_STAGE) * 16;
+    u32x4 fa[4][FM], fb[4][FN];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const lds_char* Lb = (const lds_char*)lds + bslot + 16 * s * (BN * 2) + btr[j];
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)Lb);
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Lb + 4 * (BN * 2)));
+        fb[s][j] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
+                         __builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 2, 3)),
+                         __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 0, 1)),
+                         __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i) fa[s][i] = LA[a_base + i * 256 + ((2 * s + lhalf) ^ perm)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (next) issue(zn, m0n, n0n, slot ^ 1);
+    __builtin_amdgcn_sched_barrier(0);
+
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mma<T>(fa[s][i], fb[s][j], acc[i][j]);
+
+    store_tile<FM, FN, WTM, WTN, NW, static_cast<int>(sizeof(lds))>(
+        out, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, wave, lane, z);
+    have = next;
+    z = zn;
+    m0 = m0n;
+    n0 = n0n;
+    slot ^= 1;
+  }
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN>
+hipError_t launch_m16s(const LaunchArgs& a, hipStream_t s) {
+  const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.batch;
+  // a.split: the workgroups the device keeps resident (set at plan time); a multiple
+  // of 8 so each XCD gets the same number
+  int64_t g = a.split > 1 ? a.split : 512;
+  if (tiles < g) g = (tiles + 7) / 8 * 8;
+  hipLaunchKernelGGL((gemm_m16s_kernel<T, BM, BN, WGM, WGN>), dim3(static_cast<unsigned>(g)),
+                     dim3(64 * WGM * WGN), 0, s, a);
+  return hipGetLastError();
+}
+
+#define G15_M16S(T, TN, BM, BN, WGM, WGN)                                                      \
+  {"m16s_" TN "_" #BM "x" #BN "x64_w" #WGM "x" #WGN, KIND_K1, T::code, BM, BN, 64,             \
+   64 * WGM * WGN, 2 * (BM + BN) * 128, 1, 1, launch_m16s<T, BM, BN, WGM, WGN>, 1}
+
+const KernelEntry kM16S[] = {
+    G15_M16S(bf16_t, "bf16", 128, 128, 2, 2), G15_M16S(bf16_t, "bf16", 128, 256, 2, 4),
+    G15_M16S(bf16_t, "bf16", 256, 128, 4, 2), G15_M16S(f16_t, "f16", 128, 128, 2, 2),
+    G15_M16S(f16_t, "f16", 128, 256, 2, 4),   G15_M16S(f16_t, "f16", 256, 128, 4, 2),
+};
+
+}  // namespace
+
+int mfma16_k1_entries(const KernelEntry** out) {
+  *out = kM16S;
+  return static_cast<int>(sizeof(kM16S) / sizeof(kM16S[0]));
+}
+
+}  // namespace g15

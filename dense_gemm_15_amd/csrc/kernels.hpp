@@ -15,6 +15,8 @@ enum KernelKind : int {
   KIND_F32 = 2,     // fp32 MFMA kernel
   KIND_GEMV = 3,    // few-row split-K kernel (M small)
   KIND_LADDER = 4,  // optimisation-ladder rungs: run only when forced by name
+  KIND_K1 = 5,      // one K slice (K <= bk), workgroups streaming over tiles: taken
+                    // by the measured shape table or by name, not the cost model
 };
 
 // One launch: a strided batch of row-major products C = epi(A x B).
@@ -31,7 +33,7 @@ struct LaunchArgs {
   Epi epi;
   void* workspace;      // split-K partials (GEMV kind only)
   int64_t workspace_bytes;
-  int split;            // split-K factor (GEMV kind only)
+  int split;            // split-K factor (GEMV kind); resident workgroups (K1 kind)
   // Row strides in elements. Every kernel handles lda = K, ldb = N, ldc = N;
   // only the m16d kernels take other strides (operands packed into padded rows).
   int64_t lda, ldb, ldc;
@@ -70,5 +72,6 @@ int f32_entries(const KernelEntry** out);
 int f32_dlds_entries(const KernelEntry** out);
 int gemv_entries(const KernelEntry** out);
 int ladder_entries(const KernelEntry** out);
+int mfma16_k1_entries(const KernelEntry** out);
 
 }  // namespace g15

@@ -165,7 +165,7 @@ TUNED = [
     ((8192, 8192, 8192), 1, "bf16", "m16d_bf16_256x256x64_w4x2_a3_b4_r1"),
     ((8192, 3072, 768), 1, "bf16", "m16t_bf16_128x128x64_w2x2_a2_b2"),
     ((8192, 768, 3072), 1, "bf16", "m16d_bf16_128x256x64_w2x4_a3_b4_r1"),
-    ((512, 512, 64), 96, "bf16", "m16d_bf16_128x256x64_w2x4_a3_b4_r1"),
+    ((512, 512, 64), 96, "bf16", "m16s_bf16_256x128x64_w4x2"),
     ((2048, 2048, 2048), 1, "bf16", "m16d_bf16_128x128x64_w2x2_a3_b4_r1"),
     ((512, 64, 512), 96, "bf16", "m16t_bf16_128x128x64_w2x2_a2_b2"),
     ((512, 512, 512), 1, "f16", "m16d_f16_64x128x64_w2x2_a4_b4_r2"),

@@ -54,7 +54,7 @@ def _dtype_of(name):
 
 
 CONFIGS = _configs()
-TILE_CONFIGS = [c for c in CONFIGS if not c.startswith("gemv") and not c.startswith("m16n")
+TILE_CONFIGS = [c for c in CONFIGS if not c.startswith(("gemv", "m16n", "m16s"))
                 and "acc16" not in c]
 NT_CONFIGS = [c for c in CONFIGS if c.startswith("m16n")]
 GEMV_CONFIGS = [c for c in CONFIGS if c.startswith("gemv")]
