@@ -163,7 +163,7 @@ const TunedRow kTuned[] = {
     {false, 2048, 2048, 2048, 1, "m16n_{t}_128x128x64_w2x2_a3_b3"},
     {false, 8192, 3072, 768, 1, "m16n_{t}_128x128x64_w2x2_a2_b2"},
     {false, 8192, 768, 3072, 1, "m16n_{t}_128x256x64_w2x4_a3_b3"},
-    {false, 512, 512, 64, 96, "m16n_{t}_128x128x64_w2x2_a2_b2"},
+    {false, 512, 512, 64, 96, "m16s_{t}_128x128x64_w2x2_nk"},  // Q K^T with K as stored
     {false, 512, 64, 512, 96, "m16t_{t}_128x128x64_w2x2_a2_b2"},  // 96 heads of P V
     {false, 512, 64, 512, 96, "m16n_{t}_128x128x64_w2x2_a2_b2"},
     {true, 4096, 4096, 4096, 1, "f32d_256x256x16_w4x2_a3"},
@@ -274,12 +274,11 @@ int tuned_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, i
   for (const TunedRow& r : kTuned) {
     if (r.f32 != (dtype == GEMM_F32) || r.M != M || r.N != N || r.K != K || r.batch != batch)
       continue;
-    if ((std::strncmp(r.config, "m16n_", 5) == 0) != b_nk) continue;
     std::string name(r.config);
     const size_t at = name.find("{t}");
     if (at != std::string::npos) name.replace(at, 3, dtype == GEMM_BF16 ? "bf16" : "f16");
     for (int i = 0; i < static_cast<int>(all.size()); ++i)
-      if (name == all[i].name) return i;
+      if (name == all[i].name && (all[i].b_nk != 0) == b_nk) return i;
   }
   return -1;
 }

@@ -37,7 +37,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 
-template <typename T, int BM, int BN, int WGM, int WGN>
+template <typename T, int BM, int BN, int WGM, int WGN, bool BROW>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a) {
   constexpr int BK = 64;
   constexpr int NW = WGM * WGN;
@@ -50,7 +50,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
   static_assert(BM % (8 * NW) == 0 && AI >= 1, "A rows must split evenly over the waves");
   static_assert(BN % (8 * NW) == 0 && BI >= 1, "B chunks must split evenly over the waves");
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 block");
-  static_assert(CPR_B >= 16 && 64 % CPR_B == 0, "B rows of 128 or 256 columns");
+  static_assert(!BROW || (CPR_B >= 16 && 64 % CPR_B == 0), "row-major B: 128 or 256 columns");
   __shared__ u32x4 lds[2 * (A_STAGE + B_STAGE)];
   u32x4* const ringA = lds;
   u32x4* const ringB = lds + 2 * A_STAGE;
@@ -79,12 +79,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
     a_koff[i] = static_cast<uint32_t>(chk * 8);
     a_kin[i] = chk * 8 < K;  // K is a multiple of 8: a chunk is wholly inside K or past it
   }
+  // B given transposed (Bt [N x K], !BROW) loads like A: rows n, chunks of k.
   int b_row[BI], b_col[BI];
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
-    const int row = (wave * BI + i) * RPI + lane / CPR_B;
-    b_row[i] = row;
-    b_col[i] = ((lane % CPR_B) ^ (4 * (row & 3))) * 8;
+    if constexpr (BROW) {
+      const int row = (wave * BI + i) * RPI + lane / CPR_B;
+      b_row[i] = row;
+      b_col[i] = ((lane % CPR_B) ^ (4 * (row & 3))) * 8;
+    } else {
+      // slot row (wave BI + i) 8 + l / 8 is n within the tile; b_row holds the k of
+      // this lane's chunk, or K for a chunk past K
+      const int chk = (lane & 7) ^ (lane >> 3) ^ ((wave * BI + i) & 3);
+      b_col[i] = (wave * BI + i) * 8 + (lane >> 3);
+      b_row[i] = chk * 8 < K ? chk * 8 : K;
+    }
   }
   // k at or past K: zero those chunks of both slots once
 #pragma unroll
@@ -135,7 +144,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
     const uint16_t* Az = static_cast<const uint16_t*>(a.A) + z * a.sA;
     const uint16_t* Bz = static_cast<const uint16_t*>(a.B) + z * a.sB;
     const auto rA = rsrc(Az, static_cast<uint32_t>(static_cast<int64_t>(M) * LDA * 2));
-    const auto rB = rsrc(Bz, static_cast<uint32_t>(static_cast<int64_t>(K) * LDB * 2));
+    const auto rB = rsrc(Bz, static_cast<uint32_t>(static_cast<int64_t>(BROW ? K : N) * LDB * 2));
 #pragma unroll
     for (int i = 0; i < AI; ++i) {
       const int gm = m0 + a_row[i];
@@ -147,9 +156,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
       const int gn = n0 + b_col[i];
-      const uint32_t off = (b_row[i] < K && gn < N)
-                               ? static_cast<uint32_t>(b_row[i] * LDB + gn) * 2u
-                               : OOB;
+      // row-major B: row b_row (k), column gn; transposed: row gn (n), k chunk at b_row
+      const uint32_t off =
+          (b_row[i] < K && gn < N)
+              ? static_cast<uint32_t>(BROW ? b_row[i] * LDB + gn : gn * LDB + b_row[i]) * 2u
+              : OOB;
       u32x4* dst = ringB + slot * B_STAGE + (wave * BI + i) * 64;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)dst, 16, off, 0, 0, 0);
     }
@@ -162,6 +173,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
   const int lrow = lane & 31, lhalf = lane >> 5;
   const int a_base = (wm * WTM + lrow) * 8;
   const int perm = (lrow & 7) ^ ((lrow >> 3) & 3);
+  // transposed B: fragment row wn*WTN + 32 j + (lane & 31), laid out like A
+  const int b_base = (wn * WTN + lrow) * 8;
+  const int bperm = (lrow & 7) ^ (((wn * WTN + lrow) >> 3) & 3);
   int btr[FN];
   {
     const int g = lane >> 4, t = lane & 15;
@@ -190,12 +204,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
     lds_barrier();  // every wave's loads have landed; every wave is done with the other slot
 
     const u32x4* LA = ringA + slot * A_STAGE;
+    const u32x4* LB = ringB + slot * B_STAGE;
     const int bslot = (static_cast<int>(ringB - lds) + slot * B_STAGE) * 16;
     u32x4 fa[4][FM], fb[4][FN];
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
+        if constexpr (!BROW) {
+          fb[s][j] = LB[b_base + j * 256 + ((2 * s + lhalf) ^ bperm)];
+          continue;
+        }
         const lds_char* Lb = (const lds_char*)lds + bslot + 16 * s * (BN * 2) + btr[j];
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)Lb);
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Lb + 4 * (BN * 2)));
@@ -234,26 +253,30 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
   }
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN>
+template <typename T, int BM, int BN, int WGM, int WGN, bool BROW>
 hipError_t launch_m16s(const LaunchArgs& a, hipStream_t s) {
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.batch;
   // a.split: the workgroups the device keeps resident (set at plan time); a multiple
   // of 8 so each XCD gets the same number
   int64_t g = a.split > 1 ? a.split : 512;
   if (tiles < g) g = (tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_m16s_kernel<T, BM, BN, WGM, WGN>), dim3(static_cast<unsigned>(g)),
+  hipLaunchKernelGGL((gemm_m16s_kernel<T, BM, BN, WGM, WGN, BROW>), dim3(static_cast<unsigned>(g)),
                      dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }
 
-#define G15_M16S(T, TN, BM, BN, WGM, WGN)                                                      \
-  {"m16s_" TN "_" #BM "x" #BN "x64_w" #WGM "x" #WGN, KIND_K1, T::code, BM, BN, 64,             \
-   64 * WGM * WGN, 2 * (BM + BN) * 128, 1, 1, launch_m16s<T, BM, BN, WGM, WGN>, 1}
+// SFX "" for row-major B [K x N], "_nk" for B given transposed [N x K]
+#define G15_M16S(T, TN, BM, BN, WGM, WGN, BROW, SFX)                                           \
+  {"m16s_" TN "_" #BM "x" #BN "x64_w" #WGM "x" #WGN SFX, KIND_K1, T::code, BM, BN, 64,          \
+   64 * WGM * WGN, 2 * (BM + BN) * 128, 1, 1, launch_m16s<T, BM, BN, WGM, WGN, BROW>, 1,        \
+   BROW ? 0 : 1}
+#define G15_M16S_ALL(T, TN, BROW, SFX)                                      \
+  G15_M16S(T, TN, 128, 128, 2, 2, BROW, SFX), G15_M16S(T, TN, 128, 256, 2, 4, BROW, SFX), \
+      G15_M16S(T, TN, 256, 128, 4, 2, BROW, SFX)
 
 const KernelEntry kM16S[] = {
-    G15_M16S(bf16_t, "bf16", 128, 128, 2, 2), G15_M16S(bf16_t, "bf16", 128, 256, 2, 4),
-    G15_M16S(bf16_t, "bf16", 256, 128, 4, 2), G15_M16S(f16_t, "f16", 128, 128, 2, 2),
-    G15_M16S(f16_t, "f16", 128, 256, 2, 4),   G15_M16S(f16_t, "f16", 256, 128, 4, 2),
+    G15_M16S_ALL(bf16_t, "bf16", true, ""),    G15_M16S_ALL(f16_t, "f16", true, ""),
+    G15_M16S_ALL(bf16_t, "bf16", false, "_nk"), G15_M16S_ALL(f16_t, "f16", false, "_nk"),
 };
 
 }  // namespace

@@ -173,6 +173,18 @@ TUNED = [
 ]
 
 
+def test_select_tuned_transposed_b():
+    """The shape table keeps the two B layouts apart: 4096^3 and the 96-head scores
+    product with B given transposed take their own measured configurations."""
+    nk = dict(b_layout="nk", **MI355X)
+    assert g.config_names()[g.select(4096, 4096, 4096, "bf16", **nk).config] == \
+        "m16n_bf16_256x256x64_w2x4_a3_b2"
+    assert g.config_names()[g.select(512, 512, 64, "bf16", batch_hint=96, **nk).config] == \
+        "m16s_bf16_128x128x64_w2x2_nk"
+    assert g.config_names()[g.select(512, 512, 64, "bf16", batch_hint=96, **MI355X).config] == \
+        "m16s_bf16_256x128x64_w4x2"
+
+
 @pytest.mark.parametrize("shape,batch,dtype,name", TUNED)
 def test_select_uses_tuned_shapes(shape, batch, dtype, name):
     """Workload shapes take their measured configuration, on the device they were

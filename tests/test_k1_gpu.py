@@ -1,5 +1,6 @@
 """Parity of the one-slice streaming kernels (m16s_*: K <= 64, each workgroup looping
-over tiles and batch items with the next tile's operands loading) against the fp64
+over tiles and batch items with the next tile's operands loading; *_nk with B given
+transposed) against the fp64
 oracle, through the C ABI: ragged shapes with K below, at and well under 64, more
 tiles than resident workgroups and fewer, batches split by item over the XCDs (8 or
 more items, an uneven number per XCD) and not (fewer items), every epilogue and
@@ -50,6 +51,20 @@ def _dtype(name):
     return "bf16" if "_bf16_" in name else "f16"
 
 
+def _nk(name):
+    """Configurations for B given transposed (Bt [N x K]) end in _nk."""
+    return name.endswith("_nk")
+
+
+def _plan(g, name, M, N, K, **kw):
+    return g.Plan(M, N, K, _dtype(name), config=name, b_layout="nk" if _nk(name) else "kn", **kw)
+
+
+def _given(name, B):
+    """B as the configuration takes it (the oracle always gets B [.., K, N])."""
+    return B.transpose(-1, -2).contiguous() if _nk(name) else B
+
+
 @pytest.mark.parametrize("name", K1)
 def test_k1_ragged(g, name):
     """Ragged shapes with K = 64, 40, 16 and 8, each element against the oracle; a
@@ -59,18 +74,18 @@ def test_k1_ragged(g, name):
     for si, (M, N, K) in enumerate([(2 * bm + 3, bn + 8, 64), (bm, 2 * bn + 8, 40), (1, 8, 8),
                                     (3 * bm + 5, 5 * bn + 24, 16)]):
         say(f"[{name}] M={M} N={N} K={K}")
-        plan = g.Plan(M, N, K, dtype, config=name)
+        plan = _plan(g, name, M, N, K)
         assert plan.config_name == name
         for kind in ("uniform", "int"):
             A, B = gc.inputs(M, N, K, dtype, 1300 + 11 * si, kind)
-            C = gc.run_gpu(plan, A, B)
+            C = gc.run_gpu(plan, A, _given(name, B))
             r = gc.check_full(C, A, B, dtype, exact=(kind == "int"))
             assert r["ok"], (name, M, N, K, kind, r)
     M, N, K = 4096 + 5, 4096 + 8, 64
     say(f"[{name}] M={M} N={N} K={K} (more tiles than workgroups)")
-    plan = g.Plan(M, N, K, dtype, config=name)
+    plan = _plan(g, name, M, N, K)
     A, B = gc.inputs(M, N, K, dtype, 1350, "uniform")
-    C = gc.run_gpu(plan, A, B)
+    C = gc.run_gpu(plan, A, _given(name, B))
     rows, cols = gc.sample_indices(M, N, 400, 1351)
     r = gc.check_sampled(C, A, B, dtype, rows, cols)
     assert r["ok"], (name, r)
@@ -89,13 +104,13 @@ def test_k1_epilogues(g, name):
              dict(out_dtype=dtype, resid=True, scale=-2.0, bias=True)]
     for ci, epi in enumerate(cases):
         say(f"[{name}] epilogue {epi}")
-        plan = g.Plan(M, N, K, dtype, config=name, **epi)
+        plan = _plan(g, name, M, N, K, **epi)
         assert plan.config_name == name
         A, B = gc.inputs(M, N, K, dtype, 1400 + ci)
         bias = synth.normal(1410 + ci, (N,), 0.5, "f32") if epi.get("bias") else None
         resid = (synth.normal(1420 + ci, (M, N), 1.0, epi["out_dtype"])
                  if epi.get("resid") else None)
-        C = gc.run_gpu(plan, A, B, bias, resid)
+        C = gc.run_gpu(plan, A, _given(name, B), bias, resid)
         r = gc.check_full(C, A, B, dtype, epi["out_dtype"], bias, resid, epi.get("scale"),
                           epi.get("gelu", False))
         assert r["ok"], (name, epi, r)
@@ -105,15 +120,15 @@ def test_k1_epilogues(g, name):
 def test_k1_batched_ragged(g, nb, M, N):
     """Batches of ragged products with K = 64: fewer than 8 items (tiles strided over
     the workgroups), 9 and 17 items (split by item over the XCDs, uneven per XCD);
-    every element of every item, on every bf16 configuration."""
+    every element of every item, on every bf16 configuration (both B layouts)."""
     K = 64
     for name in [c for c in K1 if "_bf16_" in c]:
         say(f"[{name}] batch {nb} M={M} N={N} K={K}")
-        plan = g.Plan(M, N, K, "bf16", config=name, batch_hint=nb)
+        plan = _plan(g, name, M, N, K, batch_hint=nb)
         A = synth.uniform(1500 + nb, (nb, M, K), "bf16")
         B = synth.uniform(1501 + nb, (nb, K, N), "bf16")
         dev = torch.device("cuda")
-        C = plan.run_batched(A.to(dev), B.to(dev))
+        C = plan.run_batched(A.to(dev), _given(name, B).to(dev))
         torch.cuda.synchronize()
         C = C.cpu()
         for b in range(nb):
@@ -128,12 +143,12 @@ def test_k1_attention_scores(g):
     Q, Kt = synth.qk_inputs()
     nb, S, D = Q.shape
     dev = torch.device("cuda")
-    Qd, Ktd = Q.to(dev), Kt.to(dev)
+    Qd = Q.to(dev)
     rng = np.random.default_rng(1600)
     for name in [c for c in K1 if "_bf16_" in c]:
         say(f"[{name}] 96 x 512x512x64")
-        plan = g.Plan(S, S, D, "bf16", config=name, batch_hint=nb)
-        out = plan.run_batched(Qd, Ktd)
+        plan = _plan(g, name, S, S, D, batch_hint=nb)
+        out = plan.run_batched(Qd, _given(name, Kt).to(dev))
         torch.cuda.synchronize()
         out = out.cpu()
         for b in range(nb):
@@ -149,12 +164,14 @@ def test_k1_needs_one_slice(g):
     """K above 64 cannot run on a one-slice configuration: plan creation refuses it."""
     with pytest.raises(g.GemmError):
         g.Plan(128, 128, 72, "bf16", config=K1[0])
+    with pytest.raises(g.GemmError):
+        g.Plan(128, 128, 72, "bf16", config=[c for c in K1 if _nk(c)][0], b_layout="nk")
 
 
 def test_k1_graph_replay(g):
     """The streaming kernel captured in a HIP graph and replayed, with eager work and
     a changed A between replays: every replay equals the eager result bit for bit."""
-    name = [c for c in K1 if "_bf16_" in c][0]
+    name = [c for c in K1 if "_bf16_" in c and not _nk(c)][0]
     nb, M, N, K = 9, 300, 264, 64
     plan = g.Plan(M, N, K, "bf16", config=name, batch_hint=nb)
     dev = torch.device("cuda")
