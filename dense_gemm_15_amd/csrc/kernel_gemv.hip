@@ -212,12 +212,12 @@ __global__ __launch_bounds__(256) void gemv_reduce_kernel(LaunchArgs a, int64_t 
   const int64_t stride = static_cast<int64_t>(MR) * N;
   const float* p = ws + m * N + n;
   float s = 0.f;
-  for (int s0 = 0; s0 < a.split; s0 += 16) {  // 16 loads in flight, summed in slice order
-    float t[16];
+  for (int s0 = 0; s0 < a.split; s0 += 32) {  // 32 loads in flight, summed in slice order
+    float t[32];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) t[j] = s0 + j < a.split ? p[(s0 + j) * stride] : 0.f;
+    for (int j = 0; j < 32; ++j) t[j] = s0 + j < a.split ? p[(s0 + j) * stride] : 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) s += t[j];
+    for (int j = 0; j < 32; ++j) s += t[j];
   }
   const Epi& e = a.epi;
   const int64_t ob = e.out_dtype == DT_F32 ? 4 : 2;
