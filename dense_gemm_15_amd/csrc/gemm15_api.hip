@@ -23,6 +23,7 @@
 
 #include "../../include/gemm15.h"
 #include "kernels.hpp"
+#include "splitk.hpp"
 #include "softmax.hpp"
 
 using namespace g15;
@@ -239,6 +240,7 @@ int64_t gemv_workspace_bytes(const KernelEntry& k, int64_t N, int split) {
 int64_t cfg_workgroups(const KernelEntry& k, int64_t M, int64_t N, int split, int64_t batch) {
   const int64_t tiles = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn);
   if (k.kind == KIND_K1) return tiles * batch < split ? (tiles * batch + 7) / 8 * 8 : split;
+  if (k.kind == KIND_MFMA16 && split > 1) return tiles * split;  // split-K, one batch item
   return k.kind == KIND_GEMV ? tiles * split : tiles * batch;
 }
 
@@ -295,6 +297,23 @@ int64_t round_up8(int64_t x) { return (x + 7) / 8 * 8; }
 
 bool is_m16d(const KernelEntry& k) { return std::strncmp(k.name, "m16d_", 5) == 0; }
 
+// Split-K factor of a tile configuration on a problem with few tiles and a long K
+// (at most half the CUs busy, at least 32 K slices each): S slices of K, each a
+// multiple of 8 elements (16-byte aligned A columns) and at least 512 deep, with at
+// most two workgroups per CU in all. Measured: 256 x 256 x 4096 11.4 us split 8
+// against 28.9 us whole, 128 x 128 x 65536 52.7 against 356 us; 512^3 and 1024^3
+// (8 and 16 slices) are faster whole (the partial sums and the second kernel cost
+// ~3-10 us). Only the m16d kernels, which take any row strides.
+int tile_split(const KernelEntry& k, int64_t M, int64_t N, int64_t K, int64_t batch,
+               const gemm_device_desc& dev) {
+  if (!is_m16d(k) || K < 2048) return 1;
+  const int64_t tiles = ((M + k.bm - 1) / k.bm) * ((N + k.bn - 1) / k.bn) * batch;
+  if (2 * tiles > dev.cu_count) return 1;
+  for (int S = 32; S >= 2; S /= 2)
+    if (K % (8 * S) == 0 && K / S >= 512 && tiles * S <= 2 * dev.cu_count) return S;
+  return 1;
+}
+
 Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dtype,
                         const gemm_epilogue& epi, int64_t batch, bool aligned16, bool b_nk) {
   const auto& all = registry().all;
@@ -336,6 +355,22 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
   if (tuned >= 0 && cfg_fits(all[tuned], dtype, vec_a, vec_b, dev, M, N, K, epi.out_dtype, b_nk)) {
     s.config = tuned;
     return s;
+  }
+  // Few tiles and a long K: the m16d configuration with the smallest tile that
+  // runs the product split along K (the cost model does not model the split).
+  if (!b_nk && dtype != GEMM_F32 && vec_a && vec_b) {
+    int pick = -1;
+    for (int i = 0; i < static_cast<int>(all.size()); ++i) {
+      const KernelEntry& k = all[i];
+      if (!is_m16d(k) || !cfg_fits(k, dtype, vec_a, vec_b, dev, M, N, K, epi.out_dtype, b_nk))
+        continue;
+      if (tile_split(k, M, N, K, batch, dev) < 2) continue;
+      if (pick < 0 || k.bm * k.bn < all[pick].bm * all[pick].bn) pick = i;
+    }
+    if (pick >= 0) {
+      s.config = pick;
+      return s;
+    }
   }
   double cost = 0;
   s.config = best_for(vec_a, vec_b, K, N, any, &cost);
@@ -493,6 +528,65 @@ int run_packed(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, con
   return GEMM_OK;
 }
 
+// Split-K run of a tile configuration: the S slices of K run as the S items of one
+// strided batch (A advanced Kc columns, B Kc rows, K = Kc, C the workspace's fp32
+// partial products, no epilogue; A's row stride stays K, and the kernel's K tail
+// keeps each item inside its slice), then the reduction kernel adds the partials in
+// slice order and applies the epilogue. Batch items run one after the other and
+// share the workspace.
+int run_split_k(const gemm_plan* p, const KernelEntry& k, int64_t batch, const void* A,
+                int64_t sA, const void* B, int64_t sB, const float* bias, const void* resid,
+                int64_t sR, void* C, int64_t sC, hipStream_t s) {
+  const int S = p->split;
+  const int64_t kc = p->K / S;
+  const int64_t ie = elem_bytes(p->dtype);
+  for (int64_t z = 0; z < batch; ++z) {
+    LaunchArgs la{};
+    la.M = p->M;
+    la.N = p->N;
+    la.K = kc;
+    la.batch = S;
+    la.A = static_cast<const char*>(A) + z * sA * ie;
+    la.sA = kc;
+    la.B = static_cast<const char*>(B) + z * sB * ie;
+    la.sB = kc * p->N;
+    la.C = p->workspace;
+    la.sC = p->M * p->N;
+    la.sR = 0;
+    la.epi.flags = 0;
+    la.epi.scale = 1.f;
+    la.epi.bias = nullptr;
+    la.epi.resid = nullptr;
+    la.epi.out_dtype = DT_F32;
+    la.workspace = nullptr;
+    la.workspace_bytes = 0;
+    la.split = 1;
+    la.lda = p->K;
+    la.ldb = p->N;
+    la.ldc = p->N;
+    la.c_vec = 1;
+    if (k.launch(la, s) != hipSuccess) return GEMM_ERR_HIP;
+    LaunchArgs lr{};
+    lr.M = p->M;
+    lr.N = p->N;
+    lr.K = p->K;
+    lr.batch = 1;
+    lr.C = C;
+    lr.sC = sC;
+    lr.sR = sR;
+    lr.epi.flags = p->epi.flags;
+    lr.epi.scale = p->epi.scale;
+    lr.epi.bias = bias;
+    lr.epi.resid = resid;
+    lr.epi.out_dtype = p->epi.out_dtype;
+    lr.workspace = p->workspace;
+    lr.workspace_bytes = p->workspace_bytes;
+    lr.split = S;
+    if (launch_splitk_reduce(lr, z, p->M, s) != hipSuccess) return GEMM_ERR_HIP;
+  }
+  return GEMM_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -571,6 +665,17 @@ gemm_plan* gemm_plan_create_layout(int64_t M, int64_t N, int64_t K, int32_t dtyp
   }
   const KernelEntry& k = all[cfg];
   if (k.kind == KIND_K1) p->split = k1_workgroups(k, desc);
+  if (k.kind == KIND_MFMA16 && !sel.packed && !b_nk) {
+    p->split = tile_split(k, M, N, K, batch_hint, desc);
+    if (p->split > 1) {
+      p->workspace_bytes = static_cast<int64_t>(p->split) * M * N * 4;
+      if (hipMalloc(&p->workspace, static_cast<size_t>(p->workspace_bytes)) != hipSuccess) {
+        (void)hipGetLastError();
+        delete p;
+        return fail(GEMM_ERR_NOMEM);
+      }
+    }
+  }
   if (k.kind == KIND_GEMV) {
     p->split = gemv_split(k, N, K, batch_hint, desc);
     p->workspace_bytes = gemv_workspace_bytes(k, N, p->split);
@@ -644,6 +749,9 @@ int gemm_run_strided_batched(const gemm_plan* p, int64_t batch, const void* A, i
   const int ci = a16 && !p->packed ? p->config : p->fallback;
   if (ci < 0) return GEMM_ERR_ALIGN;  // transposed B: 16-byte aligned operands required
   const KernelEntry& k = all[ci];
+  if (p->split > 1 && ci == p->config && k.kind == KIND_MFMA16)
+    return run_split_k(p, k, batch, A, sA, B, sB, bias, resid, sR, C, sC,
+                       static_cast<hipStream_t>(stream));
 
   const int64_t tiles = ((p->M + k.bm - 1) / k.bm) * ((p->N + k.bn - 1) / k.bn);
   if (tiles > 0x7fffffff) return GEMM_ERR_SHAPE;
@@ -753,7 +861,9 @@ int gemm_select_layout(const gemm_device_desc* dev, int64_t M, int64_t N, int64_
   out->lds_bytes = k.lds_bytes;
   out->split = k.kind == KIND_GEMV ? gemv_split(k, N, K, batch_hint, *dev)
                : k.kind == KIND_K1   ? k1_workgroups(k, *dev)
-                                     : 1;
+               : (k.kind == KIND_MFMA16 && !sel.packed && !b_nk)
+                   ? tile_split(k, M, N, K, batch_hint, *dev)
+                   : 1;
   out->workgroups = cfg_workgroups(k, M, N, out->split, batch_hint);
   out->packed = sel.packed;
   return GEMM_OK;

@@ -20,6 +20,7 @@
 // reach memory, the counter's round trip and the partials' reads in turn. Accumulation is
 // fp32; the result does not depend on timing (fixed summation order).
 #include "kernels.hpp"
+#include "splitk.hpp"
 
 namespace g15 {
 namespace {
@@ -201,15 +202,15 @@ __global__ __launch_bounds__(GNT) void gemv_kernel(LaunchArgs a, int64_t z0) {
   }
 }
 
-// C[m][n] = epi(sum over s of partial[s][m][n]), s ascending; one thread per element.
-template <int MR>
-__global__ __launch_bounds__(256) void gemv_reduce_kernel(LaunchArgs a, int64_t z) {
+// C[m][n] = epi(sum over s of partial[s][m][n]), s ascending; one thread per element
+// (partial [split][rows][N]).
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(LaunchArgs a, int64_t z, int64_t rows) {
   const int64_t N = a.N;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= a.M * N) return;
   const int64_t m = i / N, n = i - m * N;
   const float* ws = static_cast<const float*>(a.workspace);
-  const int64_t stride = static_cast<int64_t>(MR) * N;
+  const int64_t stride = rows * N;
   const float* p = ws + m * N + n;
   float s = 0.f;
   for (int s0 = 0; s0 < a.split; s0 += 32) {  // 32 loads in flight, summed in slice order
@@ -240,14 +241,12 @@ hipError_t launch_gemv(const LaunchArgs& a, hipStream_t s) {
   if (!a.workspace ||
       a.workspace_bytes < static_cast<int64_t>(a.split) * MR * a.N * 4)
     return hipErrorInvalidValue;
-  const unsigned rblocks = static_cast<unsigned>((a.M * a.N + 255) / 256);
   for (int64_t z = 0; z < a.batch; ++z) {  // batch items share the workspace, in stream order
     hipLaunchKernelGGL((gemv_kernel<T, MR, KMAX, U>), dim3(strips, static_cast<unsigned>(a.split)),
                        dim3(GNT), 0, s, a, z);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((gemv_reduce_kernel<MR>), dim3(rblocks), dim3(256), 0, s, a, z);
-    err = hipGetLastError();
+    err = launch_splitk_reduce(a, z, MR, s);
     if (err != hipSuccess) return err;
   }
   return hipSuccess;
@@ -269,6 +268,12 @@ const KernelEntry kGemv[] = {
 };
 
 }  // namespace
+
+hipError_t launch_splitk_reduce(const LaunchArgs& a, int64_t z, int64_t rows, hipStream_t s) {
+  const unsigned blocks = static_cast<unsigned>((a.M * a.N + 255) / 256);
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3(blocks), dim3(256), 0, s, a, z, rows);
+  return hipGetLastError();
+}
 
 int gemv_entries(const KernelEntry** out) {
   *out = kGemv;

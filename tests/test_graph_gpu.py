@@ -33,6 +33,8 @@ CASES = [
     (300, 261, 203, "f16", dict()),                     # padded copies of A and B, element-wise C
     (512, 512, 256, "bf16", dict(b_layout="nk")),       # B given transposed
     (200, 136, 77, "bf16", dict(b_layout="nk")),        # transposed B with padded copies
+    (256, 256, 4096, "bf16", dict(bias=True, gelu=True, out_dtype="bf16",
+                                  config="m16d_bf16_64x128x64_w2x2_a4_b4_r2")),  # split along K
 ]
 
 

@@ -560,6 +560,50 @@ def test_wide_b_rows(g):
         torch.cuda.empty_cache()
 
 
+SPLIT_CASES = [
+    # (M, N, K, dtype, epilogue, batch, expected split), on m16d_{t}_64x128x64_w2x2_a4_b4_r2
+    (256, 256, 4096, "f16", dict(), 1, 8),
+    (256, 256, 4096, "bf16", dict(bias=True, gelu=True, out_dtype="bf16"), 1, 8),
+    (200, 296, 8192, "bf16", dict(resid=True, scale=0.5), 1, 16),
+    (130, 136, 4096, "f16", dict(bias=True, out_dtype="f16"), 1, 8),
+    (256, 256, 4096, "bf16", dict(bias=True), 3, 8),
+    (512, 512, 512, "bf16", dict(), 1, 1),  # 8 K slices: faster whole
+]
+
+
+@pytest.mark.parametrize("case", range(len(SPLIT_CASES)))
+def test_split_k_tiles(g, case):
+    """Tile products with few tiles and a long K run split along K (the slices as
+    the items of one strided batch into fp32 partials, then the reduction kernel
+    adds them in slice order and applies the epilogue): every element against the
+    oracle, float and small-integer inputs, batch items in turn on one workspace,
+    each plan run twice; a short K stays whole."""
+    M, N, K, dtype, epi, nb, split = SPLIT_CASES[case]
+    cfg = f"m16d_{dtype}_64x128x64_w2x2_a4_b4_r2"
+    out_dtype = epi.get("out_dtype", "f32")
+    exact = not any(epi.get(f) for f in ("bias", "gelu", "resid"))  # integer sums stay exact
+    plan = g.Plan(M, N, K, dtype, batch_hint=nb, config=cfg, **epi)
+    d = _describe(plan)
+    say(f"[split-K] {plan.describe()}")
+    assert int(d["split"]) == split and d["config"].startswith("m16d"), d
+    dev = torch.device("cuda")
+    for kind in ("uniform", "int"):
+        A = torch.stack([gc.inputs(M, N, K, dtype, 1800 + 10 * case + b, kind)[0] for b in range(nb)])
+        B = torch.stack([gc.inputs(M, N, K, dtype, 1800 + 10 * case + b, kind)[1] for b in range(nb)])
+        bias = synth.normal(1890 + case, (N,), 0.5, "f32") if epi.get("bias") else None
+        resid = synth.normal(1895 + case, (nb, M, N), 1.0, out_dtype) if epi.get("resid") else None
+        for rep in range(2):
+            C = plan.run_batched(A.to(dev), B.to(dev), None if bias is None else bias.to(dev),
+                                 None if resid is None else resid.to(dev))
+            torch.cuda.synchronize()
+            C = C.cpu()
+            for b in range(nb):
+                r = gc.check_full(C[b], A[b], B[b], dtype, out_dtype, bias,
+                                  None if resid is None else resid[b], epi.get("scale"),
+                                  epi.get("gelu", False), exact=exact and kind == "int")
+                assert r["ok"], (case, kind, rep, b, r)
+
+
 def test_repeat_shape_hits_cache(g):
     """A repeated shape is served from the exact-shape cache."""
     h0, m0, _ = g.cache_stats()
