@@ -828,7 +828,8 @@ int gemm_plan_describe(const gemm_plan* p, char* buf, size_t len) {
       "config=%s id=%d tile=%dx%dx%d threads=%d lds=%d workgroups=%lld split=%d packed=%d "
       "b=%s fallback=%s",
       k.name, p->config, k.bm, k.bn, k.bk, k.threads, k.lds_bytes,
-      static_cast<long long>(cfg_workgroups(k, p->M, p->N, p->split, p->batch_hint)), p->split,
+      static_cast<long long>(cfg_workgroups(k, p->M, p->N, p->split, p->batch_hint)),
+      k.kind == KIND_K1 ? 1 : p->split,  // a K1 plan keeps its resident workgroups there
       p->packed, p->b_nk ? "nk" : "kn", p->fallback >= 0 ? all[p->fallback].name : "none");
   if (buf && len > 0) {
     std::strncpy(buf, tmp, len - 1);
@@ -860,11 +861,11 @@ int gemm_select_layout(const gemm_device_desc* dev, int64_t M, int64_t N, int64_
   out->threads = k.threads;
   out->lds_bytes = k.lds_bytes;
   out->split = k.kind == KIND_GEMV ? gemv_split(k, N, K, batch_hint, *dev)
-               : k.kind == KIND_K1   ? k1_workgroups(k, *dev)
                : (k.kind == KIND_MFMA16 && !sel.packed && !b_nk)
                    ? tile_split(k, M, N, K, batch_hint, *dev)
                    : 1;
-  out->workgroups = cfg_workgroups(k, M, N, out->split, batch_hint);
+  out->workgroups = cfg_workgroups(k, M, N, k.kind == KIND_K1 ? k1_workgroups(k, *dev) : out->split,
+                                   batch_hint);
   out->packed = sel.packed;
   return GEMM_OK;
 }

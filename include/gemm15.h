@@ -211,11 +211,13 @@ typedef struct gemm_device_desc {
 /* What a configuration choice resolves to. */
 typedef struct gemm_choice {
   int32_t config;    /* index for gemm_config_name / gemm_plan_create_ex */
-  int32_t kind;      /* 0 simple, 1 mfma16, 2 fp32 mfma, 3 few-row split-K */
+  int32_t kind;      /* 0 simple, 1 mfma16, 2 fp32 mfma, 3 few-row split-K, 4 optimisation-
+                        ladder rung (by name only), 5 one K slice streaming over tiles */
   int32_t bm, bn, bk;
   int32_t threads;
   int32_t lds_bytes;
-  int32_t split;     /* K split factor (1 = none) */
+  int32_t split;     /* K split factor (1 = none): the few-row kernel's, or a tile
+                        product's run as split-K partial sums */
   int64_t workgroups;
   int32_t packed;    /* bit 0: A, bit 1: B copied into 16-byte-padded rows before the kernel */
 } gemm_choice;

@@ -181,8 +181,10 @@ def test_select_tuned_transposed_b():
         "m16n_bf16_256x256x64_w2x4_a3_b2"
     assert g.config_names()[g.select(512, 512, 64, "bf16", batch_hint=96, **nk).config] == \
         "m16s_bf16_128x128x64_w2x2_nk"
-    assert g.config_names()[g.select(512, 512, 64, "bf16", batch_hint=96, **MI355X).config] == \
-        "m16s_bf16_256x128x64_w4x2"
+    c = g.select(512, 512, 64, "bf16", batch_hint=96, **MI355X)
+    assert g.config_names()[c.config] == "m16s_bf16_256x128x64_w4x2"
+    # the streaming kernel splits nothing and keeps every CU full (one 96 KB workgroup each)
+    assert c.split == 1 and c.workgroups == 256 and c.kind == 5
 
 
 @pytest.mark.parametrize("shape,batch,dtype,name", TUNED)
@@ -193,6 +195,18 @@ def test_select_uses_tuned_shapes(shape, batch, dtype, name):
     assert g.config_names()[ch.config] == name
     small = g.select(*shape, dtype, batch_hint=batch, cu_count=80, lds_bytes=65536)
     assert small.lds_bytes <= 65536
+
+
+def test_select_split_k_tiles():
+    """Few tiles and a long K take the smallest splitting m16d tile, split along K;
+    short K stays whole."""
+    for (M, N, K), split in [((256, 256, 4096), 8), ((64, 4096, 4096), 8),
+                             ((128, 128, 65536), 32), ((512, 512, 512), 1), ((1024, 1024, 1024), 1)]:
+        c = g.select(M, N, K, "bf16", **MI355X)
+        assert g.config_names()[c.config].startswith("m16d_bf16_64x128"), (M, N, K)
+        assert c.split == split, (M, N, K, c.split)
+        tiles = -(-M // 64) * -(-N // 128)
+        assert c.workgroups == tiles * split
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16", "f32"])
