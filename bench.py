@@ -520,7 +520,7 @@ def main():
         print("[bench] copy calibration: 3 x 256 MiB device copies", file=sys.stderr, flush=True)
     if args.all:
         for name in ("fp16_4096", "fp16_512", "gemv_1x4096x4096", "odd_127x1000x771",
-                     "odd_4095x4097x63"):
+                     "odd_4095x4097x63", "longk_256x256x4096", "longk_64x4096x4096"):
             extra[name] = gemm_workload(g, name, args.steps, args.warmup, graph=True)
             print(f"[bench] {json.dumps(extra[name])}", file=sys.stderr, flush=True)
         extra.update(ffn_workload(g, args.steps, args.warmup))

@@ -99,6 +99,9 @@ WORKLOADS = {
     "gemv_1x4096x4096": dict(kind="gemm", M=1, N=4096, K=4096, dtype="f16", seeds=(511, 512)),
     "odd_127x1000x771": dict(kind="gemm", M=127, N=1000, K=771, dtype="f16", seeds=(521, 522)),
     "odd_4095x4097x63": dict(kind="gemm", M=4095, N=4097, K=63, dtype="f16", seeds=(531, 532)),
+    # Few tiles, long K (the small-M x N, large-K shapes run split along K).
+    "longk_256x256x4096": dict(kind="gemm", M=256, N=256, K=4096, dtype="bf16", seeds=(541, 542)),
+    "longk_64x4096x4096": dict(kind="gemm", M=64, N=4096, K=4096, dtype="bf16", seeds=(543, 544)),
 }
 
 

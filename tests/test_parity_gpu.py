@@ -280,6 +280,26 @@ def test_workload_square_4096(g, name):
     assert np.isfinite(C.float().numpy()).all()
 
 
+@pytest.mark.parametrize("name", ["longk_256x256x4096", "longk_64x4096x4096"])
+def test_workload_long_k(g, name):
+    """The long-K benchmark workloads at their launch configuration (split along K):
+    256 x 256 x 4096 every element, 64 x 4096 x 4096 sampled elements (random,
+    corners, tile edges), against the oracle."""
+    w = synth.WORKLOADS[name]
+    M, N, K = w["M"], w["N"], w["K"]
+    A, B = synth.gemm_inputs(name)
+    plan = g.Plan(M, N, K, w["dtype"])
+    say(f"[{name}]", plan.describe())
+    assert int(_describe(plan)["split"]) > 1
+    C = gc.run_gpu(plan, A, B)
+    if M * N <= 65536:
+        r = gc.check_full(C, A, B, w["dtype"])
+    else:
+        rows, cols = gc.sample_indices(M, N, 2000, 7)
+        r = gc.check_sampled(C, A, B, w["dtype"], rows, cols)
+    assert r["ok"], r
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_square_4096_integer_rowsums(g, dtype):
     """Small-integer 4096^3: sampled elements exact, and every row sum of C equals
