@@ -71,27 +71,59 @@ import sys
 sys.path.insert(0, {root!r})
 import oracle
 from tests import oracle_pins
-lib = oracle.load({path!r})
-for pin in oracle_pins.PINS:
-    try:
-        pin(lib)
-    except Exception as e:
-        print("CAUGHT", pin.__name__, type(e).__name__)
-        sys.exit(0)
-print("MISSED")
-sys.exit(0)
+for name, path in {paths!r}:
+    lib = oracle.load(path)
+    verdict = "MISSED"
+    for pin in oracle_pins.PINS:
+        try:
+            pin(lib)
+        except Exception as e:
+            verdict = "CAUGHT " + pin.__name__ + " " + type(e).__name__
+            break
+    print("VERDICT", name, verdict, flush=True)
 """
 
 
-@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
-def test_pins_catch_mutant(tmp_path, name, old, new):
+def _run_pins(paths):
+    """Every mutant library in `paths` ([(name, path)]) through the pins in one
+    process (the pins import torch and scipy, which take seconds to load)."""
+    return subprocess.run([sys.executable, "-c", RUNNER.format(root=ROOT, paths=paths)],
+                          capture_output=True, text=True, timeout=900)
+
+
+@pytest.fixture(scope="module")
+def mutant_runs(tmp_path_factory):
+    """Build every mutant (in parallel), run them all through the pins at once; the
+    verdict lines by mutant name, with the libraries for a rerun."""
+    from concurrent.futures import ThreadPoolExecutor
+    d = tmp_path_factory.mktemp("mutants")
     src = open(oracle.SRC).read()
-    assert src.count(old) == 1, f"mutation site for {name} not unique/present"
-    mut = tmp_path / "mutant.c"
-    mut.write_text(src.replace(old, new))
-    so = tmp_path / "libmutant.so"
-    oracle.build(str(mut), str(so))
-    out = subprocess.run([sys.executable, "-c", RUNNER.format(root=ROOT, path=str(so))],
-                         capture_output=True, text=True, timeout=300)
-    # a crash of the mutant counts as caught as well
-    assert out.returncode != 0 or "CAUGHT" in out.stdout, (name, out.stdout, out.stderr[-500:])
+    paths = []
+    for name, old, new in MUTANTS:
+        assert src.count(old) == 1, f"mutation site for {name} not unique/present"
+        (d / f"{name}.c").write_text(src.replace(old, new))
+        paths.append((name, str(d / f"lib_{name}.so")))
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        list(ex.map(lambda np_: oracle.build(str(d / f"{np_[0]}.c"), np_[1]), paths))
+    out = _run_pins(paths)
+    verdicts = {}
+    for line in out.stdout.splitlines():
+        if line.startswith("VERDICT "):
+            _, name, v = line.split(" ", 2)
+            verdicts[name] = v
+    return verdicts, dict(paths)
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(mutant_runs, name, old, new):
+    """Each planted mistake in the oracle fails at least one pin."""
+    verdicts, paths = mutant_runs
+    v = verdicts.get(name)
+    if v is None:
+        # the shared run ended before this mutant (one crashed): run it alone, where
+        # a crash of the mutant counts as caught as well
+        out = _run_pins([(name, paths[name])])
+        assert out.returncode != 0 or "CAUGHT" in out.stdout, (name, out.stdout,
+                                                                out.stderr[-500:])
+        return
+    assert v.startswith("CAUGHT"), (name, v)
