@@ -333,7 +333,8 @@ def qk_workload(g, steps, warmup, b_layout="kn"):
 def attention_workload(g, steps, warmup):
     """Attention continuation (tutorial page, section 2: Softmax(Q K^T) V) on the 96
     heads of sequence 512, dimension 64: S = Q K^T (fp32), P = softmax(S) row by row
-    (bf16), O = P V (fp32), each stage timed alone and the chain as a whole. The
+    (bf16), O = P V (fp32), each stage timed alone and the chain as a whole; then the
+    first two stages as the one kernel of gemm_attention_probs and that chain. The
     softmax is HBM-bound: its bytes are S read once and P written once."""
     import torch
     import synth
@@ -351,6 +352,9 @@ def attention_workload(g, steps, warmup):
                nb * (2 * Sq * D * 2 + Sq * Sq * 4), qk.config_name),
         "softmax": (lambda: g.softmax_rows(S, 1.0, "bf16", out=P), 0, nb * Sq * Sq * (4 + 2),
                     "softmax_rows"),
+        # QK^T and the softmax in one kernel: Q and K^T read, P written, S never stored
+        "probs": (lambda: g.attention_probs(Q, Kt, 1.0, "kn", "bf16", out=P), 2 * nb * Sq * Sq * D,
+                  nb * (2 * Sq * D * 2 + Sq * Sq * 2), "attention_probs"),
         "pv": (lambda: pv.run_batched(P, V, out=O), 2 * nb * Sq * Sq * D,
                nb * (Sq * Sq * 2 + Sq * D * 2 + Sq * D * 4), pv.config_name),
     }
@@ -369,6 +373,13 @@ def attention_workload(g, steps, warmup):
     med, mean, _ = time_calls(chain, steps, warmup)
     gms = time_graph(chain)
     out["chain"] = dict(median_ms=med, graph_ms=gms)
+
+    def chain_fused():
+        g.attention_probs(Q, Kt, 1.0, "kn", "bf16", out=P)
+        pv.run_batched(P, V, out=O)
+    med, mean, _ = time_calls(chain_fused, steps, warmup)
+    gms = time_graph(chain_fused)
+    out["chain_fused"] = dict(median_ms=med, graph_ms=gms)
     return dict(workload="attention_96x512x64", stages=out)
 
 

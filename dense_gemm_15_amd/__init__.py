@@ -69,6 +69,8 @@ SIGNATURES = {
     "gemm_plan_destroy": (None, [_VP]),
     "gemm_softmax_rows": (ctypes.c_int, [_VP, _I64, _I64, _I64, ctypes.c_float, _VP, _I64, _I32,
                                          _VP]),
+    "gemm_attention_probs": (ctypes.c_int, [_VP, _VP, _I64, _I64, _I64, _I64, _I32, _I32,
+                                            ctypes.c_float, _VP, _I32, _VP]),
     "gemm_last_error": (ctypes.c_int, []),
     "gemm_strerror": (ctypes.c_char_p, [ctypes.c_int]),
     "gemm_plan_describe": (ctypes.c_int, [_VP, ctypes.c_char_p, ctypes.c_size_t]),
@@ -249,4 +251,36 @@ def softmax_rows(S, scale: float = 1.0, out_dtype: str = "bf16", out=None, strea
                                _CODE[out_dtype], ctypes.c_void_p(s.cuda_stream))
     if rc != 0:
         raise GemmError(rc, "gemm_softmax_rows")
+    return out
+
+
+def attention_probs(Q, Kmat, scale: float = 1.0, k_layout: str = "kn", out_dtype: str = "bf16",
+                    out=None, stream=None):
+    """P = softmax(scale * Q K^T) per batch item in one kernel (gemm_attention_probs).
+    Q [batch, M, D] bf16/f16; Kmat [batch, D, N] (K^T, k_layout "kn") or [batch, N, D]
+    (the keys, "nk"), Q's type; P [batch, M, N] of out_dtype. All contiguous cuda."""
+    if Q.dim() != 3 or Kmat.dim() != 3 or k_layout not in ("kn", "nk"):
+        raise ValueError("Q and Kmat must be 3-d; k_layout 'kn' or 'nk'")
+    nb, M, D = Q.shape
+    N = Kmat.shape[2] if k_layout == "kn" else Kmat.shape[1]
+    want = (nb, D, N) if k_layout == "kn" else (nb, N, D)
+    if tuple(Kmat.shape) != want or Kmat.dtype != Q.dtype:
+        raise ValueError(f"Kmat must be {want} of Q's type")
+    for t in (Q, Kmat):
+        if t.device.type != "cuda" or not t.is_contiguous():
+            raise ValueError("Q and Kmat must be contiguous cuda tensors")
+    if Q.dtype not in (torch.bfloat16, torch.float16):
+        raise ValueError("Q must be bf16 or f16")
+    dt = "bf16" if Q.dtype == torch.bfloat16 else "f16"
+    if out is None:
+        out = torch.empty((nb, M, N), dtype=_TORCH[_CODE[out_dtype]], device=Q.device)
+    elif (tuple(out.shape) != (nb, M, N) or out.dtype != _TORCH[_CODE[out_dtype]]
+          or not out.is_contiguous() or out.device != Q.device):
+        raise ValueError("out must be a contiguous [batch, M, N] tensor of out_dtype")
+    s = stream if stream is not None else torch.cuda.current_stream()
+    rc = lib.gemm_attention_probs(_ptr(Q), _ptr(Kmat), nb, M, N, D, _CODE[dt],
+                                  0 if k_layout == "kn" else 1, float(scale), _ptr(out),
+                                  _CODE[out_dtype], ctypes.c_void_p(s.cuda_stream))
+    if rc != 0:
+        raise GemmError(rc, "gemm_attention_probs")
     return out

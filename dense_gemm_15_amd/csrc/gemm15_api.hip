@@ -25,6 +25,7 @@
 #include "kernels.hpp"
 #include "splitk.hpp"
 #include "softmax.hpp"
+#include "attention.hpp"
 
 using namespace g15;
 
@@ -712,6 +713,49 @@ int gemm_softmax_rows(const float* S, int64_t rows, int64_t cols, int64_t ld_s, 
   const int dt = p_dtype == GEMM_F32 ? DT_F32 : p_dtype == GEMM_BF16 ? DT_BF16 : DT_F16;
   const hipError_t err = launch_softmax_rows(S, rows, cols, ld_s, scale, P, ld_p, dt,
                                              static_cast<hipStream_t>(stream));
+  return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+int gemm_attention_probs(const void* Q, const void* Kmat, int64_t batch, int64_t M, int64_t N,
+                         int64_t D, int32_t dtype, int32_t k_layout, float scale, void* P,
+                         int32_t p_dtype, void* stream) {
+  const bool kn = k_layout == GEMM_B_KN;
+  if (batch < 1 || M < 1 || N < 1 || N > 512 || D < 8 || D > 64 || D % 8 != 0 ||
+      (kn && N % 8 != 0))
+    return GEMM_ERR_SHAPE;
+  if (!kn && k_layout != GEMM_B_NK) return GEMM_ERR_ARG;
+  if (!std::isfinite(scale)) return GEMM_ERR_ARG;
+  if (dtype != GEMM_BF16 && dtype != GEMM_F16) return GEMM_ERR_DTYPE;
+  if (p_dtype != GEMM_F32 && p_dtype != GEMM_F16 && p_dtype != GEMM_BF16) return GEMM_ERR_DTYPE;
+  if (!Q || !Kmat || !P) return GEMM_ERR_NULL;
+  if (!aligned_to(Q, 16) || !aligned_to(Kmat, 16) || !aligned_to(P, elem_bytes(p_dtype)))
+    return GEMM_ERR_ALIGN;
+  // 32-bit byte offsets inside one item; the workgroup loop counts tiles in int64
+  if (M * D * 2 >= (int64_t(1) << 31) || M * N * 4 >= (int64_t(1) << 31)) return GEMM_ERR_SHAPE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_NO_DEVICE;
+  gemm_device_desc desc;
+  if (device_desc(dev, &desc) != GEMM_OK) return GEMM_ERR_HIP;
+  LaunchArgs a{};
+  a.M = M;
+  a.N = N;
+  a.K = D;
+  a.batch = batch;
+  a.A = Q;
+  a.sA = M * D;
+  a.B = Kmat;
+  a.sB = N * D;
+  a.C = P;
+  a.sC = M * N;
+  a.epi.flags = 0;
+  a.epi.scale = scale;
+  a.epi.out_dtype = p_dtype == GEMM_F32 ? DT_F32 : p_dtype == GEMM_BF16 ? DT_BF16 : DT_F16;
+  a.split = (desc.cu_count + 7) / 8 * 8;  // one resident workgroup per CU (144 KB of LDS)
+  a.lda = D;
+  a.ldb = kn ? N : D;
+  a.ldc = N;
+  const hipError_t err = launch_attention_probs(a, dtype == GEMM_BF16, kn,
+                                                static_cast<hipStream_t>(stream));
   return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 

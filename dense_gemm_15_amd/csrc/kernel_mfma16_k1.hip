@@ -29,6 +29,7 @@
 // fetched into one L2; otherwise the tiles of the single product are strided over
 // the workgroups in the XCD-aware order of tile_of.
 #include "m16_common.hpp"
+#include "attention.hpp"
 
 namespace g15 {
 namespace {
@@ -37,7 +38,36 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 
-template <typename T, int BM, int BN, int WGM, int WGN, bool BROW>
+// Row reduction of 32 values per lane over the 32 lanes of each half-wave: after
+// the round with lane offset o a lane keeps the half of its values that lane bit o
+// selects and combines it with its partner's copy of that half (31 exchanges in
+// all). The result is the reduction of value index lane % 32, in a fixed order.
+// The per-lane choice of half is a bit select (v_bfi_b32) behind inline assembly:
+// written as a conditional, the compiler turns it into a lane-dependent index into
+// the 32 registers, i.e. a 32-way compare-and-select chain per value.
+__device__ __forceinline__ float bit_pick(uint32_t m, float a, float b) {  // m ? a : b
+  float r;
+  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
+  return r;
+}
+
+template <bool MAXOP>
+__device__ __forceinline__ float halve32(float (&x)[32], int lane) {
+#pragma unroll
+  for (int o = 16, c = 32; o >= 1; o >>= 1, c >>= 1) {
+    const uint32_t up = (lane & o) != 0 ? 0xffffffffu : 0u;
+#pragma unroll
+    for (int q = 0; q < c / 2; ++q) {
+      const float send = bit_pick(up, x[q], x[q + c / 2]);
+      const float keep = bit_pick(up, x[q + c / 2], x[q]);
+      const float recv = __shfl_xor(send, o);
+      x[q] = MAXOP ? fmaxf(keep, recv) : keep + recv;
+    }
+  }
+  return x[0];
+}
+
+template <typename T, int BM, int BN, int WGM, int WGN, bool BROW, bool SMAX>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a) {
   constexpr int BK = 64;
   constexpr int NW = WGM * WGN;
@@ -52,6 +82,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 block");
   static_assert(!BROW || (CPR_B >= 16 && 64 % CPR_B == 0), "row-major B: 128 or 256 columns");
   __shared__ u32x4 lds[2 * (A_STAGE + B_STAGE)];
+  // SMAX: every row of the tile lies in one tile (N <= BN) and in every wave (WGM = 1)
+  static_assert(!SMAX || (WGM == 1 && FM == 2 && FN == 2), "softmax tile: 64 rows, 64 columns a wave");
+  __shared__ float sm_red[SMAX ? NW * BM : 1];  // per-wave partial of each row
+  __shared__ __align__(16) float sm_row[SMAX ? BM : 1];  // row maximum, then 1 / row sum
   u32x4* const ringA = lds;
   u32x4* const ringB = lds + 2 * A_STAGE;
 
@@ -243,6 +277,76 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = mma<T>(fa[s][i], fb[s][j], acc[i][j]);
 
+    if constexpr (SMAX) {
+      // P = softmax(scale S) along each row: scores of columns past N are -inf; the
+      // row maximum and the row sum of exp(s - max) go through the halving exchange
+      // (each lane ends with one row of its wave's 64 columns), then across the
+      // waves in LDS; exp is the hardware exp2 of the argument times log2(e), and P
+      // is exp(s - max) times the reciprocal of the sum (as in kernel_softmax.hip).
+      const float scl = a.epi.scale;
+      const int h = lane >> 5, q = lane & 31;
+      const int own = 32 * (q >> 4) + 8 * ((q & 15) >> 2) + 4 * h + (q & 3);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const bool cin = n0 + wn * WTN + 32 * j + lrow < N;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = cin ? acc[i][j][r] * scl : -INFINITY;
+        }
+      float x[32];
+      auto row_values = [&](float (&rv)[FM][16]) {  // per-row LDS value of this lane's rows
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(sm_row + 32 * i + 8 * r4 + 4 * h);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) rv[i][4 * r4 + t] = v[t];
+          }
+      };
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[16 * i + r] = fmaxf(acc[i][0][r], acc[i][1][r]);
+      sm_red[wave * BM + own] = halve32<true>(x, lane);
+      lds_barrier();
+      if (wave == 0) {
+        float m = sm_red[own];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) m = fmaxf(m, sm_red[w * BM + own]);
+        sm_row[own] = m;
+      }
+      lds_barrier();
+      float rv[FM][16];
+      row_values(rv);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] = __expf(acc[i][j][r] - rv[i][r]);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[16 * i + r] = acc[i][0][r] + acc[i][1][r];
+      sm_red[wave * BM + own] = halve32<false>(x, lane);
+      lds_barrier();  // every wave has read the row maxima
+      if (wave == 0) {
+        float sum = sm_red[own];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) sum += sm_red[w * BM + own];
+        sm_row[own] = 1.f / sum;
+      }
+      lds_barrier();
+      row_values(rv);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[i][j][r] *= rv[i][r];
+    }
     store_tile<FM, FN, WTM, WTN, NW, static_cast<int>(sizeof(lds))>(
         out, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, wave, lane, z);
     have = next;
@@ -253,14 +357,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
   }
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, bool BROW>
+template <typename T, int BM, int BN, int WGM, int WGN, bool BROW, bool SMAX = false>
 hipError_t launch_m16s(const LaunchArgs& a, hipStream_t s) {
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.batch;
   // a.split: the workgroups the device keeps resident (set at plan time); a multiple
   // of 8 so each XCD gets the same number
   int64_t g = a.split > 1 ? a.split : 512;
   if (tiles < g) g = (tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_m16s_kernel<T, BM, BN, WGM, WGN, BROW>), dim3(static_cast<unsigned>(g)),
+  hipLaunchKernelGGL((gemm_m16s_kernel<T, BM, BN, WGM, WGN, BROW, SMAX>), dim3(static_cast<unsigned>(g)),
                      dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }
@@ -280,6 +384,15 @@ const KernelEntry kM16S[] = {
 };
 
 }  // namespace
+
+hipError_t launch_attention_probs(const LaunchArgs& a, bool bf16, bool b_rowmajor, hipStream_t s) {
+  if (a.K > 64 || a.N > 512 || a.epi.flags != 0) return hipErrorInvalidValue;
+  if (bf16)
+    return b_rowmajor ? launch_m16s<bf16_t, 64, 512, 1, 8, true, true>(a, s)
+                      : launch_m16s<bf16_t, 64, 512, 1, 8, false, true>(a, s);
+  return b_rowmajor ? launch_m16s<f16_t, 64, 512, 1, 8, true, true>(a, s)
+                    : launch_m16s<f16_t, 64, 512, 1, 8, false, true>(a, s);
+}
 
 int mfma16_k1_entries(const KernelEntry** out) {
   *out = kM16S;

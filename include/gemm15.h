@@ -183,6 +183,37 @@ int gemm_run_strided_batched(const gemm_plan* plan, int64_t batch, const void* A
 int gemm_softmax_rows(const float* S, int64_t rows, int64_t cols, int64_t ld_s, float scale,
                       void* P, int64_t ld_p, int32_t p_dtype, void* stream);
 
+/*
+ * The attention probabilities in one kernel: per batch item b,
+ *
+ *     P_b = softmax_rows(scale * Q_b K_b^T)      (as gemm_softmax_rows)
+ *
+ * i.e. the first product of attention and the softmax after it (tutorial page,
+ * section 2) with the scores kept in FP32 registers: each workgroup holds whole
+ * rows (64 query rows x every key), takes their maximum and the FP32 sum of
+ * exp(s - max) there (DeepGEMM page, section 3.4), and writes P once, so the FP32
+ * score matrix is never written to or read back from memory.
+ *
+ * Q      device, batch x M x D row-major of dtype (GEMM_BF16 or GEMM_F16), items
+ *        contiguous (item b at Q + b*M*D)
+ * Kmat   device, per item the keys: with k_layout GEMM_B_KN their transpose K^T,
+ *        D x N row-major; with GEMM_B_NK the keys themselves, N x D row-major
+ *        (a linear layer's [out x in] weight); item b at Kmat + b*N*D
+ * P      device, batch x M x N row-major of p_dtype (GEMM_F32, GEMM_F16 or GEMM_BF16),
+ *        computed in FP32 and rounded once (nearest, ties to even); must not
+ *        overlap Q or Kmat
+ * Limits: 1 <= N <= 512 keys and 8 <= D <= 64 (D % 8 == 0); with GEMM_B_KN also
+ * N % 8 == 0; Q and Kmat 16-byte aligned, P aligned to its element; one item's
+ * Q and P each under 2 GiB. scale finite.
+ * Enqueues one kernel on `stream` (NULL = default) and returns GEMM_OK, or
+ * GEMM_ERR_SHAPE (batch, M < 1, N or D out of range), GEMM_ERR_ARG (k_layout,
+ * scale), GEMM_ERR_DTYPE, GEMM_ERR_NULL, GEMM_ERR_ALIGN, GEMM_ERR_NO_DEVICE,
+ * GEMM_ERR_HIP. Q and Kmat must hold finite values.
+ */
+int gemm_attention_probs(const void* Q, const void* Kmat, int64_t batch, int64_t M, int64_t N,
+                         int64_t D, int32_t dtype, int32_t k_layout, float scale, void* P,
+                         int32_t p_dtype, void* stream);
+
 /* Release a plan and its workspace. NULL is ignored. The caller must make sure no
  * enqueued run of the plan is still pending on a stream. */
 void gemm_plan_destroy(gemm_plan* plan);
