@@ -38,32 +38,56 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 
-// Row reduction of 32 values per lane over the 32 lanes of each half-wave: after
-// the round with lane offset o a lane keeps the half of its values that lane bit o
-// selects and combines it with its partner's copy of that half (31 exchanges in
-// all). The result is the reduction of value index lane % 32, in a fixed order.
-// The per-lane choice of half is a bit select (v_bfi_b32) behind inline assembly:
-// written as a conditional, the compiler turns it into a lane-dependent index into
-// the 32 registers, i.e. a 32-way compare-and-select chain per value.
-__device__ __forceinline__ float bit_pick(uint32_t m, float a, float b) {  // m ? a : b
+// Row reduction of 32 values per lane over the 32 lanes of each half-wave, by
+// halving: in the round for lane bit b a lane keeps the half of its values that
+// bit b selects and combines it with its partner's copy of that half; the partner
+// differs in bit b and agrees in the bits of the earlier rounds, so it holds the
+// same values. Rounds: bit 4 with v_permlane16_swap (lanes 16 apart), then bit 3,
+// 2, 1, 0 with DPP moves from lane l ^ 15 (row_mirror), l ^ 7 (row_half_mirror),
+// l ^ 2 and l ^ 1 (quad permutations); 31 exchanges, no LDS. The result is the
+// reduction of value index lane % 32, in a fixed order.
+template <bool MAXOP>
+__device__ __forceinline__ float comb(float a, float b) {
+  return MAXOP ? fmaxf(a, b) : a + b;
+}
+
+// m ? a : b as a bit select (v_bfi_b32) behind inline assembly: written as a
+// conditional, the compiler turns the choice into a lane-dependent index into the
+// 32 registers, i.e. a 32-way compare-and-select chain per value.
+__device__ __forceinline__ float bit_pick(uint32_t m, float a, float b) {
   float r;
   asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
   return r;
 }
 
+template <bool MAXOP, int H, int CTRL>
+__device__ __forceinline__ void halve_dpp(float (&x)[32], int lane) {
+  const uint32_t up = (lane & H) != 0 ? 0xffffffffu : 0u;
+#pragma unroll
+  for (int q = 0; q < H; ++q) {
+    const float send = bit_pick(up, x[q], x[q + H]);
+    const float keep = bit_pick(up, x[q + H], x[q]);
+    const float recv =
+        __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(send), CTRL, 0xf, 0xf, false));
+    x[q] = comb<MAXOP>(keep, recv);
+  }
+}
+
 template <bool MAXOP>
 __device__ __forceinline__ float halve32(float (&x)[32], int lane) {
+  // v_permlane16_swap exchanges the odd 16-lane rows of its first operand with the
+  // even rows of its second: from (x[q], x[q + 16]) a lane of an even row gets its
+  // own and its partner's x[q], a lane of an odd row both copies of x[q + 16]
 #pragma unroll
-  for (int o = 16, c = 32; o >= 1; o >>= 1, c >>= 1) {
-    const uint32_t up = (lane & o) != 0 ? 0xffffffffu : 0u;
-#pragma unroll
-    for (int q = 0; q < c / 2; ++q) {
-      const float send = bit_pick(up, x[q], x[q + c / 2]);
-      const float keep = bit_pick(up, x[q + c / 2], x[q]);
-      const float recv = __shfl_xor(send, o);
-      x[q] = MAXOP ? fmaxf(keep, recv) : keep + recv;
-    }
+  for (int q = 0; q < 16; ++q) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[q]), __float_as_uint(x[q + 16]),
+                                                    false, false);
+    x[q] = comb<MAXOP>(__uint_as_float(r[0]), __uint_as_float(r[1]));
   }
+  halve_dpp<MAXOP, 8, 0x140>(x, lane);  // row_mirror
+  halve_dpp<MAXOP, 4, 0x141>(x, lane);  // row_half_mirror
+  halve_dpp<MAXOP, 2, 0x4E>(x, lane);   // quad_perm 2 3 0 1
+  halve_dpp<MAXOP, 1, 0xB1>(x, lane);   // quad_perm 1 0 3 2
   return x[0];
 }
 
@@ -84,8 +108,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
   __shared__ u32x4 lds[2 * (A_STAGE + B_STAGE)];
   // SMAX: every row of the tile lies in one tile (N <= BN) and in every wave (WGM = 1)
   static_assert(!SMAX || (WGM == 1 && FM == 2 && FN == 2), "softmax tile: 64 rows, 64 columns a wave");
-  __shared__ float sm_red[SMAX ? NW * BM : 1];  // per-wave partial of each row
-  __shared__ __align__(16) float sm_row[SMAX ? BM : 1];  // row maximum, then 1 / row sum
+  __shared__ float2 sm_part[SMAX ? NW * BM : 1];         // per wave and row: (max, sum)
+  __shared__ __align__(16) float sm_w[SMAX ? NW * BM : 1];  // per wave and row, wave-private
   u32x4* const ringA = lds;
   u32x4* const ringB = lds + 2 * A_STAGE;
 
@@ -278,11 +302,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
         for (int j = 0; j < FN; ++j) acc[i][j] = mma<T>(fa[s][i], fb[s][j], acc[i][j]);
 
     if constexpr (SMAX) {
-      // P = softmax(scale S) along each row: scores of columns past N are -inf; the
-      // row maximum and the row sum of exp(s - max) go through the halving exchange
-      // (each lane ends with one row of its wave's 64 columns), then across the
-      // waves in LDS; exp is the hardware exp2 of the argument times log2(e), and P
-      // is exp(s - max) times the reciprocal of the sum (as in kernel_softmax.hip).
+      // P = softmax(scale S) along each row, columns past N at -inf. Each wave
+      // reduces its own 64 columns: the row maximum m_w (halving exchange, so lane
+      // `own` holds row own), then e = exp(s - m_w) and the sum s_w of e. After one
+      // barrier the lane owning a row merges the 8 waves' (m_w, s_w) as the online
+      // softmax does: M = max m_w, S = sum s_w exp(m_w - M), and scales its wave's
+      // e by exp(m_w - M) / S. Per-row values reach the other lanes of the wave
+      // through the wave's own LDS row (a wave's LDS accesses complete in order).
+      // exp is the hardware exp2 of the argument times log2(e).
       const float scl = a.epi.scale;
       const int h = lane >> 5, q = lane & 31;
       const int own = 32 * (q >> 4) + 8 * ((q & 15) >> 2) + 4 * h + (q & 3);
@@ -294,32 +321,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] = cin ? acc[i][j][r] * scl : -INFINITY;
         }
-      float x[32];
-      auto row_values = [&](float (&rv)[FM][16]) {  // per-row LDS value of this lane's rows
+      float* const wrow = sm_w + wave * BM;
+      float rv[FM][16];
+      auto row_values = [&]() {  // wrow at the rows of this lane's registers
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(sm_row + 32 * i + 8 * r4 + 4 * h);
+            const f32x4 v = *reinterpret_cast<const f32x4*>(wrow + 32 * i + 8 * r4 + 4 * h);
 #pragma unroll
             for (int t = 0; t < 4; ++t) rv[i][4 * r4 + t] = v[t];
           }
       };
+      float x[32];
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[16 * i + r] = fmaxf(acc[i][0][r], acc[i][1][r]);
-      sm_red[wave * BM + own] = halve32<true>(x, lane);
-      lds_barrier();
-      if (wave == 0) {
-        float m = sm_red[own];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) m = fmaxf(m, sm_red[w * BM + own]);
-        sm_row[own] = m;
-      }
-      lds_barrier();
-      float rv[FM][16];
-      row_values(rv);
+      const float mw = halve32<true>(x, lane);
+      // a wave whose columns are all past N has m_w = -inf: subtract 0 instead (e = 0)
+      wrow[own] = mw == -INFINITY ? 0.f : mw;
+      row_values();
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -330,16 +352,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) x[16 * i + r] = acc[i][0][r] + acc[i][1][r];
-      sm_red[wave * BM + own] = halve32<false>(x, lane);
-      lds_barrier();  // every wave has read the row maxima
-      if (wave == 0) {
-        float sum = sm_red[own];
-#pragma unroll
-        for (int w = 1; w < NW; ++w) sum += sm_red[w * BM + own];
-        sm_row[own] = 1.f / sum;
-      }
+      const float sw = halve32<false>(x, lane);
+      sm_part[wave * BM + own] = float2{mw, sw};
       lds_barrier();
-      row_values(rv);
+      float2 pw[NW];
+#pragma unroll
+      for (int w = 0; w < NW; ++w) pw[w] = sm_part[w * BM + own];
+      float mx = pw[0].x;
+#pragma unroll
+      for (int w = 1; w < NW; ++w) mx = fmaxf(mx, pw[w].x);
+      float sum = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) sum += pw[w].y * __expf(pw[w].x - mx);
+      wrow[own] = __expf(mw - mx) * (1.f / sum);
+      row_values();
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
