@@ -249,6 +249,58 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
   out.c_vec = 0;  // 16-bit C straight from the registers: LDS holds the next tile's operands
 
   f32x16 acc[FM][FN];
+  // SMAX with a 16-bit P of even N: a tile's P leaves one tile later, right after
+  // the next tile's loads are issued, so the loop-top wait for every load and store
+  // in flight finds the stores a tile old instead of just issued. Registers 2p and
+  // 2p+1 of a block are rows R and R+1 of one column and lanes l, l^1 hold
+  // neighbouring columns: after one exchange the even lane holds columns (c, c+1)
+  // of row R and the odd lane (c-1, c) of row R+1, one 4-byte store each.
+  const bool defer = SMAX && a.epi.out_dtype != DT_F32 && (N & 1) == 0 && (a.ldc & 1) == 0;
+  uint32_t pk[SMAX ? FM : 1][SMAX ? FN : 1][8];
+  bool pend = false;
+  int64_t zp = 0;
+  int m0p = 0, n0p = 0;
+  const bool odd_lane = (lane & 1) != 0;
+  const uint32_t odd_mask = odd_lane ? 0xffffffffu : 0u;
+  auto pack = [&]() {
+    const bool bf = a.epi.out_dtype == DT_BF16;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const float e0 = acc[i][j][2 * p], e1 = acc[i][j][2 * p + 1];
+          // DPP quad_perm [1, 0, 3, 2]: the neighbour's row R (odd lane) or R+1 (even)
+          const float recv = __uint_as_float(__builtin_amdgcn_mov_dpp(
+              __float_as_uint(bit_pick(odd_mask, e0, e1)), 0xB1, 0xf, 0xf, false));
+          const float lo = bit_pick(odd_mask, recv, e0);
+          const float hi = bit_pick(odd_mask, e1, recv);
+          pk[i][j][p] = bf ? (static_cast<uint32_t>(narrow_bf16(lo)) |
+                              (static_cast<uint32_t>(narrow_bf16(hi)) << 16))
+                           : (static_cast<uint32_t>(narrow_f16(lo)) |
+                              (static_cast<uint32_t>(narrow_f16(hi)) << 16));
+        }
+  };
+  auto put = [&](int64_t zz, int mm, int nn) {
+    const int LDC = static_cast<int>(a.ldc);
+    char* Cz = static_cast<char*>(a.C) + zz * a.sC * 2;
+    const auto rC = rsrc(Cz, static_cast<uint32_t>(static_cast<int64_t>(M) * LDC * 2));
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int ce = (nn + wn * WTN + 32 * j + lrow) & ~1;
+        const int rb = mm + wm * WTM + 32 * i + 4 * lhalf + (odd_lane ? 1 : 0);
+#pragma unroll
+        for (int p = 0; p < 8; ++p) {
+          const int row = rb + 8 * (p >> 1) + 2 * (p & 1);
+          const uint32_t off = (row < M && ce < N) ? static_cast<uint32_t>(row * LDC + ce) * 2u : OOB;
+          __builtin_amdgcn_raw_buffer_store_b32(pk[i][j][p], rC, off, 0, 0);
+        }
+      }
+  };
+
   int64_t z;
   int m0, n0;
   bool have = tile(0, z, m0, n0);
@@ -286,6 +338,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
     }
     __builtin_amdgcn_sched_barrier(0);
     if (next) issue(zn, m0n, n0n, slot ^ 1);
+    if constexpr (SMAX) {
+      if (pend) put(zp, m0p, n0p);  // the previous tile's P
+      pend = false;
+    }
     __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
@@ -373,13 +429,24 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] *= rv[i][r];
     }
-    store_tile<FM, FN, WTM, WTN, NW, static_cast<int>(sizeof(lds))>(
-        out, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, wave, lane, z);
+    if (SMAX && defer) {
+      pack();
+      pend = true;
+      zp = z;
+      m0p = m0;
+      n0p = n0;
+    } else {
+      store_tile<FM, FN, WTM, WTN, NW, static_cast<int>(sizeof(lds))>(
+          out, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, wave, lane, z);
+    }
     have = next;
     z = zn;
     m0 = m0n;
     n0 = n0n;
     slot ^= 1;
+  }
+  if constexpr (SMAX) {
+    if (pend) put(zp, m0p, n0p);
   }
 }
 
