@@ -255,8 +255,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
   // 2p+1 of a block are rows R and R+1 of one column and lanes l, l^1 hold
   // neighbouring columns: after one exchange the even lane holds columns (c, c+1)
   // of row R and the odd lane (c-1, c) of row R+1, one 4-byte store each.
-  const bool defer = SMAX && a.epi.out_dtype != DT_F32 && (N & 1) == 0 && (a.ldc & 1) == 0;
+  // Without the softmax the same delay applies to fp32 C with no epilogue on the
+  // 8-wave tiles (their registers have room for the held tile).
+  constexpr bool HOLD = !SMAX && NW == 8;
+  const bool defer = SMAX ? (a.epi.out_dtype != DT_F32 && (N & 1) == 0 && (a.ldc & 1) == 0)
+                          : (HOLD && a.epi.out_dtype == DT_F32 && a.epi.flags == 0);
   uint32_t pk[SMAX ? FM : 1][SMAX ? FN : 1][8];
+  f32x16 held[HOLD ? FM : 1][HOLD ? FN : 1];
   bool pend = false;
   int64_t zp = 0;
   int m0p = 0, n0p = 0;
@@ -301,6 +306,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
       }
   };
 
+  auto put32 = [&](int64_t zz, int mm, int nn) {
+    const int LDC = static_cast<int>(a.ldc);
+    char* Cz = static_cast<char*>(a.C) + zz * a.sC * 4;
+    const auto rC = rsrc(Cz, static_cast<uint32_t>(static_cast<int64_t>(M) * LDC * 4));
+#pragma unroll
+    for (int i = 0; i < (HOLD ? FM : 0); ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int cl = nn + wn * WTN + 32 * j + lrow;
+        const int rb = mm + wm * WTM + 32 * i + 4 * lhalf;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = rb + 8 * (r >> 2) + (r & 3);
+          const uint32_t off = (row < M && cl < N) ? static_cast<uint32_t>(row * LDC + cl) * 4u : OOB;
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(held[i][j][r]), rC, off, 0, 0);
+        }
+      }
+  };
+
   int64_t z;
   int m0, n0;
   bool have = tile(0, z, m0, n0);
@@ -338,10 +362,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
     }
     __builtin_amdgcn_sched_barrier(0);
     if (next) issue(zn, m0n, n0n, slot ^ 1);
-    if constexpr (SMAX) {
-      if (pend) put(zp, m0p, n0p);  // the previous tile's P
-      pend = false;
+    if (pend) {  // the previous tile's C
+      if constexpr (SMAX) put(zp, m0p, n0p);
+      if constexpr (HOLD) put32(zp, m0p, n0p);
     }
+    pend = false;
     __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
@@ -429,8 +454,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc[i][j][r] *= rv[i][r];
     }
-    if (SMAX && defer) {
-      pack();
+    if (defer) {
+      if constexpr (SMAX) pack();
+      if constexpr (HOLD) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) held[i][j] = acc[i][j];
+      }
       pend = true;
       zp = z;
       m0p = m0;
@@ -445,8 +476,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
     n0 = n0n;
     slot ^= 1;
   }
-  if constexpr (SMAX) {
-    if (pend) put(zp, m0p, n0p);
+  if (pend) {
+    if constexpr (SMAX) put(zp, m0p, n0p);
+    if constexpr (HOLD) put32(zp, m0p, n0p);
   }
 }
 
