@@ -67,6 +67,34 @@ def test_layout_plan_errors_without_device():
     assert g.lib.gemm_last_error() == -2  # GEMM_ERR_DTYPE: no transposed-B fp32 kernel
 
 
+def test_attention_probs_argument_errors_without_device():
+    """gemm_attention_probs checks shapes, layout, scale, types, pointers and
+    alignment before it looks for a device (the pointers here are never touched)."""
+    q, k, p = (ctypes.c_void_p(0x10000 * (i + 1)) for i in range(3))
+    call = g.lib.gemm_attention_probs
+    assert call(q, k, 1, 64, 513, 64, g.BF16, 0, 1.0, p, g.F32, None) == -1   # N > 512
+    assert call(q, k, 1, 64, 0, 64, g.BF16, 0, 1.0, p, g.F32, None) == -1
+    assert call(q, k, 1, 0, 64, 64, g.BF16, 0, 1.0, p, g.F32, None) == -1
+    assert call(q, k, 0, 64, 64, 64, g.BF16, 0, 1.0, p, g.F32, None) == -1
+    assert call(q, k, 1, 64, 64, 4, g.BF16, 0, 1.0, p, g.F32, None) == -1     # D < 8
+    assert call(q, k, 1, 64, 64, 72, g.BF16, 0, 1.0, p, g.F32, None) == -1    # D > 64
+    assert call(q, k, 1, 64, 64, 20, g.BF16, 1, 1.0, p, g.F32, None) == -1    # D % 8
+    assert call(q, k, 1, 64, 20, 64, g.BF16, 0, 1.0, p, g.F32, None) == -1    # K^T: N % 8
+    assert call(q, k, 1, 1 << 26, 64, 64, g.BF16, 0, 1.0, p, g.F32, None) == -1  # > 2 GiB
+    assert call(q, k, 1, 64, 64, 64, g.BF16, 3, 1.0, p, g.F32, None) == -10   # layout
+    assert call(q, k, 1, 64, 64, 64, g.BF16, 0, float("inf"), p, g.F32, None) == -10
+    assert call(q, k, 1, 64, 64, 64, g.F32, 0, 1.0, p, g.F32, None) == -2
+    assert call(q, k, 1, 64, 64, 64, g.BF16, 0, 1.0, p, 5, None) == -2
+    assert call(q, None, 1, 64, 64, 64, g.BF16, 0, 1.0, p, g.F32, None) == -3
+    assert call(q, k, 1, 64, 64, 64, g.BF16, 0, 1.0, None, g.F32, None) == -3
+    q8 = ctypes.c_void_p(0x10008)
+    assert call(q8, k, 1, 64, 64, 64, g.BF16, 0, 1.0, p, g.F32, None) == -4
+    p1 = ctypes.c_void_p(0x30001)
+    assert call(q, k, 1, 64, 64, 64, g.BF16, 0, 1.0, p1, g.BF16, None) == -4
+    if not torch.cuda.is_available():  # every argument valid: the device is missing
+        assert call(q, k, 1, 64, 64, 64, g.BF16, 1, 1.0, p, g.F32, None) == -5
+
+
 def test_null_plan_rejected():
     assert g.lib.gemm_run(None, None, None, None, None, None, None) == -7
     assert g.lib.gemm_plan_describe(None, None, 0) == -7

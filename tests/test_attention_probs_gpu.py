@@ -148,3 +148,34 @@ def test_attention_probs_errors(g):
     q8 = ctypes.c_void_p(Q.data_ptr() + 8)
     assert call(q8, k, 2, 64, 64, 64, g.BF16, 0, 1.0, p, g.F32, s) == -4
     torch.cuda.synchronize()
+
+
+def test_attention_probs_graph_replay(g):
+    """The fused kernel captured in a HIP graph and replayed with new Q between
+    replays and eager work in between: every replay equals the eager result bit for
+    bit."""
+    nb, M, N, D = 9, 130, 200, 64
+    dev = torch.device("cuda")
+    Qs = [synth.normal(2200 + i, (nb, M, D), 1.0, "bf16").to(dev) for i in range(2)]
+    Kmat = synth.normal(2202, (nb, N, D), 1.0, "bf16").to(dev)
+    eager = [g.attention_probs(Q, Kmat, 0.125, "nk", "bf16").clone() for Q in Qs]
+    torch.cuda.synchronize()
+    Q0 = Qs[0].clone()
+    out = torch.empty((nb, M, N), dtype=torch.bfloat16, device=dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        g.attention_probs(Q0, Kmat, 0.125, "nk", "bf16", out=out)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        g.attention_probs(Q0, Kmat, 0.125, "nk", "bf16", out=out)
+    junk = torch.randn(1 << 20, device=dev)
+    for rep, i in enumerate((0, 1, 1, 0)):
+        Q0.copy_(Qs[i])
+        out.fill_(float("nan"))
+        graph.replay()
+        junk.mul_(1.0001)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager[i].view(torch.int16)), (rep, i)
