@@ -750,7 +750,7 @@ int gemm_attention_probs(const void* Q, const void* Kmat, int64_t batch, int64_t
   a.epi.flags = 0;
   a.epi.scale = scale;
   a.epi.out_dtype = p_dtype == GEMM_F32 ? DT_F32 : p_dtype == GEMM_BF16 ? DT_BF16 : DT_F16;
-  a.split = (desc.cu_count + 7) / 8 * 8;  // one resident workgroup per CU (144 KB of LDS)
+  a.split = attention_workgroups(desc.cu_count);
   a.lda = D;
   a.ldb = kn ? N : D;
   a.ldc = N;

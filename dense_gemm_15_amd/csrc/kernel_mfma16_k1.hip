@@ -29,7 +29,6 @@
 // fetched into one L2; otherwise the tiles of the single product are strided over
 // the workgroups in the XCD-aware order of tile_of.
 #include "m16_common.hpp"
-#include "attention.hpp"
 
 namespace g15 {
 namespace {
@@ -38,60 +37,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
 
-// Row reduction of 32 values per lane over the 32 lanes of each half-wave, by
-// halving: in the round for lane bit b a lane keeps the half of its values that
-// bit b selects and combines it with its partner's copy of that half; the partner
-// differs in bit b and agrees in the bits of the earlier rounds, so it holds the
-// same values. Rounds: bit 4 with v_permlane16_swap (lanes 16 apart), then bit 3,
-// 2, 1, 0 with DPP moves from lane l ^ 15 (row_mirror), l ^ 7 (row_half_mirror),
-// l ^ 2 and l ^ 1 (quad permutations); 31 exchanges, no LDS. The result is the
-// reduction of value index lane % 32, in a fixed order.
-template <bool MAXOP>
-__device__ __forceinline__ float comb(float a, float b) {
-  return MAXOP ? fmaxf(a, b) : a + b;
-}
-
-// m ? a : b as a bit select (v_bfi_b32) behind inline assembly: written as a
-// conditional, the compiler turns the choice into a lane-dependent index into the
-// 32 registers, i.e. a 32-way compare-and-select chain per value.
-__device__ __forceinline__ float bit_pick(uint32_t m, float a, float b) {
-  float r;
-  asm("v_bfi_b32 %0, %1, %2, %3" : "=v"(r) : "v"(m), "v"(a), "v"(b));
-  return r;
-}
-
-template <bool MAXOP, int H, int CTRL>
-__device__ __forceinline__ void halve_dpp(float (&x)[32], int lane) {
-  const uint32_t up = (lane & H) != 0 ? 0xffffffffu : 0u;
-#pragma unroll
-  for (int q = 0; q < H; ++q) {
-    const float send = bit_pick(up, x[q], x[q + H]);
-    const float keep = bit_pick(up, x[q + H], x[q]);
-    const float recv =
-        __uint_as_float(__builtin_amdgcn_mov_dpp(__float_as_uint(send), CTRL, 0xf, 0xf, false));
-    x[q] = comb<MAXOP>(keep, recv);
-  }
-}
-
-template <bool MAXOP>
-__device__ __forceinline__ float halve32(float (&x)[32], int lane) {
-  // v_permlane16_swap exchanges the odd 16-lane rows of its first operand with the
-  // even rows of its second: from (x[q], x[q + 16]) a lane of an even row gets its
-  // own and its partner's x[q], a lane of an odd row both copies of x[q + 16]
-#pragma unroll
-  for (int q = 0; q < 16; ++q) {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[q]), __float_as_uint(x[q + 16]),
-                                                    false, false);
-    x[q] = comb<MAXOP>(__uint_as_float(r[0]), __uint_as_float(r[1]));
-  }
-  halve_dpp<MAXOP, 8, 0x140>(x, lane);  // row_mirror
-  halve_dpp<MAXOP, 4, 0x141>(x, lane);  // row_half_mirror
-  halve_dpp<MAXOP, 2, 0x4E>(x, lane);   // quad_perm 2 3 0 1
-  halve_dpp<MAXOP, 1, 0xB1>(x, lane);   // quad_perm 1 0 3 2
-  return x[0];
-}
-
-template <typename T, int BM, int BN, int WGM, int WGN, bool BROW, bool SMAX>
+template <typename T, int BM, int BN, int WGM, int WGN, bool BROW>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a) {
   constexpr int BK = 64;
   constexpr int NW = WGM * WGN;
@@ -106,10 +52,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
   static_assert(FM >= 1 && FN >= 1, "wave tile must hold a 32x32 block");
   static_assert(!BROW || (CPR_B >= 16 && 64 % CPR_B == 0), "row-major B: 128 or 256 columns");
   __shared__ u32x4 lds[2 * (A_STAGE + B_STAGE)];
-  // SMAX: every row of the tile lies in one tile (N <= BN) and in every wave (WGM = 1)
-  static_assert(!SMAX || (WGM == 1 && FM == 2 && FN == 2), "softmax tile: 64 rows, 64 columns a wave");
-  __shared__ float2 sm_part[SMAX ? NW * BM : 1];         // per wave and row: (max, sum)
-  __shared__ __align__(16) float sm_w[SMAX ? NW * BM : 1];  // per wave and row, wave-private
   u32x4* const ringA = lds;
   u32x4* const ringB = lds + 2 * A_STAGE;
 
@@ -249,63 +191,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
   out.c_vec = 0;  // 16-bit C straight from the registers: LDS holds the next tile's operands
 
   f32x16 acc[FM][FN];
-  // SMAX with a 16-bit P of even N: a tile's P leaves one tile later, right after
-  // the next tile's loads are issued, so the loop-top wait for every load and store
-  // in flight finds the stores a tile old instead of just issued. Registers 2p and
-  // 2p+1 of a block are rows R and R+1 of one column and lanes l, l^1 hold
-  // neighbouring columns: after one exchange the even lane holds columns (c, c+1)
-  // of row R and the odd lane (c-1, c) of row R+1, one 4-byte store each.
-  // Without the softmax the same delay applies to fp32 C with no epilogue on the
-  // 8-wave tiles (their registers have room for the held tile).
-  constexpr bool HOLD = !SMAX && NW == 8;
-  const bool defer = SMAX ? (a.epi.out_dtype != DT_F32 && (N & 1) == 0 && (a.ldc & 1) == 0)
-                          : (HOLD && a.epi.out_dtype == DT_F32 && a.epi.flags == 0);
-  uint32_t pk[SMAX ? FM : 1][SMAX ? FN : 1][8];
+  // fp32 C without epilogue on the 8-wave tiles (their registers have room for the
+  // held tile): a tile's C leaves one tile later, right after the next tile's loads
+  // are issued, so the loop-top wait for every load and store in flight finds the
+  // stores a tile old instead of just issued.
+  constexpr bool HOLD = NW == 8;
+  const bool defer = HOLD && a.epi.out_dtype == DT_F32 && a.epi.flags == 0;
   f32x16 held[HOLD ? FM : 1][HOLD ? FN : 1];
   bool pend = false;
   int64_t zp = 0;
   int m0p = 0, n0p = 0;
-  const bool odd_lane = (lane & 1) != 0;
-  const uint32_t odd_mask = odd_lane ? 0xffffffffu : 0u;
-  auto pack = [&]() {
-    const bool bf = a.epi.out_dtype == DT_BF16;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          const float e0 = acc[i][j][2 * p], e1 = acc[i][j][2 * p + 1];
-          // DPP quad_perm [1, 0, 3, 2]: the neighbour's row R (odd lane) or R+1 (even)
-          const float recv = __uint_as_float(__builtin_amdgcn_mov_dpp(
-              __float_as_uint(bit_pick(odd_mask, e0, e1)), 0xB1, 0xf, 0xf, false));
-          const float lo = bit_pick(odd_mask, recv, e0);
-          const float hi = bit_pick(odd_mask, e1, recv);
-          pk[i][j][p] = bf ? (static_cast<uint32_t>(narrow_bf16(lo)) |
-                              (static_cast<uint32_t>(narrow_bf16(hi)) << 16))
-                           : (static_cast<uint32_t>(narrow_f16(lo)) |
-                              (static_cast<uint32_t>(narrow_f16(hi)) << 16));
-        }
-  };
-  auto put = [&](int64_t zz, int mm, int nn) {
-    const int LDC = static_cast<int>(a.ldc);
-    char* Cz = static_cast<char*>(a.C) + zz * a.sC * 2;
-    const auto rC = rsrc(Cz, static_cast<uint32_t>(static_cast<int64_t>(M) * LDC * 2));
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int ce = (nn + wn * WTN + 32 * j + lrow) & ~1;
-        const int rb = mm + wm * WTM + 32 * i + 4 * lhalf + (odd_lane ? 1 : 0);
-#pragma unroll
-        for (int p = 0; p < 8; ++p) {
-          const int row = rb + 8 * (p >> 1) + 2 * (p & 1);
-          const uint32_t off = (row < M && ce < N) ? static_cast<uint32_t>(row * LDC + ce) * 2u : OOB;
-          __builtin_amdgcn_raw_buffer_store_b32(pk[i][j][p], rC, off, 0, 0);
-        }
-      }
-  };
-
   auto put32 = [&](int64_t zz, int mm, int nn) {
     const int LDC = static_cast<int>(a.ldc);
     char* Cz = static_cast<char*>(a.C) + zz * a.sC * 4;
@@ -362,11 +257,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
     }
     __builtin_amdgcn_sched_barrier(0);
     if (next) issue(zn, m0n, n0n, slot ^ 1);
-    if (pend) {  // the previous tile's C
-      if constexpr (SMAX) put(zp, m0p, n0p);
-      if constexpr (HOLD) put32(zp, m0p, n0p);
+    if constexpr (HOLD) {
+      if (pend) put32(zp, m0p, n0p);  // the previous tile's C
+      pend = false;
     }
-    pend = false;
     __builtin_amdgcn_sched_barrier(0);
 
 #pragma unroll
@@ -382,86 +276,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = mma<T>(fa[s][i], fb[s][j], acc[i][j]);
 
-    if constexpr (SMAX) {
-      // P = softmax(scale S) along each row, columns past N at -inf. Each wave
-      // reduces its own 64 columns: the row maximum m_w (halving exchange, so lane
-      // `own` holds row own), then e = exp(s - m_w) and the sum s_w of e. After one
-      // barrier the lane owning a row merges the 8 waves' (m_w, s_w) as the online
-      // softmax does: M = max m_w, S = sum s_w exp(m_w - M), and scales its wave's
-      // e by exp(m_w - M) / S. Per-row values reach the other lanes of the wave
-      // through the wave's own LDS row (a wave's LDS accesses complete in order).
-      // exp is the hardware exp2 of the argument times log2(e).
-      const float scl = a.epi.scale;
-      const int h = lane >> 5, q = lane & 31;
-      const int own = 32 * (q >> 4) + 8 * ((q & 15) >> 2) + 4 * h + (q & 3);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const bool cin = n0 + wn * WTN + 32 * j + lrow < N;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = cin ? acc[i][j][r] * scl : -INFINITY;
-        }
-      float* const wrow = sm_w + wave * BM;
-      float rv[FM][16];
-      auto row_values = [&]() {  // wrow at the rows of this lane's registers
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const f32x4 v = *reinterpret_cast<const f32x4*>(wrow + 32 * i + 8 * r4 + 4 * h);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) rv[i][4 * r4 + t] = v[t];
-          }
-      };
-      float x[32];
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[16 * i + r] = fmaxf(acc[i][0][r], acc[i][1][r]);
-      const float mw = halve32<true>(x, lane);
-      // a wave whose columns are all past N has m_w = -inf: subtract 0 instead (e = 0)
-      wrow[own] = mw == -INFINITY ? 0.f : mw;
-      row_values();
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] = __expf(acc[i][j][r] - rv[i][r]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[16 * i + r] = acc[i][0][r] + acc[i][1][r];
-      const float sw = halve32<false>(x, lane);
-      sm_part[wave * BM + own] = float2{mw, sw};
-      lds_barrier();
-      float2 pw[NW];
-#pragma unroll
-      for (int w = 0; w < NW; ++w) pw[w] = sm_part[w * BM + own];
-      float mx = pw[0].x;
-#pragma unroll
-      for (int w = 1; w < NW; ++w) mx = fmaxf(mx, pw[w].x);
-      float sum = 0.f;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) sum += pw[w].y * __expf(pw[w].x - mx);
-      wrow[own] = __expf(mw - mx) * (1.f / sum);
-      row_values();
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[i][j][r] *= rv[i][r];
-    }
     if (defer) {
-      if constexpr (SMAX) pack();
-      if constexpr (HOLD) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) held[i][j] = acc[i][j];
-      }
+        for (int j = 0; j < FN; ++j) held[i][j] = acc[i][j];
       pend = true;
       zp = z;
       m0p = m0;
@@ -476,20 +295,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
     n0 = n0n;
     slot ^= 1;
   }
-  if (pend) {
-    if constexpr (SMAX) put(zp, m0p, n0p);
-    if constexpr (HOLD) put32(zp, m0p, n0p);
-  }
+  if (pend) put32(zp, m0p, n0p);
 }
 
-template <typename T, int BM, int BN, int WGM, int WGN, bool BROW, bool SMAX = false>
+template <typename T, int BM, int BN, int WGM, int WGN, bool BROW>
 hipError_t launch_m16s(const LaunchArgs& a, hipStream_t s) {
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN) * a.batch;
   // a.split: the workgroups the device keeps resident (set at plan time); a multiple
   // of 8 so each XCD gets the same number
   int64_t g = a.split > 1 ? a.split : 512;
   if (tiles < g) g = (tiles + 7) / 8 * 8;
-  hipLaunchKernelGGL((gemm_m16s_kernel<T, BM, BN, WGM, WGN, BROW, SMAX>), dim3(static_cast<unsigned>(g)),
+  hipLaunchKernelGGL((gemm_m16s_kernel<T, BM, BN, WGM, WGN, BROW>), dim3(static_cast<unsigned>(g)),
                      dim3(64 * WGM * WGN), 0, s, a);
   return hipGetLastError();
 }
@@ -509,15 +325,6 @@ const KernelEntry kM16S[] = {
 };
 
 }  // namespace
-
-hipError_t launch_attention_probs(const LaunchArgs& a, bool bf16, bool b_rowmajor, hipStream_t s) {
-  if (a.K > 64 || a.N > 512 || a.epi.flags != 0) return hipErrorInvalidValue;
-  if (bf16)
-    return b_rowmajor ? launch_m16s<bf16_t, 64, 512, 1, 8, true, true>(a, s)
-                      : launch_m16s<bf16_t, 64, 512, 1, 8, false, true>(a, s);
-  return b_rowmajor ? launch_m16s<f16_t, 64, 512, 1, 8, true, true>(a, s)
-                    : launch_m16s<f16_t, 64, 512, 1, 8, false, true>(a, s);
-}
 
 int mfma16_k1_entries(const KernelEntry** out) {
   *out = kM16S;

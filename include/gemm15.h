@@ -190,7 +190,7 @@ int gemm_softmax_rows(const float* S, int64_t rows, int64_t cols, int64_t ld_s, 
  *
  * i.e. the first product of attention and the softmax after it (tutorial page,
  * section 2) with the scores kept in FP32 registers: each workgroup holds whole
- * rows (64 query rows x every key), takes their maximum and the FP32 sum of
+ * rows (32 query rows x every key), takes their maximum and the FP32 sum of
  * exp(s - max) there (DeepGEMM page, section 3.4), and writes P once, so the FP32
  * score matrix is never written to or read back from memory.
  *
