@@ -46,9 +46,10 @@ constexpr int WTN = BN / NW, FN = WTN / 32;
 constexpr int A_STAGE = BM * 8, B_STAGE = BN * 8;  // 16-byte chunks
 constexpr int BI = B_STAGE / 64 / NW;               // key loads per wave
 
-template <bool MAXOP>
+enum { OP_MAX = 0, OP_MIN = 1, OP_ADD = 2 };
+template <int OP>
 __device__ __forceinline__ float comb(float a, float b) {
-  return MAXOP ? fmaxf(a, b) : a + b;
+  return OP == OP_MAX ? fmaxf(a, b) : OP == OP_MIN ? fminf(a, b) : a + b;
 }
 
 // m ? a : b as a bit select (v_bfi_b32) behind inline assembly: written as a
@@ -68,14 +69,14 @@ __device__ __forceinline__ float dpp(float v) {
 // One halving round: a lane keeps the half of its H-value pairs that lane bit BIT
 // selects and combines it with the partner's copy (partner: the DPP pattern CTRL,
 // which differs in bit BIT and agrees in the bits of the earlier rounds).
-template <bool MAXOP, int H, int BIT, int CTRL>
+template <int OP, int H, int BIT, int CTRL>
 __device__ __forceinline__ void halve_round(float (&x)[16], int lane) {
   const uint32_t up = (lane & BIT) != 0 ? 0xffffffffu : 0u;
 #pragma unroll
   for (int q = 0; q < H; ++q) {
     const float send = bit_pick(up, x[q], x[q + H]);
     const float keep = bit_pick(up, x[q + H], x[q]);
-    x[q] = comb<MAXOP>(keep, dpp<CTRL>(send));
+    x[q] = comb<OP>(keep, dpp<CTRL>(send));
   }
 }
 
@@ -85,18 +86,18 @@ __device__ __forceinline__ void halve_round(float (&x)[16], int lane) {
 // (row_mirror), l ^ 7 (row_half_mirror) and l ^ 2, bit 0 by a full exchange with
 // lane l ^ 1. Lanes 2i and 2i+1 of each half end with the reduction of value i, in
 // a fixed order.
-template <bool MAXOP>
+template <int OP>
 __device__ __forceinline__ float halve16(float (&x)[16], int lane) {
 #pragma unroll
   for (int q = 0; q < 8; ++q) {
     const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x[q]), __float_as_uint(x[q + 8]),
                                                     false, false);
-    x[q] = comb<MAXOP>(__uint_as_float(r[0]), __uint_as_float(r[1]));
+    x[q] = comb<OP>(__uint_as_float(r[0]), __uint_as_float(r[1]));
   }
-  halve_round<MAXOP, 4, 8, 0x140>(x, lane);  // row_mirror
-  halve_round<MAXOP, 2, 4, 0x141>(x, lane);  // row_half_mirror
-  halve_round<MAXOP, 1, 2, 0x4E>(x, lane);   // quad_perm 2 3 0 1
-  return comb<MAXOP>(x[0], dpp<0xB1>(x[0]));  // quad_perm 1 0 3 2
+  halve_round<OP, 4, 8, 0x140>(x, lane);  // row_mirror
+  halve_round<OP, 2, 4, 0x141>(x, lane);  // row_half_mirror
+  halve_round<OP, 1, 2, 0x4E>(x, lane);   // quad_perm 2 3 0 1
+  return comb<OP>(x[0], dpp<0xB1>(x[0]));  // quad_perm 1 0 3 2
 }
 
 // two workgroups per CU: at most 256 registers per lane (2 waves per SIMD)
@@ -196,22 +197,26 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_probs_kernel(LaunchArgs 
   // holds keys (c, c+1) of row R and the odd lane (c-1, c) of row R+1
   const bool defer = a.epi.out_dtype != DT_F32 && (N & 1) == 0 && (a.ldc & 1) == 0;
   const bool bf_out = a.epi.out_dtype == DT_BF16;
-  const uint32_t odd_mask = (lane & 1) != 0 ? 0xffffffffu : 0u;
   f32x16 acc[1][FN];
   uint32_t pk[FN][8];
+  // rows R, R+1 of this lane's key converted as a pair (RNE), the neighbour's pair
+  // fetched, and the row this lane stores picked bytewise: the even lane takes
+  // (R, c) and (R, c+1), the odd lane (R+1, c-1) and (R+1, c). v_perm_b32 numbers
+  // the bytes of its second operand 0-3 and of its first 4-7.
+  const uint32_t pick = (lane & 1) != 0 ? 0x03020706u : 0x05040100u;
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
   auto pack = [&]() {
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
       for (int p = 0; p < 8; ++p) {
-        const float e0 = acc[0][j][2 * p], e1 = acc[0][j][2 * p + 1];
-        const float recv = dpp<0xB1>(bit_pick(odd_mask, e0, e1));
-        const float lo = bit_pick(odd_mask, recv, e0);
-        const float hi = bit_pick(odd_mask, e1, recv);
-        pk[j][p] = bf_out ? (static_cast<uint32_t>(narrow_bf16(lo)) |
-                             (static_cast<uint32_t>(narrow_bf16(hi)) << 16))
-                          : (static_cast<uint32_t>(narrow_f16(lo)) |
-                             (static_cast<uint32_t>(narrow_f16(hi)) << 16));
+        const f32x2 e = {acc[0][j][2 * p], acc[0][j][2 * p + 1]};
+        const uint32_t own2 = bf_out ? __builtin_bit_cast(uint32_t, __builtin_convertvector(e, bf16x2))
+                                     : __builtin_bit_cast(uint32_t, __builtin_convertvector(e, f16x2));
+        const uint32_t nb2 = __builtin_amdgcn_mov_dpp(own2, 0xB1, 0xf, 0xf, false);
+        pk[j][p] = __builtin_amdgcn_perm(nb2, own2, pick);
       }
   };
   // a whole tile (32 rows inside M, all 512 keys): a per-lane byte offset fixed for
@@ -319,16 +324,18 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_probs_kernel(LaunchArgs 
 
     // softmax of the 32 rows: lane l holds key wave WTN + 32 j + l % 32 of rows
     // 8 (r / 4) + 4 (l / 32) + r % 4, r = 0 .. 15
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[0][j][r] *= scl2;
-    if (N < BN) {  // keys past N: -inf
+    // The scaled scores are c s with c = scale log2(e); their row maximum is c times
+    // the maximum of s (the minimum for a negative scale), so s stays unscaled and
+    // each exponential takes fma(s, c, -m). Keys past N (N < 512 only): s set to the
+    // far end so the maximum ignores them, their exponentials to 0 afterwards.
+    const bool neg = scl2 < 0.f;
+    if (N < BN) {
+      const float far = neg ? INFINITY : -INFINITY;
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const bool cin = wave * WTN + 32 * j + lrow < N;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[0][j][r] = cin ? acc[0][j][r] : -INFINITY;
+        for (int r = 0; r < 16; ++r) acc[0][j][r] = cin ? acc[0][j][r] : far;
       }
     }
     float x[16], rv[16];
@@ -340,30 +347,53 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_probs_kernel(LaunchArgs 
         for (int u = 0; u < 4; ++u) rv[4 * r4 + u] = w4[u];
       }
     };
+    float m_raw;
+    if (!neg) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      float m = acc[0][0][r];
+      for (int r = 0; r < 16; ++r) {
+        float m = acc[0][0][r];
 #pragma unroll
-      for (int j = 1; j < FN; ++j) m = fmaxf(m, acc[0][j][r]);
-      x[r] = m;
+        for (int j = 1; j < FN; ++j) m = fmaxf(m, acc[0][j][r]);
+        x[r] = m;
+      }
+      m_raw = halve16<OP_MAX>(x, lane);
+    } else {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float m = acc[0][0][r];
+#pragma unroll
+        for (int j = 1; j < FN; ++j) m = fminf(m, acc[0][j][r]);
+        x[r] = m;
+      }
+      m_raw = halve16<OP_MIN>(x, lane);
     }
-    const float mw = halve16<true>(x, lane);
-    // a wave whose keys all lie past N has m_w = -inf: subtract 0 instead (e = 0);
-    // both lanes of a pair write the same value (a wave's LDS accesses complete in order)
+    // the wave's row maximum of c s: -inf when its keys all lie past N, and then 0 is
+    // subtracted instead (e = 0); both lanes of a pair write the same value (a wave's
+    // LDS accesses complete in order)
+    const float mw = __builtin_isinf(m_raw) ? -INFINITY : m_raw * scl2;
     wrow[own] = mw == -INFINITY ? 0.f : mw;
     row_values();
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[0][j][r] = __builtin_amdgcn_exp2f(acc[0][j][r] - rv[r]);
+      for (int r = 0; r < 16; ++r)
+        acc[0][j][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(acc[0][j][r], scl2, -rv[r]));
+    if (N < BN) {
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const bool cin = wave * WTN + 32 * j + lrow < N;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[0][j][r] = cin ? acc[0][j][r] : 0.f;
+      }
+    }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      float s = acc[0][0][r];
+      float sm = acc[0][0][r];
 #pragma unroll
-      for (int j = 1; j < FN; ++j) s += acc[0][j][r];
-      x[r] = s;
+      for (int j = 1; j < FN; ++j) sm += acc[0][j][r];
+      x[r] = sm;
     }
-    const float sw = halve16<false>(x, lane);
+    const float sw = halve16<OP_ADD>(x, lane);
     sm_part[wave * BM + own] = float2{mw, sw};
     lds_barrier();
     float mx = -INFINITY;
