@@ -17,13 +17,14 @@
 // share an L2. A workgroup reloads the keys only where its run crosses into the
 // next item.
 //
-// Softmax per tile: scale, keys past N at -inf; each wave reduces its 128 keys to a
-// per-row maximum m_w and sum s_w of e = exp(s - m_w) by a halving exchange over the
-// 32 lanes that hold a row (v_permlane16_swap, then DPP moves; no LDS); after one
-// barrier the lanes owning a row merge the waves' (m_w, s_w) as the online softmax
-// does (M = max m_w, S = sum s_w exp(m_w - M)) and the wave scales e by
-// exp(m_w - M) / S. A 16-bit P of even N is packed into registers and stored one
-// tile late, after the next tile's loads are issued.
+// Softmax per tile, in base 2 (exp(scale s) = 2^(c s), c = scale log2 e): each wave
+// reduces its 128 keys to a per-row maximum m_w of c s and the sum s_w of
+// e = 2^(c s - m_w) by a halving exchange over the 32 lanes that hold a row
+// (v_permlane16_swap, then DPP moves; no LDS); after one barrier the lanes owning a
+// row merge the waves' (m_w, s_w) as the online softmax does (M = max m_w,
+// S = sum s_w 2^(m_w - M)) and the wave scales e by 2^(m_w - M) / S. A 16-bit P of
+// even N is packed into registers and stored one tile late, after the next tile's
+// loads are issued.
 //
 // LDS layouts (as the m16 kernels): a Q slot is 32 rows of 64 k, chunk c of row r
 // at c ^ (r & 7) ^ ((r >> 3) & 3); keys as K^T [D x N]: 64 rows (k) of 512 keys,
@@ -266,8 +267,8 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_probs_kernel(LaunchArgs 
   bool pend = false;
   int64_t zp = 0;
   int m0p = 0;
-  // the softmax runs in base 2: exp(x) = 2^(x log2 e), so the scores are scaled by
-  // scale log2(e) once and every exponential is the hardware exp2 (v_exp_f32)
+  // the softmax runs in base 2: exp(scale s) = 2^(c s) with c = scale log2(e), and
+  // every exponential is the hardware exp2 (v_exp_f32)
   const float scl2 = a.epi.scale * 1.44269504088896341f;
   const int q = lane & 31;
   const int own = 8 * (q >> 3) + 4 * lhalf + ((q >> 1) & 3);  // the row this lane's reductions end on
