@@ -125,6 +125,23 @@ def test_attention_probs_heads(g, layout):
     say(f"[attention_probs] 96 heads {layout}: max err/bound {worst:.3f}")
 
 
+@pytest.mark.parametrize("nb,M,N,layout", [(80, 250, 136, "kn"), (70, 256, 512, "nk")])
+def test_attention_probs_runs_cross_items(g, nb, M, N, layout):
+    """More 32-row tiles than resident workgroups (640 and 560 against 512), so
+    workgroups walk runs of one or two tiles and many runs cross into the next item
+    (keys reloaded mid-run); N = 512 with whole tiles takes the unchecked store
+    path. Every element of every item."""
+    dev = torch.device("cuda")
+    seed = 2300 + nb
+    Q = synth.normal(seed, (nb, M, 64), 1.0, "bf16")
+    Kmat = synth.normal(seed + 1, (nb, 64, N) if layout == "kn" else (nb, N, 64), 1.0, "bf16")
+    P = g.attention_probs(Q.to(dev), Kmat.to(dev), 0.125, layout, "bf16")
+    torch.cuda.synchronize()
+    P = P.cpu()
+    worst = max(_check_item(P[b], Q[b], Kmat[b], layout, 0.125, "bf16", "bf16") for b in range(nb))
+    say(f"[attention_probs] {nb} x {M}x{N} {layout}: max err/bound {worst:.3f}")
+
+
 def test_attention_probs_errors(g):
     """Argument errors come back as status codes and launch nothing."""
     dev = torch.device("cuda")
