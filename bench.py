@@ -105,6 +105,9 @@ def parse():
     ap.add_argument("--vendor", action="store_true",
                     help="also time torch.mm (the vendor library) and this library on the "
                          "4096^3 bf16 product with bf16 output, for context")
+    ap.add_argument("--attention", action="store_true",
+                    help="also time the attention workload alone (its stages, the fused "
+                         "QK^T + softmax kernel and both chains); part of --all")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
@@ -521,6 +524,9 @@ def main():
     if args.vendor:
         extra["vendor_bf16_out"] = vendor_reference(g, args.steps, args.warmup)
         print(f"[bench] vendor {json.dumps(extra['vendor_bf16_out'])}", file=sys.stderr, flush=True)
+    if args.attention and not args.all:
+        extra["attention"] = attention_workload(g, args.steps, args.warmup)
+        print(f"[bench] {json.dumps(extra['attention'])}", file=sys.stderr, flush=True)
     if args.copy_calibration:
         import torch as _t
         src = _t.empty(64 * 2**20, dtype=_t.float32, device="cuda")  # 256 MiB
