@@ -388,6 +388,19 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
     if (pk >= 0 && (s.config < 0 || pcost < cost)) {
       s.config = pk;
       s.packed = (pa ? 1 : 0) | (pb ? 2 : 0);
+      // padded K within one 64-deep slice and a large C: the streaming kernel, whose
+      // workgroups keep the next tile's operands loading while C of this one leaves
+      if (!b_nk && round_up8(K) <= 64 && static_cast<double>(M) * N >= double(1 << 22)) {
+        const std::string want = std::string("m16s_") + (dtype == GEMM_BF16 ? "bf16" : "f16") +
+                                 "_256x128x64_w4x2";
+        for (size_t i = 0; i < all.size(); ++i)
+          if (want == all[i].name && cfg_fits(all[i], dtype, true, true, dev, M,
+                                              (pb ? round_up8(N) : N), round_up8(K),
+                                              epi.out_dtype, false)) {
+            s.config = static_cast<int>(i);
+            break;
+          }
+      }
     }
   }
   return s;
@@ -519,7 +532,7 @@ int run_packed(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, con
     la.epi.out_dtype = p->epi.out_dtype;
     la.workspace = nullptr;
     la.workspace_bytes = 0;
-    la.split = 1;
+    la.split = k.kind == KIND_K1 ? p->split : 1;  // resident workgroups of a streaming kernel
     la.lda = p->lda_p;
     la.ldb = p->ldb_p;  // padded, or the unpadded row length
     la.ldc = p->N;
