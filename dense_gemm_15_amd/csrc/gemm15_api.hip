@@ -76,6 +76,8 @@ struct Registry {
     all.insert(all.end(), p, p + n);
     n = mfma16_k1_entries(&p);
     all.insert(all.end(), p, p + n);
+    n = mfma16_w_entries(&p);
+    all.insert(all.end(), p, p + n);
   }
 };
 

@@ -73,5 +73,6 @@ int f32_dlds_entries(const KernelEntry** out);
 int gemv_entries(const KernelEntry** out);
 int ladder_entries(const KernelEntry** out);
 int mfma16_k1_entries(const KernelEntry** out);
+int mfma16_w_entries(const KernelEntry** out);
 
 }  // namespace g15

@@ -55,8 +55,8 @@ def _dtype_of(name):
 
 CONFIGS = _configs()
 TILE_CONFIGS = [c for c in CONFIGS if not c.startswith(("gemv", "m16n", "m16s"))
-                and "acc16" not in c]
-NT_CONFIGS = [c for c in CONFIGS if c.startswith("m16n")]
+                and not c.endswith("_nk") and "acc16" not in c]
+NT_CONFIGS = [c for c in CONFIGS if c.startswith("m16n") or (c.startswith("m16w") and c.endswith("_nk"))]
 GEMV_CONFIGS = [c for c in CONFIGS if c.startswith("gemv")]
 
 
@@ -664,3 +664,34 @@ def test_errors_on_device(g):
     assert rc == -4  # fp32 A not 4-byte aligned
     rc = g.lib.gemm_run(None, None, None, None, None, None, None)
     assert rc == -7
+
+
+W_CONFIGS = [c for c in CONFIGS if c.startswith("m16w")]
+
+
+@pytest.mark.parametrize("name", W_CONFIGS)
+def test_epilogues_each_m16w(g, name):
+    """The one-wave-per-SIMD kernels with every epilogue stage and output type:
+    16-byte-aligned C rows with N % 8 == 0 (the LDS-staged store), and for B given
+    transposed also N even but not a multiple of 8 (two columns per lane) and N odd
+    (one element per lane); K with a ragged 32-deep tail. Every element."""
+    dtype = _dtype_of(name)
+    nk = name.endswith("_nk")
+    cases = [(300, 264, 200, dict(bias=True, gelu=True, out_dtype="bf16")),
+             (257, 136, 96, dict(bias=True, resid=True, out_dtype=dtype)),
+             (130, 264, 64, dict(scale=0.5, resid=True, out_dtype="f32")),
+             (70, 520, 40, dict(bias=True, out_dtype="f16"))]
+    if nk:
+        cases += [(130, 262, 64, dict(scale=0.5, resid=True, out_dtype="bf16")),
+                  (70, 263, 40, dict(bias=True, gelu=True, out_dtype="f16")),
+                  (99, 261, 72, dict(resid=True, out_dtype="f32"))]
+    for ci, (M, N, K, epi) in enumerate(cases):
+        plan = g.Plan(M, N, K, dtype, config=name, b_layout="nk" if nk else "kn", **epi)
+        say(f"[{name}] {M}x{N}x{K} {epi}")
+        A, B = gc.inputs(M, N, K, dtype, 1500 + ci)
+        od = epi.get("out_dtype", "f32")
+        bias = synth.normal(1510 + ci, (N,), 0.5, "f32") if epi.get("bias") else None
+        resid = synth.uniform(1520 + ci, (M, N), od) if epi.get("resid") else None
+        C = _run_nt(plan, A, B, bias, resid) if nk else gc.run_gpu(plan, A, B, bias, resid)
+        r = gc.check_full(C, A, B, dtype, od, bias, resid, epi.get("scale"), epi.get("gelu", False))
+        assert r["ok"], (name, M, N, K, epi, r)
