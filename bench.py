@@ -16,8 +16,13 @@ whole timed region is also bracketed by device synchronisation.
 ``cpu_baseline`` times the fp64 host oracle on a bounded row-block of the same
 product on the host's cores.
 
+The same line carries ``configs``: every configuration of the benchmark set (FP16
+512^3, FP32 4096^3, BF16/FP16 4096^3, the encoder FFN pair and chain, the 96
+attention-score heads and the odd shapes), each timed by the protocol below and
+inside a replayed HIP graph, with its roofline fraction against its own bound.
+
 Usage: python bench.py [--gpus 1] [--steps 100] [--warmup 10] [--all] [--no-cpu] [--vendor]
-       [--ladder]
+       [--ladder] [--no-configs]
 """
 from __future__ import annotations
 
@@ -98,6 +103,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--all", action="store_true", help="also time every workload (stderr + json)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the per-configuration block (every workload of the benchmark set)")
     ap.add_argument("--json-out", default=None, help="write per-workload results here")
     ap.add_argument("--ladder", action="store_true",
                     help="also time the optimisation ladder V0..V4 on the 4096^3 fp16 product "
@@ -142,6 +149,28 @@ def time_calls(fn, steps, warmup, settle_s=None):
     return med, sum(ms) / len(ms), wall
 
 
+def time_protocol(fn, steps, warmup):
+    """The measurement protocol of the benchmark: warm-up (as time_calls), then
+    `steps` samples, each an event pair around R back-to-back calls, R = 1 when a call
+    takes at least 50 us, otherwise enough calls for a sample of 200 us; per-call time
+    = median sample / R. Returns (median_ms, mean_ms, R)."""
+    import torch
+    med1, _, _ = time_calls(fn, 5, warmup)
+    reps = 1 if med1 >= 0.05 else max(1, int(0.2 / max(med1, 1e-4)) + 1)
+    st = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(steps)]
+    for a, b in ev:
+        a.record(st)
+        for _ in range(reps):
+            fn()
+        b.record(st)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) / reps for a, b in ev)
+    med = ms[len(ms) // 2] if len(ms) % 2 else 0.5 * (ms[len(ms) // 2 - 1] + ms[len(ms) // 2])
+    return med, sum(ms) / len(ms), reps
+
+
 def time_graph(fn, reps=20, replays=7):
     """Median per-call milliseconds of `reps` calls captured in one HIP graph and
     replayed: the GPU time of a call without the host's launch overhead, which
@@ -172,6 +201,13 @@ def time_graph(fn, reps=20, replays=7):
     return sorted(ts)[len(ts) // 2]
 
 
+def workspace_for(plan, dev):
+    """The plan's scratch, allocated once outside the timed calls (None: needs none)."""
+    import torch
+    n = plan.workspace_bytes
+    return torch.empty(n, dtype=torch.uint8, device=dev) if n else None
+
+
 def gemm_workload(g, name, steps, warmup, graph=False, b_layout="kn"):
     import torch
     import synth
@@ -184,7 +220,8 @@ def gemm_workload(g, name, steps, warmup, graph=False, b_layout="kn"):
     M, N, K = w["M"], w["N"], w["K"]
     plan = g.Plan(M, N, K, w["dtype"], b_layout=b_layout)
     C = torch.empty((M, N), dtype=torch.float32, device=dev)
-    run = lambda: plan.run(A, B, out=C)  # noqa: E731
+    ws = workspace_for(plan, dev)
+    run = lambda: plan.run(A, B, out=C, workspace=ws)  # noqa: E731
     med, mean, wall = time_calls(run, steps, warmup)
     flops = 2 * M * N * K
     es = 4 if w["dtype"] == "f32" else 2
@@ -386,6 +423,95 @@ def attention_workload(g, steps, warmup):
     return dict(workload="attention_96x512x64", stages=out)
 
 
+def baseline_configs(g, steps, warmup, head, f32):
+    """Every configuration of the benchmark set on this chip, each with its bound:
+    (1) FP16 512^3, (2) FP32 4096^3, (3) BF16 and FP16 4096^3, (4) the encoder FFN pair
+    and its chain, (5) 96 attention-score heads and the three odd shapes. Times: `ms` by
+    the event protocol (time_protocol), `graph_ms` per call inside a replayed HIP graph
+    (GPU time without host launch gaps); the roofline fraction uses graph_ms, against
+    the dense matrix peak of the input type (bound "mfma") or 8 TB/s of algorithmic
+    bytes (bound "hbm": A and B read once, C written once, bias and residual read
+    once); launch-bound shapes report both."""
+    import torch
+    import synth
+    dev = torch.device("cuda")
+    out = {}
+
+    def entry(fn, flops, byts, bound, kernel, dtype):
+        med, mean, reps = time_protocol(fn, steps, warmup)
+        gms = time_graph(fn)
+        e = dict(kernel=kernel, ms=round(med, 5), calls_per_sample=reps, graph_ms=round(gms, 5),
+                 tflops=round(flops / (gms * 1e-3) / 1e12, 2),
+                 gbs=round(byts / (gms * 1e-3) / 1e9, 1), bound=bound)
+        f_m = flops / (gms * 1e-3) / 1e12 / PEAK_TFLOPS[dtype]
+        f_h = byts / (gms * 1e-3) / 1e9 / PEAK_HBM_GBS
+        if bound == "mfma":
+            e["frac"] = round(f_m, 4)
+        elif bound == "hbm":
+            e["frac"] = round(f_h, 4)
+        else:  # launch/latency-bound: both figures
+            e["frac_mfma"], e["frac_hbm"] = round(f_m, 4), round(f_h, 4)
+        return e
+
+    def gemm_entry(name, bound):
+        w = synth.WORKLOADS[name]
+        A, B = (t.to(dev) for t in synth.gemm_inputs(name))
+        M, N, K, dt = w["M"], w["N"], w["K"], w["dtype"]
+        plan = g.Plan(M, N, K, dt)
+        C = torch.empty((M, N), dtype=torch.float32, device=dev)
+        ws = workspace_for(plan, dev)
+        es = 4 if dt == "f32" else 2
+        return entry(lambda: plan.run(A, B, out=C, workspace=ws), 2 * M * N * K,
+                     (M * K + K * N) * es + M * N * 4, bound, plan.config_name, dt)
+
+    out["1_fp16_512"] = gemm_entry("fp16_512", "launch")
+    print(f"[bench] configs 1 {json.dumps(out['1_fp16_512'])}", file=sys.stderr, flush=True)
+    out["2_fp32_4096"] = dict(kernel=f32["config"], ms=round(f32["median_ms"], 5),
+                              tflops=round(f32["tflops"], 2), bound="mfma",
+                              frac=round(f32["frac_peak"], 4))
+    out["3_bf16_4096"] = dict(kernel=head["config"], ms=round(head["median_ms"], 5),
+                              tflops=round(head["tflops"], 2), bound="mfma",
+                              frac=round(head["frac_peak"], 4))
+    out["3_fp16_4096"] = gemm_entry("fp16_4096", "mfma")
+    print(f"[bench] configs 3 {json.dumps(out['3_fp16_4096'])}", file=sys.stderr, flush=True)
+
+    X, W1, b1, W2, b2 = (t.to(dev) for t in synth.ffn_inputs())
+    T, Hd, F = X.shape[0], X.shape[1], W1.shape[1]
+    p1 = g.Plan(T, F, Hd, "bf16", bias=True, gelu=True, out_dtype="bf16")
+    p2 = g.Plan(T, Hd, F, "bf16", bias=True, resid=True, out_dtype="bf16")
+    H = torch.empty((T, F), dtype=torch.bfloat16, device=dev)
+    Y = torch.empty((T, Hd), dtype=torch.bfloat16, device=dev)
+    w1, w2 = workspace_for(p1, dev), workspace_for(p2, dev)
+    f1 = lambda: p1.run(X, W1, bias=b1, out=H, workspace=w1)  # noqa: E731
+    f2 = lambda: p2.run(H, W2, bias=b2, resid=X, out=Y, workspace=w2)  # noqa: E731
+    fl = 2 * T * F * Hd
+    by1 = (T * Hd + Hd * F + T * F) * 2 + F * 4
+    by2 = (T * F + F * Hd + 2 * T * Hd) * 2 + Hd * 4
+    out["4_ffn1_bias_gelu_bf16"] = entry(f1, fl, by1, "mfma", p1.config_name, "bf16")
+    out["4_ffn2_bias_resid_bf16"] = entry(f2, fl, by2, "mfma", p2.config_name, "bf16")
+
+    def chain():
+        f1()
+        f2()
+    out["4_ffn_chain"] = entry(chain, 2 * fl, by1 + by2, "mfma", "ffn1+ffn2", "bf16")
+    print(f"[bench] configs 4 {json.dumps(out['4_ffn_chain'])}", file=sys.stderr, flush=True)
+
+    Q, Kt = (t.to(dev) for t in synth.qk_inputs())
+    nb, S, D = Q.shape
+    pq = g.Plan(S, S, D, "bf16", batch_hint=nb)
+    Sc = torch.empty((nb, S, S), dtype=torch.float32, device=dev)
+    wq = workspace_for(pq, dev)
+    out["5_qk_96x512x512x64"] = entry(lambda: pq.run_batched(Q, Kt, out=Sc, workspace=wq),
+                                      2 * nb * S * S * D, nb * (2 * S * D * 2 + S * S * 4), "hbm",
+                                      pq.config_name, "bf16")
+    out["5_gemv_1x4096x4096"] = gemm_entry("gemv_1x4096x4096", "hbm")
+    out["5_odd_127x1000x771"] = gemm_entry("odd_127x1000x771", "launch")
+    out["5_odd_4095x4097x63"] = gemm_entry("odd_4095x4097x63", "hbm")
+    print(f"[bench] configs 5 {json.dumps({k: v for k, v in out.items() if k[0] == '5'})}",
+          file=sys.stderr, flush=True)
+    return out
+
+
 def cpu_baseline(target_s=15.0):
     """The fp64 oracle on the 4096^3 bf16 product on all host cores: a row block
     sized to about `target_s` seconds, or the whole product repeated until that
@@ -409,8 +535,28 @@ def cpu_baseline(target_s=15.0):
         reps += 1
     fl = 2 * rows2 * 4096 * 4096 * reps
     what = (f"rows 0..{rows2 - 1} of" if rows2 < 4096 else f"{reps} x the whole")
+    # one core: the whole fp16 512^3 product on a single thread
+    A5, B5 = synth.gemm_inputs("fp16_512")
+    A5b, B5b = synth.bits(A5), synth.bits(B5)
+    t0 = time.perf_counter()
+    oracle.gemm(A5b, B5b, "f16", nthreads=1, lib=lib)
+    t1 = time.perf_counter() - t0
     return dict(value=fl / t2 / 1e12, unit="TFLOPS", cores=oracle.threads(lib), kind="oracle",
-                sample=f"{what} 4096^3 bf16 product (fp64 loop), {t2:.1f} s")
+                sample=f"{what} 4096^3 bf16 product (fp64 loop), {t2:.1f} s",
+                cpu_model=cpu_model(),
+                single_core_512_gflops=round(2 * 512 ** 3 / t1 / 1e9, 3))
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def symbol_to_config(sym: str):
@@ -557,6 +703,10 @@ def main():
         extra["qk_nt"] = qk_workload(g, args.steps, args.warmup, b_layout="nk")
         print(f"[bench] {json.dumps(extra['qk_nt'])}", file=sys.stderr, flush=True)
 
+    configs = None
+    if not args.no_configs:
+        configs = baseline_configs(g, args.steps, args.warmup, head, f32)
+
     cpu = None
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
@@ -592,6 +742,7 @@ def main():
                                          "peak": PEAK_TFLOPS["f32"], "unit": "TFLOP/s",
                                          "frac": round(f32["frac_peak"], 4),
                                          "traffic": measured_traffic(f32["config"])}},
+        "configs": configs,
         "cpu_baseline": cpu,
     }
     if args.json_out:

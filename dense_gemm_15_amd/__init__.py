@@ -31,7 +31,7 @@ _NAME = {v: k for k, v in _CODE.items()}
 STATUS = {
     0: "GEMM_OK", -1: "GEMM_ERR_SHAPE", -2: "GEMM_ERR_DTYPE", -3: "GEMM_ERR_NULL",
     -4: "GEMM_ERR_ALIGN", -5: "GEMM_ERR_NO_DEVICE", -6: "GEMM_ERR_HIP", -7: "GEMM_ERR_PLAN",
-    -8: "GEMM_ERR_NOMEM", -9: "GEMM_ERR_CONFIG", -10: "GEMM_ERR_ARG",
+    -8: "GEMM_ERR_NOMEM", -9: "GEMM_ERR_CONFIG", -10: "GEMM_ERR_ARG", -11: "GEMM_ERR_WORKSPACE",
 }
 
 
@@ -66,6 +66,10 @@ SIGNATURES = {
     "gemm_run": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP]),
     "gemm_run_strided_batched": (ctypes.c_int, [_VP, _I64, _VP, _I64, _VP, _I64, _VP, _VP, _I64,
                                                 _VP, _I64, _VP]),
+    "gemm_run_ws": (ctypes.c_int, [_VP, _VP, _VP, _VP, _VP, _VP, _VP, _I64, _VP]),
+    "gemm_run_strided_batched_ws": (ctypes.c_int, [_VP, _I64, _VP, _I64, _VP, _I64, _VP, _VP,
+                                                   _I64, _VP, _I64, _VP, _I64, _VP]),
+    "gemm_plan_workspace_bytes": (_I64, [_VP]),
     "gemm_plan_destroy": (None, [_VP]),
     "gemm_softmax_rows": (ctypes.c_int, [_VP, _I64, _I64, _I64, ctypes.c_float, _VP, _I64, _I32,
                                          _VP]),
@@ -172,6 +176,31 @@ class Plan:
             lib.gemm_plan_destroy(h)
             self._h = None
 
+    @property
+    def workspace_bytes(self) -> int:
+        """Device scratch the plan's runs use (0 for most plans)."""
+        n = lib.gemm_plan_workspace_bytes(self._h)
+        if n < 0:
+            raise GemmError(n, "gemm_plan_workspace_bytes")
+        return n
+
+    def _workspace(self, workspace, device, stream):
+        """(pointer, bytes) of the scratch for one run: None allocates it through torch
+        when the plan needs some; False runs the plan's workspace-free configuration; a
+        uint8 cuda tensor is used as given."""
+        if workspace is False:
+            return None, 0, None
+        n = self.workspace_bytes
+        if workspace is None:
+            if n == 0:
+                return None, 0, None
+            workspace = torch.empty(n, dtype=torch.uint8, device=device)
+        if workspace.device.type != "cuda" or workspace.dtype != torch.uint8:
+            raise TypeError("workspace must be a uint8 cuda tensor")
+        if stream is not None and stream != torch.cuda.current_stream(workspace.device):
+            workspace.record_stream(stream)  # freed memory is not reused before the run ends
+        return ctypes.c_void_p(workspace.data_ptr()), workspace.numel(), workspace
+
     def describe(self) -> str:
         buf = ctypes.create_string_buffer(512)
         rc = lib.gemm_plan_describe(self._h, buf, len(buf))
@@ -195,8 +224,11 @@ class Plan:
         s = stream if stream is not None else torch.cuda.current_stream()
         return ctypes.c_void_p(s.cuda_stream)
 
-    def run(self, A, B, bias=None, resid=None, out=None, stream=None):
-        """C = epi(A x B) on the current (or given) stream; returns C."""
+    def run(self, A, B, bias=None, resid=None, out=None, stream=None, workspace=None):
+        """C = epi(A x B) on the current (or given) stream; returns C. workspace: None
+        (scratch allocated through torch when the plan needs some), False (the plan's
+        workspace-free configuration) or a uint8 cuda tensor of at least
+        workspace_bytes."""
         M, N, K = self.M, self.N, self.K
         self._check(A, (M, K), self.dtype, "A")
         self._check(B, (K, N) if self.b_layout == "kn" else (N, K), self.dtype, "B")
@@ -207,14 +239,16 @@ class Plan:
             self._check(bias, (N,), "f32", "bias")
         if self.flags.flags & EPI_RESID:
             self._check(resid, (M, N), self.out_dtype, "resid")
-        rc = lib.gemm_run(self._h, _ptr(A), _ptr(B), _ptr(bias), _ptr(resid), _ptr(out),
-                          self._stream(stream))
+        wp, wn, _keep = self._workspace(workspace, A.device, stream)
+        rc = lib.gemm_run_ws(self._h, _ptr(A), _ptr(B), _ptr(bias), _ptr(resid), _ptr(out),
+                             wp, wn, self._stream(stream))
         if rc != 0:
-            raise GemmError(rc, "gemm_run")
+            raise GemmError(rc, "gemm_run_ws")
         return out
 
-    def run_batched(self, A, B, bias=None, resid=None, out=None, stream=None):
-        """C[b] = epi(A[b] x B[b]) for 3-D contiguous A [b,M,K], B [b,K,N]; returns C."""
+    def run_batched(self, A, B, bias=None, resid=None, out=None, stream=None, workspace=None):
+        """C[b] = epi(A[b] x B[b]) for 3-D contiguous A [b,M,K], B [b,K,N]; returns C
+        (workspace as for run)."""
         M, N, K = self.M, self.N, self.K
         nb = A.shape[0]
         self._check(A, (nb, M, K), self.dtype, "A")
@@ -226,11 +260,12 @@ class Plan:
             self._check(bias, (N,), "f32", "bias")
         if self.flags.flags & EPI_RESID:
             self._check(resid, (nb, M, N), self.out_dtype, "resid")
-        rc = lib.gemm_run_strided_batched(self._h, nb, _ptr(A), M * K, _ptr(B), K * N,
-                                          _ptr(bias), _ptr(resid), M * N, _ptr(out), M * N,
-                                          self._stream(stream))
+        wp, wn, _keep = self._workspace(workspace, A.device, stream)
+        rc = lib.gemm_run_strided_batched_ws(self._h, nb, _ptr(A), M * K, _ptr(B), K * N,
+                                             _ptr(bias), _ptr(resid), M * N, _ptr(out), M * N,
+                                             wp, wn, self._stream(stream))
         if rc != 0:
-            raise GemmError(rc, "gemm_run_strided_batched")
+            raise GemmError(rc, "gemm_run_strided_batched_ws")
         return out
 
 

@@ -29,6 +29,8 @@
 
 using namespace g15;
 
+// A plan holds host state only: the choice of configuration and the sizes of the
+// scratch its runs use, which the caller passes in (gemm_run_ws).
 struct gemm_plan {
   int64_t M, N, K;
   int32_t dtype;
@@ -36,16 +38,16 @@ struct gemm_plan {
   int device;
   int config;    // primary configuration
   int fallback;  // configuration for pointers without 16-byte alignment (may equal config)
+  int nows;      // configuration run when the plan needs a workspace and none is given
+                 // (-1: none exists); it needs no workspace itself
   int64_t batch_hint;
-  void* workspace;
-  int64_t workspace_bytes;
-  int split;
+  int64_t workspace_bytes;  // scratch of the primary configuration's runs (0: none)
+  int split;        // K split of the primary configuration (resident workgroups: K1 kind)
   int b_nk;         // 1: B is given transposed, Bt [N x K] row-major
-  int packed;       // bit 0: A rows padded into pack_a; bit 1: B rows into pack_b
-  int64_t lda_p;    // padded row lengths (elements) of pack_a and pack_b
+  int packed;       // bit 0: A rows padded into the workspace; bit 1: B rows
+  int64_t lda_p;    // padded row lengths (elements) of the A and B copies
   int64_t ldb_p;
-  void* pack_a;
-  void* pack_b;
+  int64_t pack_b_off;  // byte offset of the B copy in the workspace (the A copy is at 0)
 };
 
 namespace {
@@ -294,6 +296,7 @@ struct Selection {
   int config = -1;
   int fallback = -1;
   int packed = 0;
+  int tile = -1;  // best tile configuration that needs no workspace, for aligned pointers
 };
 
 int64_t round_up8(int64_t x) { return (x + 7) / 8 * 8; }
@@ -344,6 +347,7 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
   auto any = [](const KernelEntry&) { return true; };
   Selection s;
   s.fallback = best_for(false, false, K, N, any, nullptr);
+  s.tile = best_for(vec_a, vec_b, K, N, any, nullptr);
   // A few rows (M <= 8): the product is a stream over B, served by the
   // split-K few-row kernel with the fewest rows that covers M (DeepGEMM page,
   // section 4.3: small shapes get their own small-block kernel).
@@ -503,15 +507,17 @@ bool aligned_to(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p
 // padded buffers, then run the 16-byte-load kernel with the padded row strides.
 int run_packed(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, const void* B,
                int64_t sB, const float* bias, const void* resid, int64_t sR, void* C, int64_t sC,
-               bool c16, hipStream_t s) {
+               bool c16, void* ws, hipStream_t s) {
   const KernelEntry& k = registry().all[p->config];
   const int64_t ie = elem_bytes(p->dtype), oe = elem_bytes(p->epi.out_dtype);
+  void* const pack_a = ws;
+  void* const pack_b = static_cast<char*>(ws) + p->pack_b_off;
   for (int64_t z = 0; z < batch; ++z) {
     const char* Az = static_cast<const char*>(A) + z * sA * ie;
     const char* Bz = static_cast<const char*>(B) + z * sB * ie;
-    if ((p->packed & 1) && pack_rows16(Az, p->M, p->K, p->pack_a, p->lda_p, s) != hipSuccess)
+    if ((p->packed & 1) && pack_rows16(Az, p->M, p->K, pack_a, p->lda_p, s) != hipSuccess)
       return GEMM_ERR_HIP;
-    if ((p->packed & 2) && pack_rows16(Bz, p->b_nk ? p->N : p->K, p->b_nk ? p->K : p->N, p->pack_b,
+    if ((p->packed & 2) && pack_rows16(Bz, p->b_nk ? p->N : p->K, p->b_nk ? p->K : p->N, pack_b,
                                        p->ldb_p, s) != hipSuccess)
       return GEMM_ERR_HIP;
     LaunchArgs la;
@@ -519,9 +525,9 @@ int run_packed(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, con
     la.N = p->N;
     la.K = p->K;
     la.batch = 1;
-    la.A = (p->packed & 1) ? p->pack_a : Az;
+    la.A = (p->packed & 1) ? pack_a : Az;
     la.sA = 0;
-    la.B = (p->packed & 2) ? p->pack_b : Bz;
+    la.B = (p->packed & 2) ? pack_b : Bz;
     la.sB = 0;
     la.C = static_cast<char*>(C) + z * sC * oe;
     la.sC = 0;
@@ -552,7 +558,7 @@ int run_packed(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, con
 // share the workspace.
 int run_split_k(const gemm_plan* p, const KernelEntry& k, int64_t batch, const void* A,
                 int64_t sA, const void* B, int64_t sB, const float* bias, const void* resid,
-                int64_t sR, void* C, int64_t sC, hipStream_t s) {
+                int64_t sR, void* C, int64_t sC, void* ws, hipStream_t s) {
   const int S = p->split;
   const int64_t kc = p->K / S;
   const int64_t ie = elem_bytes(p->dtype);
@@ -566,7 +572,7 @@ int run_split_k(const gemm_plan* p, const KernelEntry& k, int64_t batch, const v
     la.sA = kc;
     la.B = static_cast<const char*>(B) + z * sB * ie;
     la.sB = kc * p->N;
-    la.C = p->workspace;
+    la.C = ws;
     la.sC = p->M * p->N;
     la.sR = 0;
     la.epi.flags = 0;
@@ -595,12 +601,42 @@ int run_split_k(const gemm_plan* p, const KernelEntry& k, int64_t batch, const v
     lr.epi.bias = bias;
     lr.epi.resid = resid;
     lr.epi.out_dtype = p->epi.out_dtype;
-    lr.workspace = p->workspace;
+    lr.workspace = ws;
     lr.workspace_bytes = p->workspace_bytes;
     lr.split = S;
     if (launch_splitk_reduce(lr, z, p->M, s) != hipSuccess) return GEMM_ERR_HIP;
   }
   return GEMM_OK;
+}
+
+// One-line description of a plan (its configuration choice, for logs and tuning).
+int describe_plan(const gemm_plan* p, char* buf, size_t len) {
+  const auto& all = registry().all;
+  const KernelEntry& k = all[p->config];
+  char tmp[384];
+  const int n = std::snprintf(
+      tmp, sizeof(tmp),
+      "config=%s id=%d tile=%dx%dx%d threads=%d lds=%d workgroups=%lld split=%d packed=%d "
+      "b=%s fallback=%s workspace=%lld nows=%s",
+      k.name, p->config, k.bm, k.bn, k.bk, k.threads, k.lds_bytes,
+      static_cast<long long>(cfg_workgroups(k, p->M, p->N, p->split, p->batch_hint)),
+      k.kind == KIND_K1 ? 1 : p->split,  // a K1 plan keeps its resident workgroups there
+      p->packed, p->b_nk ? "nk" : "kn", p->fallback >= 0 ? all[p->fallback].name : "none",
+      static_cast<long long>(p->workspace_bytes), p->nows >= 0 ? all[p->nows].name : "none");
+  if (buf && len > 0) {
+    std::strncpy(buf, tmp, len - 1);
+    buf[len - 1] = '\0';
+  }
+  return n;
+}
+
+// GEMM15_LOG set (and not "0"): every plan creation prints its choice to stderr.
+bool log_enabled() {
+  static const bool on = [] {
+    const char* s = std::getenv("GEMM15_LOG");
+    return s && *s && std::strcmp(s, "0") != 0;
+  }();
+  return on;
 }
 
 }  // namespace
@@ -657,50 +693,47 @@ gemm_plan* gemm_plan_create_layout(int64_t M, int64_t N, int64_t K, int32_t dtyp
   p->config = cfg;
   p->fallback = fb;
   p->batch_hint = batch_hint;
-  p->workspace = nullptr;
   p->workspace_bytes = 0;
   p->split = 1;
   p->b_nk = b_nk ? 1 : 0;
   p->packed = sel.packed;
   p->lda_p = (sel.packed & 1) ? round_up8(K) : K;
   p->ldb_p = b_nk ? ((sel.packed & 2) ? round_up8(K) : K) : ((sel.packed & 2) ? round_up8(N) : N);
-  p->pack_a = nullptr;
-  p->pack_b = nullptr;
+  p->pack_b_off = 0;
   if (sel.packed) {
     const int64_t es = elem_bytes(dtype);
-    const bool ok =
-        (!(sel.packed & 1) || hipMalloc(&p->pack_a, static_cast<size_t>(M * p->lda_p * es)) == hipSuccess) &&
-        (!(sel.packed & 2) ||
-         hipMalloc(&p->pack_b, static_cast<size_t>((b_nk ? N : K) * p->ldb_p * es)) == hipSuccess);
-    if (!ok) {
-      (void)hipGetLastError();
-      if (p->pack_a) (void)hipFree(p->pack_a);
-      delete p;
-      return fail(GEMM_ERR_NOMEM);
-    }
+    const int64_t a_bytes = (sel.packed & 1) ? M * p->lda_p * es : 0;
+    const int64_t b_bytes = (sel.packed & 2) ? (b_nk ? N : K) * p->ldb_p * es : 0;
+    p->pack_b_off = (a_bytes + 255) / 256 * 256;
+    p->workspace_bytes = p->pack_b_off + b_bytes;
   }
   const KernelEntry& k = all[cfg];
   if (k.kind == KIND_K1) p->split = k1_workgroups(k, desc);
   if (k.kind == KIND_MFMA16 && !sel.packed && !b_nk) {
     p->split = tile_split(k, M, N, K, batch_hint, desc);
-    if (p->split > 1) {
-      p->workspace_bytes = static_cast<int64_t>(p->split) * M * N * 4;
-      if (hipMalloc(&p->workspace, static_cast<size_t>(p->workspace_bytes)) != hipSuccess) {
-        (void)hipGetLastError();
-        delete p;
-        return fail(GEMM_ERR_NOMEM);
-      }
-    }
+    if (p->split > 1) p->workspace_bytes = static_cast<int64_t>(p->split) * M * N * 4;
   }
   if (k.kind == KIND_GEMV) {
     p->split = gemv_split(k, N, K, batch_hint, desc);
     p->workspace_bytes = gemv_workspace_bytes(k, N, p->split);
-    if (p->workspace_bytes > 0 &&
-        hipMalloc(&p->workspace, static_cast<size_t>(p->workspace_bytes)) != hipSuccess) {
-      (void)hipGetLastError();
-      delete p;
-      return fail(GEMM_ERR_NOMEM);
-    }
+  }
+  // Without a workspace: the same kernel with K unsplit when it can take all of K,
+  // otherwise the best plain tile configuration; padded copies give way to the
+  // scalar-load configuration (none for a transposed B).
+  p->nows = cfg;
+  if (sel.packed) {
+    p->nows = b_nk ? -1 : fb;
+  } else if (k.kind == KIND_GEMV && p->split > 1 && K > k.bk) {
+    int t = sel.tile;
+    if (forced >= 0) t = select_config(desc, M, N, K, dtype, epi, batch_hint, true, b_nk).tile;
+    p->nows = t >= 0 ? t : fb;
+  }
+  if (log_enabled()) {
+    char line[512];
+    describe_plan(p, line, sizeof(line));
+    std::fprintf(stderr, "gemm15: plan M=%lld N=%lld K=%lld dtype=%d flags=%u out=%d batch=%lld: %s\n",
+                 static_cast<long long>(M), static_cast<long long>(N), static_cast<long long>(K),
+                 dtype, epi.flags, epi.out_dtype, static_cast<long long>(batch_hint), line);
   }
   return p;
 }
@@ -774,12 +807,14 @@ int gemm_attention_probs(const void* Q, const void* Kmat, int64_t batch, int64_t
   return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
 }
 
-int gemm_run_strided_batched(const gemm_plan* p, int64_t batch, const void* A, int64_t sA,
-                             const void* B, int64_t sB, const float* bias, const void* resid,
-                             int64_t sR, void* C, int64_t sC, void* stream) {
+int gemm_run_strided_batched_ws(const gemm_plan* p, int64_t batch, const void* A, int64_t sA,
+                                const void* B, int64_t sB, const float* bias, const void* resid,
+                                int64_t sR, void* C, int64_t sC, void* ws, int64_t ws_bytes,
+                                void* stream) {
   if (!p) return GEMM_ERR_PLAN;
   if (batch < 1 || batch > 65535 || sA < 0 || sB < 0 || sC < 0 || sR < 0) return GEMM_ERR_ARG;
   if (!A || !B || !C) return GEMM_ERR_NULL;
+  if (ws_bytes < 0 || (!ws && ws_bytes != 0)) return GEMM_ERR_ARG;
   const gemm_epilogue& e = p->epi;
   if ((e.flags & GEMM_EPI_BIAS) && !bias) return GEMM_ERR_NULL;
   if ((e.flags & GEMM_EPI_RESID) && !resid) return GEMM_ERR_NULL;
@@ -787,9 +822,16 @@ int gemm_run_strided_batched(const gemm_plan* p, int64_t batch, const void* A, i
   if (!aligned_to(A, ie) || !aligned_to(B, ie) || !aligned_to(C, oe)) return GEMM_ERR_ALIGN;
   if ((e.flags & GEMM_EPI_BIAS) && !aligned_to(bias, 4)) return GEMM_ERR_ALIGN;
   if ((e.flags & GEMM_EPI_RESID) && !aligned_to(resid, oe)) return GEMM_ERR_ALIGN;
+  if (ws && !aligned_to(ws, 256)) return GEMM_ERR_ALIGN;
+  if (ws && ws_bytes < p->workspace_bytes) return GEMM_ERR_WORKSPACE;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
   if (dev != p->device) return GEMM_ERR_PLAN;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  // scratch for the plan's own configuration, or its workspace-free configuration
+  const bool use_ws = p->workspace_bytes > 0 && ws != nullptr;
+  const bool no_ws = p->workspace_bytes > 0 && !use_ws;
+  if (no_ws && p->nows < 0) return GEMM_ERR_WORKSPACE;
 
   // The vector kernels need 16-byte aligned base pointers and batch strides.
   const bool a16 = aligned_to(A, 16) && aligned_to(B, 16) && aligned_to(C, 16) &&
@@ -798,19 +840,19 @@ int gemm_run_strided_batched(const gemm_plan* p, int64_t batch, const void* A, i
   const auto& all = registry().all;
   const bool c16 = aligned_to(C, 16) && (p->N * oe) % 16 == 0 && (sC * oe) % 16 == 0 &&
                    (!(e.flags & GEMM_EPI_RESID) || (aligned_to(resid, 16) && (sR * oe) % 16 == 0));
-  if (p->packed) {
+  if (p->packed && use_ws) {
     // operands that are not copied must still be 16-byte aligned for the kernel
     const bool a_ok = (p->packed & 1) || (aligned_to(A, 16) && (sA * ie) % 16 == 0);
     const bool b_ok = (p->packed & 2) || (aligned_to(B, 16) && (sB * ie) % 16 == 0);
-    if (a_ok && b_ok) return run_packed(p, batch, A, sA, B, sB, bias, resid, sR, C, sC, c16,
-                                        static_cast<hipStream_t>(stream));
+    if (a_ok && b_ok) return run_packed(p, batch, A, sA, B, sB, bias, resid, sR, C, sC, c16, ws, st);
   }
-  const int ci = a16 && !p->packed ? p->config : p->fallback;
+  int ci = p->fallback;
+  if (a16 && !p->packed) ci = no_ws ? p->nows : p->config;
+  else if (a16 && no_ws) ci = p->nows;
   if (ci < 0) return GEMM_ERR_ALIGN;  // transposed B: 16-byte aligned operands required
   const KernelEntry& k = all[ci];
-  if (p->split > 1 && ci == p->config && k.kind == KIND_MFMA16)
-    return run_split_k(p, k, batch, A, sA, B, sB, bias, resid, sR, C, sC,
-                       static_cast<hipStream_t>(stream));
+  if (p->split > 1 && ci == p->config && k.kind == KIND_MFMA16 && use_ws)
+    return run_split_k(p, k, batch, A, sA, B, sB, bias, resid, sR, C, sC, ws, st);
 
   const int64_t tiles = ((p->M + k.bm - 1) / k.bm) * ((p->N + k.bn - 1) / k.bn);
   if (tiles > 0x7fffffff) return GEMM_ERR_SHAPE;
@@ -833,30 +875,48 @@ int gemm_run_strided_batched(const gemm_plan* p, int64_t batch, const void* A, i
   la.epi.bias = bias;
   la.epi.resid = resid;
   la.epi.out_dtype = e.out_dtype;
-  la.workspace = p->workspace;
-  la.workspace_bytes = p->workspace_bytes;
-  la.split = p->split;
+  la.workspace = nullptr;
+  la.workspace_bytes = 0;
+  la.split = 1;
+  if (ci == p->config && k.kind == KIND_K1) la.split = p->split;  // resident workgroups
+  if (ci == p->config && k.kind == KIND_GEMV && use_ws) {
+    la.split = p->split;
+    la.workspace = ws;
+    la.workspace_bytes = p->workspace_bytes;
+  }
   la.lda = p->K;
   la.ldb = p->b_nk ? p->K : p->N;
   la.ldc = p->N;
   la.c_vec = (a16 && p->N % 8 == 0) ? 1 : 0;
-  const hipError_t err = k.launch(la, static_cast<hipStream_t>(stream));
+  const hipError_t err = k.launch(la, st);
   return err == hipSuccess ? GEMM_OK : GEMM_ERR_HIP;
+}
+
+int gemm_run_strided_batched(const gemm_plan* p, int64_t batch, const void* A, int64_t sA,
+                             const void* B, int64_t sB, const float* bias, const void* resid,
+                             int64_t sR, void* C, int64_t sC, void* stream) {
+  return gemm_run_strided_batched_ws(p, batch, A, sA, B, sB, bias, resid, sR, C, sC, nullptr, 0,
+                                     stream);
+}
+
+int gemm_run_ws(const gemm_plan* p, const void* A, const void* B, const float* bias,
+                const void* resid, void* C, void* ws, int64_t ws_bytes, void* stream) {
+  if (!p) return GEMM_ERR_PLAN;
+  return gemm_run_strided_batched_ws(p, 1, A, 0, B, 0, bias, resid, 0, C, 0, ws, ws_bytes, stream);
 }
 
 int gemm_run(const gemm_plan* p, const void* A, const void* B, const float* bias,
              const void* resid, void* C, void* stream) {
   if (!p) return GEMM_ERR_PLAN;
-  return gemm_run_strided_batched(p, 1, A, 0, B, 0, bias, resid, 0, C, 0, stream);
+  return gemm_run_strided_batched_ws(p, 1, A, 0, B, 0, bias, resid, 0, C, 0, nullptr, 0, stream);
 }
 
-void gemm_plan_destroy(gemm_plan* p) {
-  if (!p) return;
-  if (p->workspace) (void)hipFree(p->workspace);
-  if (p->pack_a) (void)hipFree(p->pack_a);
-  if (p->pack_b) (void)hipFree(p->pack_b);
-  delete p;
+int64_t gemm_plan_workspace_bytes(const gemm_plan* p) {
+  if (!p) return GEMM_ERR_PLAN;
+  return p->workspace_bytes;
 }
+
+void gemm_plan_destroy(gemm_plan* p) { delete p; }
 
 int gemm_last_error(void) { return t_last_error; }
 
@@ -873,28 +933,15 @@ const char* gemm_strerror(int s) {
     case GEMM_ERR_NOMEM: return "out of memory while creating a plan";
     case GEMM_ERR_CONFIG: return "the requested configuration cannot run this problem";
     case GEMM_ERR_ARG: return "invalid argument";
+    case GEMM_ERR_WORKSPACE:
+      return "the workspace is smaller than the plan needs, or the plan cannot run without one";
   }
   return "unknown status";
 }
 
 int gemm_plan_describe(const gemm_plan* p, char* buf, size_t len) {
   if (!p) return GEMM_ERR_PLAN;
-  const auto& all = registry().all;
-  const KernelEntry& k = all[p->config];
-  char tmp[256];
-  const int n = std::snprintf(
-      tmp, sizeof(tmp),
-      "config=%s id=%d tile=%dx%dx%d threads=%d lds=%d workgroups=%lld split=%d packed=%d "
-      "b=%s fallback=%s",
-      k.name, p->config, k.bm, k.bn, k.bk, k.threads, k.lds_bytes,
-      static_cast<long long>(cfg_workgroups(k, p->M, p->N, p->split, p->batch_hint)),
-      k.kind == KIND_K1 ? 1 : p->split,  // a K1 plan keeps its resident workgroups there
-      p->packed, p->b_nk ? "nk" : "kn", p->fallback >= 0 ? all[p->fallback].name : "none");
-  if (buf && len > 0) {
-    std::strncpy(buf, tmp, len - 1);
-    buf[len - 1] = '\0';
-  }
-  return n;
+  return describe_plan(p, buf, len);
 }
 
 int gemm_select_layout(const gemm_device_desc* dev, int64_t M, int64_t N, int64_t K,

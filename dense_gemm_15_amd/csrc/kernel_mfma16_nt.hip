@@ -25,7 +25,10 @@
 // bytes per slice). With SB = SA - 1 (the 256 x 256 tile, whose rings would not
 // fit otherwise) B is fetched one slice ahead, A two; the B loads of a slice are
 // issued before its A loads so the wait at the slice boundary can leave the
-// newest A loads in flight.
+// newest A loads in flight. The compiler makes an LDS read that may alias a
+// direct-to-LDS load in flight wait for every load (vmcnt(0)); each slice takes
+// its read and load slots as separate restrict parameters, so that wait is gone
+// and the A loads keep their lead across the slice boundary.
 #include "m16_common.hpp"
 
 namespace g15 {
@@ -34,6 +37,7 @@ namespace {
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 typedef __attribute__((address_space(3))) char lds_char;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 template <typename T, int BM, int BN, int WGM, int WGN, int SA, int SB, bool BROW>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a) {
@@ -180,22 +184,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
   }
   // Fragment read r of k-step s, in the order the ops of a k-step consume them:
   // A block 0, B blocks 0 .. FN-1, then A blocks 1 .. FM-1.
-  auto read_frag = [&](const u32x4* LA, const u32x4* LB, int s, int r, u32x4 (&fa)[FM],
-                       u32x4 (&fb)[FN]) {
+  auto read_frag = [&](const lds_char* LA, const lds_char* LB, int s, int r, u32x4 (&fa)[FM],
+                       u32x4 (&fb)[FN]) __attribute__((always_inline)) {
     const int c = (2 * s + lhalf) ^ perm;
     if (r == 0 || r > FN) {
       const int i = r == 0 ? 0 : r - FN;
-      fa[i] = LA[a_base + i * 256 + c];
+      fa[i] = *(const lds_u32x4*)(LA + (a_base + i * 256 + c) * 16);
       return;
     }
     const int j = r - 1;
     if constexpr (!BROW) {
-      fb[j] = LB[b_base + j * 256 + c];
+      fb[j] = *(const lds_u32x4*)(LB + (b_base + j * 256 + c) * 16);
     } else {
-      // address the LDS array itself (an address-space cast of a derived generic
-      // pointer is not available in the host compilation of this kernel)
-      const int boff = static_cast<int>(LB - lds) * 16 + 16 * s * (BN * 2) + btr[j];
-      const lds_char* Lb = (const lds_char*)lds + boff;
+      const lds_char* Lb = LB + 16 * s * (BN * 2) + btr[j];
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)Lb);
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(Lb + 4 * (BN * 2)));
       fb[j] = u32x4{__builtin_bit_cast(uint32_t, __builtin_shufflevector(lo, lo, 0, 1)),
@@ -204,9 +205,15 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
                     __builtin_bit_cast(uint32_t, __builtin_shufflevector(hi, hi, 2, 3))};
     }
   };
-  auto frags = [&](const u32x4* LA, const u32x4* LB, int s, u32x4 (&fa)[FM], u32x4 (&fb)[FN]) {
+  auto frags = [&](const lds_char* LA, const lds_char* LB, int s, u32x4 (&fa)[FM],
+                   u32x4 (&fb)[FN]) __attribute__((always_inline)) {
 #pragma unroll
     for (int r = 0; r < FM + FN; ++r) read_frag(LA, LB, s, r, fa, fb);
+  };
+  lds_char* const L8 = (lds_char*)lds;
+  auto slotA8 = [&](int sl) __attribute__((always_inline)) { return L8 + sl * A_STAGE * 16; };
+  auto slotB8 = [&](int sl) __attribute__((always_inline)) {
+    return L8 + (SA * A_STAGE + sl * B_STAGE) * 16;
   };
 
   // matrix-core ops of one k-step on rows [I0, I1) of the wave's blocks
@@ -227,7 +234,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
   wait_vm<0>();
   lds_barrier();
   u32x4 f0a[FM], f0b[FN], f1a[FM], f1b[FN];
-  frags(ringA, ringB, 0, f0a, f0b);
+  frags(slotA8(0), slotB8(0), 0, f0a, f0b);
 
   // m16n: the instruction order of a slice is fixed here, op by op: each
   // matrix-core op is followed by the fragment reads and direct loads assigned to
@@ -252,8 +259,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
     const int na = ca + 1 == SA ? 0 : ca + 1, nb = cb + 1 == SB ? 0 : cb + 1;
     const int fa = ca == 0 ? SA - 1 : ca - 1;  // slot of A(kt-1), refilled with A(kt+SA-1)
     const int fb = cb == 0 ? SB - 1 : cb - 1;  // slot of B(kt-1), refilled with B(kt+SB-1)
-    const u32x4* LA = ringA + ca * A_STAGE;
-    const u32x4* LB = ringB + cb * B_STAGE;
+    // Slot pointers of this slice (reads of slice kt, of slice kt+1 after the
+    // boundary, loads of the slices kt+SA-1 / kt+SB-1) passed as restrict parameters:
+    // the compiler then does not make the transposing reads wait for the loads in
+    // flight (each slot it reads has been waited for explicitly before the barrier).
+    auto body = [&](const lds_char* __restrict__ LA, const lds_char* __restrict__ LB,
+                    const lds_char* __restrict__ NA, const lds_char* __restrict__ NB,
+                    lds_char* __restrict__ WA, lds_char* __restrict__ WB)
+                    __attribute__((always_inline)) {
     // descriptors of this slice's direct loads (scalar work)
     const int k0a = (kt + SA - 1) * BK, k0b = (kt + SB - 1) * BK;
     const int64_t lefta = static_cast<int64_t>(M) * LDA - k0a;
@@ -271,21 +284,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
     auto dma = [&](int v) {
       if (v < BI) {
         const int i = v;
-        u32x4* dst = ringB + fb * B_STAGE + (wave * BI + i) * 64;
+        lds_char* dst = WB + (wave * BI + i) * 1024;
         bool kin;
         if constexpr (!BROW)
           kin = !TAIL || k0b + b_chk[i] * 8 < K;
         else
           kin = !TAIL || k0b + b_row[i] < K;
         const uint32_t off = kin ? b_voff[i] : OOB;
-        if (TAIL && !kin) dst[lane] = u32x4{0u, 0u, 0u, 0u};
+        if (TAIL && !kin) ((lds_u32x4*)dst)[lane] = u32x4{0u, 0u, 0u, 0u};
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rB, (lds_void*)dst, 16, off, 0, 0, 0);
       } else {
         const int i = v - BI;
-        u32x4* dst = ringA + fa * A_STAGE + (wave * AI + i) * 64;
+        lds_char* dst = WA + (wave * AI + i) * 1024;
         const bool kin = !TAIL || k0a + a_chk[i] * 8 < K;
         const uint32_t off = kin ? a_voff[i] : OOB;
-        if (TAIL && !kin) dst[lane] = u32x4{0u, 0u, 0u, 0u};
+        if (TAIL && !kin) ((lds_u32x4*)dst)[lane] = u32x4{0u, 0u, 0u, 0u};
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rA, (lds_void*)dst, 16, off, 0, 0, 0);
       }
     };
@@ -313,8 +326,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
       plan_slice<0, FM * FN, FM + FN, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
       // the B fragments of k-step 3 are read here too, before the slice's direct
-      // loads: the compiler makes a transposing LDS read that follows a direct load
-      // wait for every load in flight (plain reads it lets through)
+      // loads (measured order; with the slots as restrict parameters the compiler no
+      // longer makes these reads wait for the loads in flight, so this order is not
+      // required for that any more)
       u32x4 f3b[FN];
       frags(LA, LB, 2, f0a, f0b);
 #pragma unroll
@@ -336,12 +350,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
       __builtin_amdgcn_sched_barrier(0);
       wait_vm<WAITN>();
       lds_barrier();
-      frags(ringA + na * A_STAGE, ringB + nb * B_STAGE, 0, f0a, f0b);
+      frags(NA, NB, 0, f0a, f0b);
       mmas(f1a, f1b, HALF, FM);
       plan_slice<0, (FM - HALF) * FN, FM + FN, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
-      ca = na;
-      cb = nb;
       return;
     }
     step(0, f0a, f0b, f1a, f1b);
@@ -354,8 +366,6 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
     }
     wait_vm<WAITN>();
     lds_barrier();
-    const u32x4* NA = ringA + na * A_STAGE;
-    const u32x4* NB = ringB + nb * B_STAGE;
 #pragma unroll
     for (int q = Q3; q < NM; ++q) {
       acc[q / FN][q % FN] = mma<T>(f1a[q / FN], f1b[q % FN], acc[q / FN][q % FN]);
@@ -363,6 +373,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
       if (q == Q3) frags(NA, NB, 0, f0a, f0b);
       __builtin_amdgcn_sched_barrier(0);
     }
+    };
+    body(slotA8(ca), slotB8(cb), slotA8(na), slotB8(nb), slotA8(fa), slotB8(fb));
     ca = na;
     cb = nb;
   };

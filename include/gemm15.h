@@ -28,16 +28,19 @@
  * Conventions of every entry point below:
  *  - All pointers to matrix data are DEVICE pointers (memory of the GPU that is
  *    current on the calling thread). The caller allocates and owns them; the
- *    library never frees, copies or synchronises them.
+ *    library never frees or synchronises them and writes only C (and a
+ *    workspace passed to it).
  *  - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *    gemm_run* only enqueue work on it and return; results are ready when the
  *    stream reaches that point.
  *  - Errors are negative gemm_status codes; the creating calls return NULL and
- *    record the code for gemm_last_error(). No call aborts the process.
- *  - Thread safety: plans are immutable after creation and may be run from
- *    several host threads. A plan whose description has split > 1 or packed > 0
- *    owns a device workspace; two runs of such a plan must not overlap in time
- *    (use one plan per stream).
+ *    record the code for gemm_last_error(). No call aborts the process; launch
+ *    failures are read back with hipGetLastError (tutorial page, section 7: check
+ *    the error state after every launch).
+ *  - Plans hold host state only: no call allocates device memory except through
+ *    a workspace the caller passes in. A plan is immutable after creation and may
+ *    be run concurrently from several host threads and streams; runs that use a
+ *    workspace need one workspace each while they overlap.
  */
 #ifndef GEMM15_H
 #define GEMM15_H
@@ -78,7 +81,9 @@ typedef enum gemm_status {
   GEMM_ERR_PLAN = -7,      /* NULL plan, or a plan used on another device than its own */
   GEMM_ERR_NOMEM = -8,     /* host or device memory for a plan could not be allocated */
   GEMM_ERR_CONFIG = -9,    /* a forced configuration does not exist or does not fit */
-  GEMM_ERR_ARG = -10       /* another invalid argument (batch < 1, a bad stride, ...) */
+  GEMM_ERR_ARG = -10,      /* another invalid argument (batch < 1, a bad stride, ...) */
+  GEMM_ERR_WORKSPACE = -11 /* the workspace passed is smaller than the plan needs, or the
+                              plan has no configuration that runs without one */
 } gemm_status;
 
 /* Storage of the right operand B. */
@@ -93,10 +98,11 @@ typedef struct gemm_plan gemm_plan;
 /*
  * Create a plan for C = epi(A x B) with A M x K and B K x N of type `dtype`.
  * Chooses the kernel configuration (shape-bucket rules, exact-shape cache) for
- * the device current on the calling thread. Host work only, except that a plan
- * whose configuration splits K, or that copies 16-bit operands whose rows are not
- * 16-byte multiples (K or N not a multiple of 8) into zero-padded rows, allocates
- * its own device workspace (freed by gemm_plan_destroy).
+ * the device current on the calling thread. Host work only: the plan owns no
+ * device memory. A configuration that splits K (fp32 partial sums), or that
+ * copies 16-bit operands whose rows are not 16-byte multiples (K or N not a
+ * multiple of 8) into zero-padded rows, needs device scratch that the caller
+ * passes to gemm_run_ws (size from gemm_plan_workspace_bytes).
  * Returns NULL on error (see gemm_last_error()).
  */
 gemm_plan* gemm_plan_create(int64_t M, int64_t N, int64_t K, int32_t dtype,
@@ -123,12 +129,24 @@ gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
  * as the matrix core reads them, and both stream straight into LDS.
  * GEMM_B_NK needs a 16-bit dtype (GEMM_ERR_DTYPE otherwise) and 16-byte aligned
  * A, Bt and C base pointers and batch strides at run time (GEMM_ERR_ALIGN
- * otherwise); when K is not a multiple of 8 the plan copies A and Bt into
- * zero-padded rows before each run. GEMM_ERR_ARG for another b_layout.
+ * otherwise); when K is not a multiple of 8 a run with a workspace first copies
+ * A and Bt into zero-padded rows there (without one: GEMM_ERR_WORKSPACE).
+ * GEMM_ERR_ARG for another b_layout.
  */
 gemm_plan* gemm_plan_create_layout(int64_t M, int64_t N, int64_t K, int32_t dtype,
                                    const gemm_epilogue* epi, int64_t batch_hint, int32_t config,
                                    int32_t b_layout);
+
+/*
+ * Device scratch, in bytes, that gemm_run_ws and gemm_run_strided_batched_ws use
+ * for this plan (0 for most plans): the fp32 partial sums of a plan that splits K
+ * (split x M x N floats, or split x rows x N for the few-row kernel), or the
+ * zero-padded copies of A and/or B of a plan with padded operands (each copy's
+ * rows rounded up to 8 elements, the B copy at the next 256-byte boundary).
+ * Batch items of one call reuse it in stream order. Returns the size, or a
+ * negative status (GEMM_ERR_PLAN for NULL).
+ */
+int64_t gemm_plan_workspace_bytes(const gemm_plan* plan);
 
 /*
  * Enqueue C = epi(A x B) on `stream`.
@@ -140,9 +158,27 @@ gemm_plan* gemm_plan_create_layout(int64_t M, int64_t N, int64_t K, int32_t dtyp
  *  C      device, M x N row-major of out_dtype; must not overlap A or B
  * Returns GEMM_OK, or GEMM_ERR_PLAN / _NULL / _ALIGN / _HIP. Pointers need only
  * element alignment; 16-byte aligned rows take the vector-load kernels.
+ * Without a workspace, a plan that would use one runs its configuration that
+ * needs none: the same kernel with K unsplit, or the scalar-load kernel in place
+ * of padded copies (GEMM_ERR_WORKSPACE for a transposed-B plan with padded
+ * operands, which has none). Nothing is allocated or copied.
  */
 int gemm_run(const gemm_plan* plan, const void* A, const void* B, const float* bias,
              const void* resid, void* C, void* stream);
+
+/*
+ * gemm_run with caller-provided device scratch: `workspace` (256-byte aligned,
+ * GEMM_ERR_ALIGN otherwise) of `workspace_bytes` >= gemm_plan_workspace_bytes(plan)
+ * (GEMM_ERR_WORKSPACE otherwise); NULL with 0 bytes behaves as gemm_run. The
+ * caller owns it; it must stay allocated until the run completes on `stream`, and
+ * runs that overlap in time (other streams) need separate workspaces. Its contents
+ * on entry do not matter: every byte a run reads back it has written first.
+ * This is the path of the plan's chosen configuration (split-K partial sums, or
+ * padded operand copies made into the workspace before the product).
+ */
+int gemm_run_ws(const gemm_plan* plan, const void* A, const void* B, const float* bias,
+                const void* resid, void* C, void* workspace, int64_t workspace_bytes,
+                void* stream);
 
 /*
  * Enqueue `batch` independent products C_b = epi(A_b x B_b), b = 0..batch-1, with
@@ -158,6 +194,13 @@ int gemm_run_strided_batched(const gemm_plan* plan, int64_t batch, const void* A
                              int64_t strideA, const void* B, int64_t strideB, const float* bias,
                              const void* resid, int64_t strideR, void* C, int64_t strideC,
                              void* stream);
+
+/* gemm_run_strided_batched with caller-provided scratch, as gemm_run_ws. */
+int gemm_run_strided_batched_ws(const gemm_plan* plan, int64_t batch, const void* A,
+                                int64_t strideA, const void* B, int64_t strideB,
+                                const float* bias, const void* resid, int64_t strideR, void* C,
+                                int64_t strideC, void* workspace, int64_t workspace_bytes,
+                                void* stream);
 
 /*
  * Row softmax between the two batched products of attention (tutorial page,
@@ -214,20 +257,23 @@ int gemm_attention_probs(const void* Q, const void* Kmat, int64_t batch, int64_t
                          int64_t D, int32_t dtype, int32_t k_layout, float scale, void* P,
                          int32_t p_dtype, void* stream);
 
-/* Release a plan and its workspace. NULL is ignored. The caller must make sure no
- * enqueued run of the plan is still pending on a stream. */
+/* Release a plan (host memory only). NULL is ignored. Runs already enqueued do not
+ * use the plan object and may still be pending. */
 void gemm_plan_destroy(gemm_plan* plan);
 
-/* The status of the last failing gemm_plan_create* call on this thread. */
+/* The status of the last failing gemm_plan_create* call on this thread (tutorial
+ * page, section 7: report every failure to the caller). */
 int gemm_last_error(void);
 
-/* A static English message for a status code (never NULL). */
+/* A static English message for a status code (never NULL; tutorial page, section 7). */
 const char* gemm_strerror(int status);
 
 /*
  * Write a one-line description of the plan (configuration name, tile, grid,
- * LDS bytes, split) into buf (always NUL-terminated when len > 0).
- * Returns the number of characters the full line needs, or a negative status.
+ * LDS bytes, split, workspace bytes) into buf (always NUL-terminated when
+ * len > 0): the configuration the shape-bucket choice made (DeepGEMM page,
+ * section 2.3), for logs and tuning. Returns the number of characters the full
+ * line needs, or a negative status.
  */
 int gemm_plan_describe(const gemm_plan* plan, char* buf, size_t len);
 

@@ -38,10 +38,17 @@ def sample_indices(M, N, count, seed):
     return rows, cols
 
 
-def run_gpu(plan, A, B, bias=None, resid=None):
+def nan_out(shape, out_dtype, dev="cuda"):
+    """An output buffer filled with NaN, so an element the kernel never writes fails the
+    comparison instead of passing on a stale value from an earlier run."""
+    return torch.full(shape, float("nan"), dtype=TORCH[out_dtype], device=dev)
+
+
+def run_gpu(plan, A, B, bias=None, resid=None, workspace=None):
     dev = torch.device("cuda")
-    out = plan.run(A.to(dev), B.to(dev), None if bias is None else bias.to(dev),
-                   None if resid is None else resid.to(dev))
+    out = nan_out((plan.M, plan.N), plan.out_dtype)
+    plan.run(A.to(dev), B.to(dev), None if bias is None else bias.to(dev),
+             None if resid is None else resid.to(dev), out=out, workspace=workspace)
     torch.cuda.synchronize()
     return out.cpu()
 

@@ -97,6 +97,8 @@ def test_attention_probs_argument_errors_without_device():
 
 def test_null_plan_rejected():
     assert g.lib.gemm_run(None, None, None, None, None, None, None) == -7
+    assert g.lib.gemm_run_ws(None, None, None, None, None, None, None, 0, None) == -7
+    assert g.lib.gemm_plan_workspace_bytes(None) == -7
     assert g.lib.gemm_plan_describe(None, None, 0) == -7
     g.lib.gemm_plan_destroy(None)  # no-op
 
