@@ -70,6 +70,9 @@ SIGNATURES = {
     "gemm_run_strided_batched_ws": (ctypes.c_int, [_VP, _I64, _VP, _I64, _VP, _I64, _VP, _VP,
                                                    _I64, _VP, _I64, _VP, _I64, _VP]),
     "gemm_plan_workspace_bytes": (_I64, [_VP]),
+    "gemm_run_noalloc": (ctypes.c_int, [_VP, _I64, _VP, _I64, _VP, _I64, _VP, _VP, _I64, _VP,
+                                        _I64, _VP]),
+    "gemm_noalloc_scratch_bytes": (_I64, []),
     "gemm_plan_destroy": (None, [_VP]),
     "gemm_softmax_rows": (ctypes.c_int, [_VP, _I64, _I64, _I64, ctypes.c_float, _VP, _I64, _I32,
                                          _VP]),

@@ -29,6 +29,19 @@
 
 using namespace g15;
 
+// Scratch held by the library for gemm_run_noalloc, one copy per GPU the library runs
+// on, kept until the process ends: kScratchBytes usable from a 256-byte boundary (the
+// array is 256 bytes longer, so the usable part starts at its first 256-byte boundary
+// whatever alignment the code object gives it). Host code never uses this name as an
+// address: the device address comes from hipGetSymbolAddress (scratch_address below).
+// The array has external linkage (in the library's namespace): the runtime finds a
+// registered device variable by name among the code object's global symbols, and an
+// internal-linkage (static) array is a local symbol there.
+constexpr int64_t kScratchBytes = int64_t(16) << 20;
+namespace g15 {
+__device__ __attribute__((used)) __align__(256) unsigned char scratch[kScratchBytes + 256];
+}  // namespace g15
+
 // A plan holds host state only: the choice of configuration and the sizes of the
 // scratch its runs use, which the caller passes in (gemm_run_ws).
 struct gemm_plan {
@@ -609,6 +622,25 @@ int run_split_k(const gemm_plan* p, const KernelEntry& k, int64_t batch, const v
   return GEMM_OK;
 }
 
+// Device address of the scratch array on `dev` (the current device), looked up once per
+// device with hipGetSymbolAddress and rounded up to a 256-byte boundary; nullptr when
+// the lookup fails.
+void* scratch_address(int dev) {
+  static std::mutex mu;
+  static std::map<int, void*> addr;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = addr.find(dev);
+  if (it != addr.end()) return it->second;
+  void* p = nullptr;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+    (void)hipGetLastError();
+    return nullptr;
+  }
+  const uintptr_t u = (reinterpret_cast<uintptr_t>(p) + 255) & ~uintptr_t(255);
+  addr[dev] = reinterpret_cast<void*>(u);
+  return addr[dev];
+}
+
 // One-line description of a plan (its configuration choice, for logs and tuning).
 int describe_plan(const gemm_plan* p, char* buf, size_t len) {
   const auto& all = registry().all;
@@ -910,6 +942,25 @@ int gemm_run(const gemm_plan* p, const void* A, const void* B, const float* bias
   if (!p) return GEMM_ERR_PLAN;
   return gemm_run_strided_batched_ws(p, 1, A, 0, B, 0, bias, resid, 0, C, 0, nullptr, 0, stream);
 }
+
+int gemm_run_noalloc(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, const void* B,
+                     int64_t sB, const float* bias, const void* resid, int64_t sR, void* C,
+                     int64_t sC, void* stream) {
+  if (!p) return GEMM_ERR_PLAN;
+  if (p->workspace_bytes == 0)
+    return gemm_run_strided_batched_ws(p, batch, A, sA, B, sB, bias, resid, sR, C, sC, nullptr, 0,
+                                       stream);
+  if (p->workspace_bytes > kScratchBytes) return GEMM_ERR_WORKSPACE;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
+  if (dev != p->device) return GEMM_ERR_PLAN;
+  void* ws = scratch_address(dev);
+  if (!ws) return GEMM_ERR_HIP;
+  return gemm_run_strided_batched_ws(p, batch, A, sA, B, sB, bias, resid, sR, C, sC, ws,
+                                     kScratchBytes, stream);
+}
+
+int64_t gemm_noalloc_scratch_bytes(void) { return kScratchBytes; }
 
 int64_t gemm_plan_workspace_bytes(const gemm_plan* p) {
   if (!p) return GEMM_ERR_PLAN;

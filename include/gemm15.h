@@ -195,6 +195,25 @@ int gemm_run_strided_batched(const gemm_plan* plan, int64_t batch, const void* A
                              const void* resid, int64_t strideR, void* C, int64_t strideC,
                              void* stream);
 
+/*
+ * For callers that cannot allocate memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): gemm_run_strided_batched with the
+ * plan's chosen configuration, its scratch taken from a fixed array the library
+ * holds on each GPU it runs on (gemm_noalloc_scratch_bytes() = 16 MiB, kept until
+ * the process ends) instead of a caller workspace. The call allocates nothing and
+ * calls no allocating routine. Every call on one GPU shares that GPU's array: calls
+ * that overlap in time (other streams) race and must not be issued. Nothing in it
+ * needs to start at zero (each run writes every byte it reads back). Same arguments
+ * and errors as gemm_run_strided_batched, plus GEMM_ERR_WORKSPACE when the plan needs
+ * more scratch than the array holds.
+ */
+int gemm_run_noalloc(const gemm_plan* plan, int64_t batch, const void* A, int64_t strideA,
+                     const void* B, int64_t strideB, const float* bias, const void* resid,
+                     int64_t strideR, void* C, int64_t strideC, void* stream);
+
+/* Bytes of the per-GPU scratch array gemm_run_noalloc uses. */
+int64_t gemm_noalloc_scratch_bytes(void);
+
 /* gemm_run_strided_batched with caller-provided scratch, as gemm_run_ws. */
 int gemm_run_strided_batched_ws(const gemm_plan* plan, int64_t batch, const void* A,
                                 int64_t strideA, const void* B, int64_t strideB,
