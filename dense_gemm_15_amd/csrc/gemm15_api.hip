@@ -75,8 +75,6 @@ struct Registry {
     all.insert(all.end(), p, p + n);
     n = mfma16_entries(&p);
     all.insert(all.end(), p, p + n);
-    n = mfma16_pipe_entries(&p);
-    all.insert(all.end(), p, p + n);
     n = mfma16_dlds_entries(&p);
     all.insert(all.end(), p, p + n);
     n = mfma16_nt_entries(&p);
@@ -142,9 +140,6 @@ const EffRow kEff[] = {
     {"m16n_bf16_128x128x64_w2x2_a2_b2", 0.86}, {"m16n_f16_128x128x64_w2x2_a2_b2", 0.86},
     {"m16n_bf16_128x128x64_w2x2_a3_b3", 0.85}, {"m16n_f16_128x128x64_w2x2_a3_b3", 0.85},
     {"m16n_bf16_64x128", 0.66}, {"m16n_f16_64x128", 0.66},
-    {"m16p_bf16_256x256x64_w2x2", 0.68}, {"m16p_f16_256x256x64_w2x2", 0.68},
-    {"m16p_bf16_256x256x64_w2x4", 0.62}, {"m16p_f16_256x256x64_w2x4", 0.62},
-    {"m16p_bf16_128x128", 0.48}, {"m16p_f16_128x128", 0.48},
     {"mfma16_bf16_128x128_w2x2_scalar", 0.10}, {"mfma16_f16_128x128_w2x2_scalar", 0.10},
     {"mfma16_bf16_64x64_w2x2_scalar", 0.08}, {"mfma16_f16_64x64_w2x2_scalar", 0.08},
     {"mfma16_bf16_128x128", 0.52}, {"mfma16_f16_128x128", 0.52},
@@ -662,6 +657,13 @@ int describe_plan(const gemm_plan* p, char* buf, size_t len) {
   return n;
 }
 
+// GEMM15_POISON set (and not "0"): every run first fills C with NaN (read per call, so a
+// test or a debugging session can switch it on at any time).
+bool poison_enabled() {
+  const char* s = std::getenv("GEMM15_POISON");
+  return s && *s && std::strcmp(s, "0") != 0;
+}
+
 // GEMM15_LOG set (and not "0"): every plan creation prints its choice to stderr.
 bool log_enabled() {
   static const bool on = [] {
@@ -860,6 +862,17 @@ int gemm_run_strided_batched_ws(const gemm_plan* p, int64_t batch, const void* A
   if (hipGetDevice(&dev) != hipSuccess) return GEMM_ERR_HIP;
   if (dev != p->device) return GEMM_ERR_PLAN;
   const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (poison_enabled()) {
+    // debug aid (GEMM15_POISON): C starts as NaN, unless the residual shares its memory
+    const char* c0 = static_cast<const char*>(C);
+    const char* r0 = static_cast<const char*>(resid);
+    const int64_t cspan = ((batch - 1) * sC + p->M * p->N) * static_cast<int64_t>(oe);
+    const int64_t rspan = ((batch - 1) * sR + p->M * p->N) * static_cast<int64_t>(oe);
+    const bool overlap = (e.flags & GEMM_EPI_RESID) && r0 < c0 + cspan && c0 < r0 + rspan;
+    if (!overlap && aligned_to(C, 4) && (p->N * oe) % 4 == 0 && (sC * oe) % 4 == 0 &&
+        poison_output(C, p->M, p->N, p->N, batch, sC, e.out_dtype, st) != hipSuccess)
+      return GEMM_ERR_HIP;
+  }
   // scratch for the plan's own configuration, or its workspace-free configuration
   const bool use_ws = p->workspace_bytes > 0 && ws != nullptr;
   const bool no_ws = p->workspace_bytes > 0 && !use_ws;

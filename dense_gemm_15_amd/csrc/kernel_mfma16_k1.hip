@@ -77,7 +77,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
     const int chk = (lane & 7) ^ (lane >> 3) ^ ((wave * AI + i) & 3);
     a_row[i] = (wave * AI + i) * 8 + (lane >> 3);
     a_koff[i] = static_cast<uint32_t>(chk * 8);
-    a_kin[i] = chk * 8 < K;  // K is a multiple of 8: a chunk is wholly inside K or past it
+    a_kin[i] = chk * 8 < K;  // a chunk is wholly inside K or past it: K is a multiple of 8,
+                             // or A arrives in rows zero-padded to one (the padded-copy mode)
   }
   // B given transposed (Bt [N x K], !BROW) loads like A: rows n, chunks of k.
   int b_row[BI], b_col[BI];

@@ -29,7 +29,37 @@ __global__ __launch_bounds__(256) void pack16_kernel(const uint16_t* __restrict_
   *reinterpret_cast<u32x4*>(dst + r * ld_dst + c0) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
+// Thread t writes one 4-byte word of NaN patterns (two 16-bit NaNs or one fp32 NaN)
+// into batch item blockIdx.y of C (rows x row_bytes bytes, row_bytes a multiple of 4,
+// row stride ld_bytes).
+__global__ __launch_bounds__(256) void poison_kernel(char* C, int64_t rows, int64_t row_bytes,
+                                                     int64_t ld_bytes, int64_t stride_bytes,
+                                                     uint32_t word) {
+  const int64_t words = row_bytes / 4;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= rows * words) return;
+  const int64_t r = t / words, w = t - r * words;
+  *reinterpret_cast<uint32_t*>(C + blockIdx.y * stride_bytes + r * ld_bytes + w * 4) = word;
+}
+
 }  // namespace
+
+hipError_t poison_output(void* C, int64_t rows, int64_t cols, int64_t ld, int64_t batch,
+                         int64_t stride, int out_dtype, hipStream_t s) {
+  const int64_t es = out_dtype == DT_F32 ? 4 : 2;
+  const uint16_t h = out_dtype == DT_BF16 ? 0x7FC0u : 0x7E00u;  // quiet NaNs
+  const uint32_t word = es == 4 ? 0x7FC00000u : (static_cast<uint32_t>(h) << 16) | h;
+  const int64_t row_bytes = cols * es;
+  if (reinterpret_cast<uintptr_t>(C) % 4 != 0 || row_bytes % 4 != 0 || (ld * es) % 4 != 0 ||
+      (stride * es) % 4 != 0 || batch > 65535)
+    return hipErrorInvalidValue;
+  const int64_t blocks = (rows * (row_bytes / 4) + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(poison_kernel, dim3(static_cast<unsigned>(blocks), static_cast<unsigned>(batch)),
+                     dim3(256), 0, s, static_cast<char*>(C), rows, row_bytes, ld * es, stride * es,
+                     word);
+  return hipGetLastError();
+}
 
 hipError_t pack_rows16(const void* src, int64_t rows, int64_t cols, void* dst, int64_t ld_dst,
                        hipStream_t s) {

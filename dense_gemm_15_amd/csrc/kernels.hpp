@@ -46,6 +46,13 @@ struct LaunchArgs {
 hipError_t pack_rows16(const void* src, int64_t rows, int64_t cols, void* dst, int64_t ld_dst,
                        hipStream_t s);
 
+// Debug aid: fill `batch` items of a rows x cols output (row stride ld, batch stride
+// `stride`, both in elements of out_dtype) with NaN, so elements a kernel leaves
+// unwritten show. Needs C, row lengths, row and batch strides in 4-byte multiples
+// (else hipErrorInvalidValue, nothing launched).
+hipError_t poison_output(void* C, int64_t rows, int64_t cols, int64_t ld, int64_t batch,
+                         int64_t stride, int out_dtype, hipStream_t s);
+
 typedef hipError_t (*LaunchFn)(const LaunchArgs&, hipStream_t);
 
 struct KernelEntry {
@@ -65,7 +72,6 @@ struct KernelEntry {
 // Each kernel file appends its instantiations.
 int simple_entries(const KernelEntry** out);
 int mfma16_entries(const KernelEntry** out);
-int mfma16_pipe_entries(const KernelEntry** out);
 int mfma16_dlds_entries(const KernelEntry** out);
 int mfma16_nt_entries(const KernelEntry** out);
 int f32_entries(const KernelEntry** out);

@@ -37,10 +37,16 @@
  *    record the code for gemm_last_error(). No call aborts the process; launch
  *    failures are read back with hipGetLastError (tutorial page, section 7: check
  *    the error state after every launch).
- *  - Plans hold host state only: no call allocates device memory except through
- *    a workspace the caller passes in. A plan is immutable after creation and may
- *    be run concurrently from several host threads and streams; runs that use a
+ *  - Plans hold host state only; no call allocates device memory (scratch comes
+ *    from a workspace the caller passes in). A plan is immutable after creation and
+ *    may be run concurrently from several host threads and streams; runs that use a
  *    workspace need one workspace each while they overlap.
+ *  - Debug aids read from the environment: GEMM15_LOG=1 prints each plan's
+ *    configuration choice to stderr; GEMM15_POISON=1 makes every run fill C with NaN
+ *    first (C with 4-byte aligned rows, and not when the residual shares C's memory),
+ *    so elements a kernel leaves unwritten show (tutorial page, section 7: NaN
+ *    results from unwritten or unsynchronised memory); GEMM15_FORCE_CONFIG=<name>
+ *    forces one configuration for every plan.
  */
 #ifndef GEMM15_H
 #define GEMM15_H

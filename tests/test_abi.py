@@ -145,9 +145,10 @@ def test_select_fits_budget_and_type(dtype, shape):
         # inputs) a 16-byte-load kernel on copies of exactly those operands in padded rows
         if ch.packed:
             # padded rows take the one-tile-per-workgroup kernel, or the streaming one
-            # when the padded K is one 64-deep slice and C is large
-            assert dtype != "f32" and (name.startswith("m16d") or
-                                       (name.startswith("m16s") and (K + 7) // 8 * 8 <= 64))
+            # exactly when the padded K is one 64-deep slice and C has at least 4M elements
+            streaming = (K + 7) // 8 * 8 <= 64 and M * N >= 1 << 22
+            assert dtype != "f32"
+            assert name.startswith("m16s_") if streaming else name.startswith("m16d"), name
             assert ch.packed == (1 if pa else 0) | (2 if pb else 0)
         else:
             assert "scalar" in name or name.startswith("simple")
@@ -185,7 +186,7 @@ def test_select_keeps_slice_offsets_32bit():
     64-bit kernels, one row shorter stays on the fast ones; the few-row kernels
     address B from its start and keep any width under the 2 GiB total."""
     wide = g.select(16, 1 << 24, 16, "bf16", **MI355X)
-    assert not g.config_names()[wide.config].startswith(("m16d", "m16t", "m16n", "m16p", "f32d"))
+    assert not g.config_names()[wide.config].startswith(("m16d", "m16t", "m16n", "m16w", "f32d"))
     fits = g.select(16, (1 << 24) - 8, 16, "bf16", **MI355X)
     assert g.config_names()[fits.config].startswith("m16d")
     few = g.select(1, 1 << 24, 16, "bf16", **MI355X)

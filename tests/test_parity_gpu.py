@@ -557,7 +557,7 @@ def test_operands_past_2gib(g):
     B = synth.uniform(952, (K, N), "bf16")
     plan = g.Plan(M, N, K, "bf16")
     say(f"[2GiB A] {plan.describe()}")
-    assert not plan.config_name.startswith(("m16d", "m16n", "m16t", "m16p", "f32d", "gemv"))
+    assert not plan.config_name.startswith(("m16d", "m16n", "m16t", "m16w", "f32d", "gemv"))
     C = plan.run(A, B.to(dev))
     torch.cuda.synchronize()
     rows = np.concatenate([rng.integers(0, M, 24), [M - 2, M - 1]])
@@ -817,3 +817,62 @@ def test_workspace_two_streams(g):
     for (pi, si, A, B, bias, resid, dA, dB, db, dr, C) in jobs:
         r = gc.check_full(C.cpu(), A, B, "bf16", "bf16", bias, resid)
         assert r["ok"], (pi, si, r)
+
+
+M16S_PACKED = [
+    # (M, N, K, out_dtype, epilogue, packed bits): padded K within one slice and a large C
+    (4099, 2048, 57, "bf16", dict(bias=True, resid=True), 1),   # A padded, 16-bit C, residual
+    (4099, 2050, 57, "bf16", dict(bias=True, gelu=True), 3),    # both padded, even N not % 8
+    (4100, 2051, 60, "f32", dict(scale=0.5), 3),                # both padded, odd N, fp32 C
+]
+
+
+@pytest.mark.parametrize("case", range(len(M16S_PACKED)))
+def test_packed_streaming_kernel(g, case):
+    """Padded copies feeding the one-slice streaming kernel (the padded K is one 64-deep
+    slice and C is large): bf16 inputs, 16-bit and fp32 C, every epilogue stage, A only
+    or both operands padded; the configuration is asserted. Every element."""
+    M, N, K, od, epi, bits = M16S_PACKED[case]
+    plan = g.Plan(M, N, K, "bf16", out_dtype=od, **epi)
+    d = _describe(plan)
+    say(f"[m16s packed] {plan.describe()}")
+    assert d["config"] == "m16s_bf16_256x128x64_w4x2" and int(d["packed"]) == bits
+    A, B = gc.inputs(M, N, K, "bf16", 1900 + case)
+    bias = synth.normal(1910 + case, (N,), 0.5, "f32") if epi.get("bias") else None
+    resid = synth.uniform(1920 + case, (M, N), od) if epi.get("resid") else None
+    C = gc.run_gpu(plan, A, B, bias, resid)
+    r = gc.check_full(C, A, B, "bf16", od, bias, resid, epi.get("scale"), epi.get("gelu", False))
+    assert r["ok"], r
+
+
+def test_poison_mode(g, monkeypatch):
+    """GEMM15_POISON: every run first fills C with NaN (a debug aid for unwritten
+    elements). Tile, split-K, few-row, padded-copy, streaming and batched runs with it on
+    still produce every element, against the oracle; C starts as zeros here, so an
+    element left as NaN can only come from the poison fill."""
+    monkeypatch.setenv("GEMM15_POISON", "1")
+    dev = torch.device("cuda")
+    cases = [(300, 264, 200, "bf16", dict(bias=True, out_dtype="bf16")),
+             (256, 256, 4096, "f16", dict()),
+             (3, 1000, 3000, "bf16", dict(bias=True)),
+             (300, 264, 203, "f16", dict(out_dtype="f16")),
+             (4099, 2048, 57, "bf16", dict(out_dtype="f32"))]
+    for ci, (M, N, K, dt, epi) in enumerate(cases):
+        plan = g.Plan(M, N, K, dt, **epi)
+        od = epi.get("out_dtype", "f32")
+        A, B = gc.inputs(M, N, K, dt, 2000 + ci)
+        bias = synth.normal(2010 + ci, (N,), 0.5, "f32") if epi.get("bias") else None
+        C = torch.zeros((M, N), dtype=gc.TORCH[od], device=dev)
+        plan.run(A.to(dev), B.to(dev), None if bias is None else bias.to(dev), out=C)
+        torch.cuda.synchronize()
+        r = gc.check_full(C.cpu(), A, B, dt, od, bias)
+        assert r["ok"], (plan.describe(), r)
+    Q, Kt = synth.qk_inputs()
+    Q, Kt = Q[:5], Kt[:5]
+    plan = g.Plan(512, 512, 64, "bf16", batch_hint=5)
+    S = torch.zeros((5, 512, 512), device=dev)
+    plan.run_batched(Q.to(dev), Kt.to(dev), out=S)
+    torch.cuda.synchronize()
+    for b in range(5):
+        r = gc.check_full(S[b].cpu(), Q[b], Kt[b], "bf16")
+        assert r["ok"], (b, r)
