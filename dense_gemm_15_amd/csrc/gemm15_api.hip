@@ -389,11 +389,25 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
   }
   double cost = 0;
   s.config = best_for(vec_a, vec_b, K, N, any, &cost);
-  // 16-bit rows that are not 16-byte multiples: rather than a scalar-load kernel,
-  // copy the offending operand into zero-padded rows (plan workspace) and run a
-  // 16-byte-load kernel, when the product is big enough to repay the copy (always
-  // for a transposed B, which has no scalar-load kernel).
   const bool pa = (K * es) % 16 != 0, pb = ((b_nk ? K : N) * es) % 16 != 0;
+  // 16-bit rows that are not 16-byte multiples, K within one 64-deep slice and a
+  // large C: the streaming kernel's register-load form reads the rows as they are
+  // (no padded copies, no workspace) while C of the previous tile leaves.
+  if (dtype != GEMM_F32 && aligned16 && (pa || pb) && K <= 64 &&
+      static_cast<double>(M) * N >= double(1 << 22)) {
+    const std::string want = std::string("m16s_") + (dtype == GEMM_BF16 ? "bf16" : "f16") +
+                             "_256x128x64_w4x2" + (b_nk ? "_nk" : "") + "_u";
+    for (size_t i = 0; i < all.size(); ++i)
+      if (want == all[i].name &&
+          cfg_fits(all[i], dtype, vec_a, vec_b, dev, M, N, K, epi.out_dtype, b_nk)) {
+        s.config = static_cast<int>(i);
+        return s;
+      }
+  }
+  // Other 16-bit rows that are not 16-byte multiples: rather than a scalar-load
+  // kernel, copy the offending operand into zero-padded rows (plan workspace) and run
+  // a 16-byte-load kernel, when the product is big enough to repay the copy (always
+  // for a transposed B, which has no scalar-load kernel).
   if (dtype != GEMM_F32 && aligned16 && (pa || pb) &&
       (b_nk || (M > 8 && static_cast<double>(M) * N * K >= double(1 << 20)))) {
     double pcost = 0;
@@ -402,19 +416,6 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
     if (pk >= 0 && (s.config < 0 || pcost < cost)) {
       s.config = pk;
       s.packed = (pa ? 1 : 0) | (pb ? 2 : 0);
-      // padded K within one 64-deep slice and a large C: the streaming kernel, whose
-      // workgroups keep the next tile's operands loading while C of this one leaves
-      if (!b_nk && round_up8(K) <= 64 && static_cast<double>(M) * N >= double(1 << 22)) {
-        const std::string want = std::string("m16s_") + (dtype == GEMM_BF16 ? "bf16" : "f16") +
-                                 "_256x128x64_w4x2";
-        for (size_t i = 0; i < all.size(); ++i)
-          if (want == all[i].name && cfg_fits(all[i], dtype, true, true, dev, M,
-                                              (pb ? round_up8(N) : N), round_up8(K),
-                                              epi.out_dtype, false)) {
-            s.config = static_cast<int>(i);
-            break;
-          }
-      }
     }
   }
   return s;
@@ -891,8 +892,14 @@ int gemm_run_strided_batched_ws(const gemm_plan* p, int64_t batch, const void* A
     const bool b_ok = (p->packed & 2) || (aligned_to(B, 16) && (sB * ie) % 16 == 0);
     if (a_ok && b_ok) return run_packed(p, batch, A, sA, B, sB, bias, resid, sR, C, sC, c16, ws, st);
   }
+  // The register-load streaming form reads A and B at any 2-byte alignment and any
+  // batch stride; it stores C (and reads the residual) in 4- or 2-byte units.
+  const KernelEntry& kp = all[p->config];
+  const bool c4 = aligned_to(C, 4) && (sC * oe) % 4 == 0 &&
+                  (!(e.flags & GEMM_EPI_RESID) || (aligned_to(resid, 4) && (sR * oe) % 4 == 0));
   int ci = p->fallback;
-  if (a16 && !p->packed) ci = no_ws ? p->nows : p->config;
+  if (!p->packed && kp.kind == KIND_K1 && !kp.vec_a && !kp.vec_b && c4) ci = p->config;
+  else if (a16 && !p->packed) ci = no_ws ? p->nows : p->config;
   else if (a16 && no_ws) ci = p->nows;
   if (ci < 0) return GEMM_ERR_ALIGN;  // transposed B: 16-byte aligned operands required
   const KernelEntry& k = all[ci];

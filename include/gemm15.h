@@ -108,7 +108,11 @@ typedef struct gemm_plan gemm_plan;
  * device memory. A configuration that splits K (fp32 partial sums), or that
  * copies 16-bit operands whose rows are not 16-byte multiples (K or N not a
  * multiple of 8) into zero-padded rows, needs device scratch that the caller
- * passes to gemm_run_ws (size from gemm_plan_workspace_bytes).
+ * passes to gemm_run_ws (size from gemm_plan_workspace_bytes). Rows that are not
+ * 16-byte multiples with K <= 64 and M x N >= 2^22 need no copies: the one-slice
+ * streaming kernel then reads them through registers (the "_u" configurations,
+ * which take A and B at any element alignment and batch stride, with C and the
+ * residual 4-byte aligned).
  * Returns NULL on error (see gemm_last_error()).
  */
 gemm_plan* gemm_plan_create(int64_t M, int64_t N, int64_t K, int32_t dtype,

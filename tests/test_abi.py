@@ -143,12 +143,13 @@ def test_select_fits_budget_and_type(dtype, shape):
     if pa or pb:
         # rows that are not 16-byte multiples take a scalar-load kernel, or (16-bit
         # inputs) a 16-byte-load kernel on copies of exactly those operands in padded rows
-        if ch.packed:
-            # padded rows take the one-tile-per-workgroup kernel, or the streaming one
-            # exactly when the padded K is one 64-deep slice and C has at least 4M elements
-            streaming = (K + 7) // 8 * 8 <= 64 and M * N >= 1 << 22
+        if dtype != "f32" and K <= 64 and M * N >= 1 << 22:
+            # K within one 64-deep slice and a large C: the streaming kernel's
+            # register-load form, which reads the rows as they are
+            assert name == f"m16s_{dtype}_256x128x64_w4x2_u" and ch.packed == 0, name
+        elif ch.packed:
             assert dtype != "f32"
-            assert name.startswith("m16s_") if streaming else name.startswith("m16d"), name
+            assert name.startswith("m16d"), name
             assert ch.packed == (1 if pa else 0) | (2 if pb else 0)
         else:
             assert "scalar" in name or name.startswith("simple")

@@ -52,8 +52,13 @@ def _dtype(name):
 
 
 def _nk(name):
-    """Configurations for B given transposed (Bt [N x K]) end in _nk."""
-    return name.endswith("_nk")
+    """Configurations for B given transposed (Bt [N x K]) carry _nk."""
+    return "_nk" in name
+
+
+def _unaligned(name):
+    """The register-load forms (_u) take rows of any 2-byte alignment."""
+    return name.endswith("_u")
 
 
 def _plan(g, name, M, N, K, **kw):
@@ -158,6 +163,86 @@ def test_k1_attention_scores(g):
                 ii, jj = rng.integers(0, S, 64), rng.integers(0, S, 64)
                 r = gc.check_sampled(out[b], Q[b], Kt[b], "bf16", ii, jj)
             assert r["ok"], (name, b, r)
+
+
+UNALIGNED = [
+    # (M, N, K): K and N not multiples of 8 (rows of odd element counts; the last
+    # chunk of a row holds 1 to 7 elements, each count at least once for K and N),
+    # thin last tile column and row, K below 8 (element loads), K of one element, a
+    # product smaller than one tile
+    (517, 261, 63),
+    (300, 1001, 57),
+    (1029, 387, 7),
+    (260, 130, 1),
+    (37, 19, 33),
+    (300, 1020, 46),
+    (70, 1022, 12),
+]
+
+
+@pytest.mark.parametrize("name", [c for c in K1 if _unaligned(c)])
+def test_k1_unaligned_rows(g, name):
+    """The register-load form on rows that are not 16-byte multiples (odd K, odd N,
+    both), with thin last tile strips, float and small-integer inputs, fp32 C and an
+    epilogue into 16-bit C: every element against the oracle."""
+    dtype = _dtype(name)
+    for si, (M, N, K) in enumerate(UNALIGNED):
+        for kind in ("uniform", "int"):
+            say(f"[{name}] M={M} N={N} K={K} {kind}")
+            plan = _plan(g, name, M, N, K)
+            assert plan.config_name == name
+            A, B = gc.inputs(M, N, K, dtype, 1800 + 7 * si, kind)
+            C = gc.run_gpu(plan, A, _given(name, B))
+            r = gc.check_full(C, A, B, dtype, exact=(kind == "int"))
+            assert r["ok"], (name, M, N, K, kind, r)
+        epi = dict(out_dtype=dtype, bias=True, gelu=True, resid=True)
+        plan = _plan(g, name, M, N, K, **epi)
+        A, B = gc.inputs(M, N, K, dtype, 1850 + si)
+        bias = synth.normal(1860 + si, (N,), 0.5, "f32")
+        resid = synth.normal(1870 + si, (M, N), 1.0, dtype)
+        C = gc.run_gpu(plan, A, _given(name, B), bias, resid)
+        r = gc.check_full(C, A, B, dtype, dtype, bias, resid, None, True)
+        assert r["ok"], (name, M, N, K, "epilogue", r)
+
+
+@pytest.mark.parametrize("nk", [False, True])
+def test_k1_unaligned_selected(g, nk):
+    """4095 x 4097 x 63 (fp16, the odd-shape benchmark product) is planned on the
+    register-load streaming kernel without copies or workspace; a batch of unaligned
+    products and an operand off a 16-byte boundary inside a larger buffer run on the
+    same configuration. Every element of the big product against the oracle."""
+    M, N, K = 4095, 4097, 63
+    plan = g.Plan(M, N, K, "f16", b_layout="nk" if nk else "kn")
+    want = "m16s_f16_256x128x64_w4x2" + ("_nk" if nk else "") + "_u"
+    say(f"[unaligned] {plan.describe()}")
+    assert plan.config_name == want and plan.workspace_bytes == 0
+    A, B = gc.inputs(M, N, K, "f16", 1880 + nk)
+    Bg = B.t().contiguous() if nk else B
+    C = gc.run_gpu(plan, A, Bg)
+    r = gc.check_full(C, A, B, "f16")
+    assert r["ok"], r
+    # A two bytes past a 16-byte boundary: the same kernel, the same bits
+    dev = torch.device("cuda")
+    buf = torch.empty(M * K + 1, dtype=torch.float16, device=dev)
+    Av = buf[1:].view(M, K)
+    Av.copy_(A.to(dev))
+    assert Av.data_ptr() % 16 == 2
+    C2 = plan.run(Av, Bg.to(dev), out=torch.full((M, N), float("nan"), device=dev))
+    torch.cuda.synchronize()
+    assert torch.equal(C2.cpu().view(torch.int32), C.view(torch.int32))
+    # a batch of 2 items with strides of odd element counts
+    nb, M, N, K = 2, 2100, 2003, 45
+    plan = g.Plan(M, N, K, "bf16", batch_hint=nb, b_layout="nk" if nk else "kn")
+    assert plan.config_name == "m16s_bf16_256x128x64_w4x2" + ("_nk" if nk else "") + "_u"
+    A = synth.uniform(1890, (nb, M, K), "bf16")
+    B = synth.uniform(1891, (nb, K, N), "bf16")
+    dev = torch.device("cuda")
+    out = plan.run_batched(A.to(dev), (B.transpose(1, 2).contiguous() if nk else B).to(dev))
+    torch.cuda.synchronize()
+    out = out.cpu()
+    for b in range(nb):
+        r = gc.check_full(out[b], A[b], B[b], "bf16")
+        assert r["ok"], (nk, b, r)
 
 
 def test_k1_needs_one_slice(g):

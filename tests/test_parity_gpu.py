@@ -819,24 +819,26 @@ def test_workspace_two_streams(g):
         assert r["ok"], (pi, si, r)
 
 
-M16S_PACKED = [
-    # (M, N, K, out_dtype, epilogue, packed bits): padded K within one slice and a large C
-    (4099, 2048, 57, "bf16", dict(bias=True, resid=True), 1),   # A padded, 16-bit C, residual
-    (4099, 2050, 57, "bf16", dict(bias=True, gelu=True), 3),    # both padded, even N not % 8
-    (4100, 2051, 60, "f32", dict(scale=0.5), 3),                # both padded, odd N, fp32 C
+M16S_UNALIGNED = [
+    # (M, N, K, out_dtype, epilogue): K within one slice, rows not 16-byte multiples, large C
+    (4099, 2048, 57, "bf16", dict(bias=True, resid=True)),   # A rows unaligned, 16-bit C
+    (4099, 2050, 57, "bf16", dict(bias=True, gelu=True)),    # both, even N not % 8
+    (4100, 2051, 60, "f32", dict(scale=0.5)),                # both, odd N, fp32 C
 ]
 
 
-@pytest.mark.parametrize("case", range(len(M16S_PACKED)))
-def test_packed_streaming_kernel(g, case):
-    """Padded copies feeding the one-slice streaming kernel (the padded K is one 64-deep
-    slice and C is large): bf16 inputs, 16-bit and fp32 C, every epilogue stage, A only
-    or both operands padded; the configuration is asserted. Every element."""
-    M, N, K, od, epi, bits = M16S_PACKED[case]
+@pytest.mark.parametrize("case", range(len(M16S_UNALIGNED)))
+def test_unaligned_streaming_kernel(g, case):
+    """Rows that are not 16-byte multiples with K within one 64-deep slice and a large
+    C: the streaming kernel's register-load form, no copies and no workspace (the
+    configuration is asserted); bf16 inputs, 16-bit and fp32 C, every epilogue stage.
+    Every element."""
+    M, N, K, od, epi = M16S_UNALIGNED[case]
     plan = g.Plan(M, N, K, "bf16", out_dtype=od, **epi)
     d = _describe(plan)
-    say(f"[m16s packed] {plan.describe()}")
-    assert d["config"] == "m16s_bf16_256x128x64_w4x2" and int(d["packed"]) == bits
+    say(f"[m16s unaligned] {plan.describe()}")
+    assert d["config"] == "m16s_bf16_256x128x64_w4x2_u" and int(d["packed"]) == 0
+    assert plan.workspace_bytes == 0
     A, B = gc.inputs(M, N, K, "bf16", 1900 + case)
     bias = synth.normal(1910 + case, (N,), 0.5, "f32") if epi.get("bias") else None
     resid = synth.uniform(1920 + case, (M, N), od) if epi.get("resid") else None
