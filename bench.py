@@ -572,10 +572,12 @@ def symbol_to_config(sym: str):
         t, bm, bn, wm, wn, sa, sb, brow = m.groups()
         kind = "m16t" if brow == "true" else "m16n"
         return f"{kind}_{t}_{bm}x{bn}x64_w{wm}x{wn}_a{sa}_b{sb}"
-    m = re.search(r"gemm_m16s_kernel<g15::(\w+)_t, (\d+), (\d+), (\d+), (\d+)>", sym)
+    m = re.search(r"gemm_m16s_kernel<g15::(\w+)_t, (\d+), (\d+), (\d+), (\d+)"
+                  r"(?:, (true|false))?(?:, (true|false))?>", sym)
     if m:
-        t, bm, bn, wm, wn = m.groups()
-        return f"m16s_{t}_{bm}x{bn}x64_w{wm}x{wn}"
+        t, bm, bn, wm, wn, brow, un = m.groups()
+        return (f"m16s_{t}_{bm}x{bn}x64_w{wm}x{wn}" + ("_nk" if brow == "false" else "")
+                + ("_u" if un == "true" else ""))
     m = re.search(r"gemm_f32d_kernel<(\d+), (\d+), (\d+), (\d+), (\d+)>", sym)
     if m:
         bm, bn, wm, wn, sa = m.groups()

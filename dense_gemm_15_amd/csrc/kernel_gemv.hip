@@ -17,8 +17,11 @@
 // (partials written and read back with agent-scope atomic stores and loads, which
 // go through to memory, and an agent-scope counter) it is still slower, 12.5
 // against 8.7 us in a graph: the last workgroup of a strip waits for its stores to
-// reach memory, the counter's round trip and the partials' reads in turn. Accumulation is
-// fp32; the result does not depend on timing (fixed summation order).
+// reach memory, the counter's round trip and the partials' reads in turn. No split at
+// all (one workgroup per strip of 16, 32 or 64 columns over all of K, strips sharing
+// cache lines on one XCD) measured 15-23 us at 1 x 4096 x 4096: too few workgroups,
+// each walking all of K. Accumulation is fp32; the result does not depend on timing
+// (fixed summation order).
 #include "kernels.hpp"
 #include "splitk.hpp"
 

@@ -22,8 +22,10 @@ def test_symbol_to_config():
              "(g15::LaunchArgs)") == "f32d_256x256x16_w4x2_a3"
     assert s("void g15::(anonymous namespace)::gemv_kernel<g15::f16_t, 1, 4096, 8>"
              "(g15::LaunchArgs, long)") == "gemv_f16_m1"
-    assert s("void g15::(anonymous namespace)::gemm_m16s_kernel<g15::bf16_t, 128, 128, 2, 2>"
-             "(g15::LaunchArgs)") == "m16s_bf16_128x128x64_w2x2"
+    assert s("void g15::(anonymous namespace)::gemm_m16s_kernel<g15::bf16_t, 128, 128, 2, 2, true,"
+             " false>(g15::LaunchArgs)") == "m16s_bf16_128x128x64_w2x2"
+    assert s("void g15::(anonymous namespace)::gemm_m16s_kernel<g15::f16_t, 256, 128, 4, 2, false,"
+             " true>(g15::LaunchArgs)") == "m16s_f16_256x128x64_w4x2_nk_u"
     assert s("__amd_rocclr_copyBuffer") is None
 
 
