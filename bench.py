@@ -578,10 +578,10 @@ def symbol_to_config(sym: str):
         t, bm, bn, wm, wn, brow, un = m.groups()
         return (f"m16s_{t}_{bm}x{bn}x64_w{wm}x{wn}" + ("_nk" if brow == "false" else "")
                 + ("_u" if un == "true" else ""))
-    m = re.search(r"gemm_f32d_kernel<(\d+), (\d+), (\d+), (\d+), (\d+)>", sym)
+    m = re.search(r"gemm_f32d_kernel<(\d+), (\d+), (\d+), (\d+), (\d+)(?:, (true|false))?>", sym)
     if m:
-        bm, bn, wm, wn, sa = m.groups()
-        return f"f32d_{bm}x{bn}x16_w{wm}x{wn}_a{sa}"
+        bm, bn, wm, wn, sa, bnk = m.groups()
+        return f"f32d_{bm}x{bn}x16_w{wm}x{wn}_a{sa}" + ("_nk" if bnk == "true" else "")
     m = re.search(r"gemv_kernel<g15::(\w+)_t, (\d+), (\d+), (\d+)>", sym)
     if m:
         return f"gemv_{m.group(1)}_m{m.group(2)}"
@@ -620,7 +620,9 @@ def summarize(db_dir: str, kind: str) -> None:
     if os.path.exists(TRAFFIC_FILE):
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
-    copy = {cn: sum(v) / len(v) for (name, cn), v in acc.items()
+    # the calibration copies are the largest device copies of the run (inputs copied
+    # from the host are smaller and read host memory)
+    copy = {cn: max(v) for (name, cn), v in acc.items()
             if "copyBuffer" in name and cn in ("FETCH_SIZE", "WRITE_SIZE")}
     for cn, kib in copy.items():
         t.setdefault("scale", {})[cn] = 262144.0 / kib

@@ -171,7 +171,7 @@ const TunedRow kTuned[] = {
     {false, 1024, 1024, 1024, 1, "m16d_{t}_64x128x64_w2x2_a4_b4_r2"},
     {false, 512, 512, 512, 1, "m16d_{t}_64x128x64_w2x2_a4_b4_r2"},
     {false, 8192, 3072, 768, 1, "m16t_{t}_128x128x64_w2x2_a2_b2"},     // encoder FFN, first GEMM
-    {false, 8192, 768, 3072, 1, "m16d_{t}_128x256x64_w2x4_a3_b4_r1"},  // encoder FFN, second GEMM
+    {false, 8192, 768, 3072, 1, "m16t_{t}_128x256x64_w2x4_a3_b3"},  // encoder FFN, second GEMM
     {false, 512, 512, 64, 96, "m16s_{t}_256x128x64_w4x2"},             // 96 heads of Q K^T
     {false, 4096, 4096, 4096, 1, "m16n_{t}_256x256x64_w2x4_a3_b2"},
     {false, 2048, 2048, 2048, 1, "m16n_{t}_128x128x64_w2x2_a3_b3"},
@@ -307,7 +307,13 @@ struct Selection {
   int tile = -1;  // best tile configuration that needs no workspace, for aligned pointers
 };
 
-int64_t round_up8(int64_t x) { return (x + 7) / 8 * 8; }
+// x rounded up to whole 16-byte chunks of es-byte elements
+int64_t round_up16B(int64_t x, int64_t es) {
+  const int64_t q = 16 / es;
+  return (x + q - 1) / q * q;
+}
+
+bool is_f32d(const KernelEntry& k) { return std::strncmp(k.name, "f32d_", 5) == 0; }
 
 bool is_m16d(const KernelEntry& k) { return std::strncmp(k.name, "m16d_", 5) == 0; }
 
@@ -404,15 +410,22 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
         return s;
       }
   }
-  // Other 16-bit rows that are not 16-byte multiples: rather than a scalar-load
-  // kernel, copy the offending operand into zero-padded rows (plan workspace) and run
-  // a 16-byte-load kernel, when the product is big enough to repay the copy (always
-  // for a transposed B, which has no scalar-load kernel).
-  if (dtype != GEMM_F32 && aligned16 && (pa || pb) &&
-      (b_nk || (M > 8 && static_cast<double>(M) * N * K >= double(1 << 20)))) {
+  // Other rows that are not 16-byte multiples: rather than a scalar-load kernel,
+  // copy the offending operand into zero-padded rows (plan workspace) and run a
+  // 16-byte-load kernel, when the product is big enough to repay the copy (always for
+  // a transposed B, which has no scalar-load kernel; fp32 from 2^27 multiply-adds,
+  // where the copies cost a few percent of the product and f32d runs 1.6-1.8x the
+  // scalar-load kernel).
+  const double mnk = static_cast<double>(M) * N * K;
+  const bool repays = M > 8 && mnk >= (dtype == GEMM_F32 ? double(1 << 27) : double(1 << 20));
+  if (aligned16 && (pa || pb) && (b_nk || repays)) {
     double pcost = 0;
-    const int pk = best_for(true, true, pa ? round_up8(K) : K, (pb && !b_nk) ? round_up8(N) : N,
-                            [&](const KernelEntry& k) { return b_nk || is_m16d(k); }, &pcost);
+    const int pk = best_for(true, true, pa ? round_up16B(K, es) : K,
+                            (pb && !b_nk) ? round_up16B(N, es) : N,
+                            [&](const KernelEntry& k) {
+                              return dtype == GEMM_F32 ? is_f32d(k) : (b_nk || is_m16d(k));
+                            },
+                            &pcost);
     if (pk >= 0 && (s.config < 0 || pcost < cost)) {
       s.config = pk;
       s.packed = (pa ? 1 : 0) | (pb ? 2 : 0);
@@ -524,10 +537,11 @@ int run_packed(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, con
   for (int64_t z = 0; z < batch; ++z) {
     const char* Az = static_cast<const char*>(A) + z * sA * ie;
     const char* Bz = static_cast<const char*>(B) + z * sB * ie;
-    if ((p->packed & 1) && pack_rows16(Az, p->M, p->K, pack_a, p->lda_p, s) != hipSuccess)
+    auto pack = p->dtype == GEMM_F32 ? pack_rows32 : pack_rows16;
+    if ((p->packed & 1) && pack(Az, p->M, p->K, pack_a, p->lda_p, s) != hipSuccess)
       return GEMM_ERR_HIP;
-    if ((p->packed & 2) && pack_rows16(Bz, p->b_nk ? p->N : p->K, p->b_nk ? p->K : p->N, pack_b,
-                                       p->ldb_p, s) != hipSuccess)
+    if ((p->packed & 2) && pack(Bz, p->b_nk ? p->N : p->K, p->b_nk ? p->K : p->N, pack_b,
+                                p->ldb_p, s) != hipSuccess)
       return GEMM_ERR_HIP;
     LaunchArgs la;
     la.M = p->M;
@@ -686,7 +700,6 @@ gemm_plan* gemm_plan_create_layout(int64_t M, int64_t N, int64_t K, int32_t dtyp
   if (rc) return fail(rc);
   if (b_layout != GEMM_B_KN && b_layout != GEMM_B_NK) return fail(GEMM_ERR_ARG);
   const bool b_nk = b_layout == GEMM_B_NK;
-  if (b_nk && dtype == GEMM_F32) return fail(GEMM_ERR_DTYPE);
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev < 1) return fail(GEMM_ERR_NO_DEVICE);
   int dev = 0;
@@ -732,11 +745,12 @@ gemm_plan* gemm_plan_create_layout(int64_t M, int64_t N, int64_t K, int32_t dtyp
   p->split = 1;
   p->b_nk = b_nk ? 1 : 0;
   p->packed = sel.packed;
-  p->lda_p = (sel.packed & 1) ? round_up8(K) : K;
-  p->ldb_p = b_nk ? ((sel.packed & 2) ? round_up8(K) : K) : ((sel.packed & 2) ? round_up8(N) : N);
+  const int64_t es = elem_bytes(dtype);
+  p->lda_p = (sel.packed & 1) ? round_up16B(K, es) : K;
+  p->ldb_p = b_nk ? ((sel.packed & 2) ? round_up16B(K, es) : K)
+                  : ((sel.packed & 2) ? round_up16B(N, es) : N);
   p->pack_b_off = 0;
   if (sel.packed) {
-    const int64_t es = elem_bytes(dtype);
     const int64_t a_bytes = (sel.packed & 1) ? M * p->lda_p * es : 0;
     const int64_t b_bytes = (sel.packed & 2) ? (b_nk ? N : K) * p->ldb_p * es : 0;
     p->pack_b_off = (a_bytes + 255) / 256 * 256;
@@ -1021,7 +1035,6 @@ int gemm_select_layout(const gemm_device_desc* dev, int64_t M, int64_t N, int64_
   if (!dev || !out) return GEMM_ERR_NULL;
   if (b_layout != GEMM_B_KN && b_layout != GEMM_B_NK) return GEMM_ERR_ARG;
   const bool b_nk = b_layout == GEMM_B_NK;
-  if (b_nk && dtype == GEMM_F32) return GEMM_ERR_DTYPE;
   if (dev->cu_count < 1 || dev->lds_bytes < 1) return GEMM_ERR_ARG;
   const gemm_epilogue epi = norm_epi(epi_in);
   const int rc = check_problem(M, N, K, dtype, epi, batch_hint);

@@ -70,7 +70,7 @@ struct FV<4> {
   typedef float type __attribute__((ext_vector_type(4)));
 };
 
-template <int BM, int BN, int WGM, int WGN, int SA>
+template <int BM, int BN, int WGM, int WGN, int SA, bool BNK>
 __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a) {
   constexpr int BK = 16;                    // k per slice
   constexpr int NW = WGM * WGN, NT = 64 * NW;
@@ -93,6 +93,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a)
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // scalar: LDS slot addresses in SGPRs
   const int wm = wave / WGN, wn = wave % WGN;
   const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), K = static_cast<int>(a.K);
+  // row strides of A and B: K and N, or those rounded up to 4 (operands copied into
+  // zero-padded rows)
+  const int LDA = static_cast<int>(a.lda), LDB = static_cast<int>(a.ldb);
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   ftile(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -109,16 +112,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a)
 #pragma unroll
   for (int i = 0; i < AI; ++i) {
     const int gm = m0 + (wave * AI + i) * 16 + a_row;
-    a_voff[i] = gm < M ? static_cast<uint32_t>(gm * K + a_chunk * 4) * 4u : FOOB;
+    a_voff[i] = gm < M ? static_cast<uint32_t>(gm * LDA + a_chunk * 4) * 4u : FOOB;
   }
   // B: instruction i of this wave fills 64 chunks of the slice: row q / (BN/4),
-  // chunk q % (BN/4), for q = (wave*BI + i)*64 + lane.
+  // chunk q % (BN/4), for q = (wave*BI + i)*64 + lane. B given transposed (Bt
+  // [N x K], BNK): the slice is BN rows (n) of 16 k laid out like A's, filled like A.
   uint32_t b_voff[BI];
 #pragma unroll
   for (int i = 0; i < BI; ++i) {
-    const int q = (wave * BI + i) * 64 + lane;
-    const int r = q / (BN / 4), gn = n0 + (q % (BN / 4)) * 4;
-    b_voff[i] = gn < N ? static_cast<uint32_t>(r * N + gn) * 4u : FOOB;
+    if constexpr (BNK) {
+      const int gn = n0 + (wave * BI + i) * 16 + a_row;
+      b_voff[i] = gn < N ? static_cast<uint32_t>(gn * LDB + a_chunk * 4) * 4u : FOOB;
+    } else {
+      const int q = (wave * BI + i) * 64 + lane;
+      const int r = q / (BN / 4), gn = n0 + (q % (BN / 4)) * 4;
+      b_voff[i] = gn < N ? static_cast<uint32_t>(r * LDB + gn) * 4u : FOOB;
+    }
   }
   // A lane whose load falls outside the matrix leaves its LDS slot untouched,
   // so it stores zeros there itself (only k past K matters: stale rows past M or
@@ -128,7 +137,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a)
   // issue is branch-free.
   auto issue = [&](int k0, int stage, auto TailC) {
     constexpr bool TAIL = decltype(TailC)::value;
-    const int64_t aleft = static_cast<int64_t>(M) * K - k0;
+    const int64_t aleft = static_cast<int64_t>(M) * LDA - k0;
     const auto ra = frsrc(Abase + k0, static_cast<uint32_t>(aleft > 0 ? aleft * 4 : 0));
     const bool kin = !TAIL || k0 + a_chunk * 4 < K;  // k past K inside a row would read the next row
 #pragma unroll
@@ -138,8 +147,20 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a)
       if (TAIL && !kin) slot[lane] = f32x4{0.f, 0.f, 0.f, 0.f};
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (flds_void*)slot, 16, off, 0, 0, 0);
     }
-    const int64_t bleft = static_cast<int64_t>(K - k0) * N;
-    const auto rb = frsrc(Bbase + static_cast<int64_t>(k0) * N,
+    if constexpr (BNK) {
+      const int64_t bleft = static_cast<int64_t>(N) * LDB - k0;
+      const auto rb = frsrc(Bbase + k0, static_cast<uint32_t>(bleft > 0 ? bleft * 4 : 0));
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+        const uint32_t off = kin ? b_voff[i] : FOOB;
+        f32x4* slot = lds + stage * STAGE + A_CH + (wave * BI + i) * 64;
+        if (TAIL && !kin) slot[lane] = f32x4{0.f, 0.f, 0.f, 0.f};
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (flds_void*)slot, 16, off, 0, 0, 0);
+      }
+      return;
+    }
+    const int64_t bleft = static_cast<int64_t>(K - k0) * LDB;
+    const auto rb = frsrc(Bbase + static_cast<int64_t>(k0) * LDB,
                           static_cast<uint32_t>(bleft > 0 ? bleft * 4 : 0));
 #pragma unroll
     for (int i = 0; i < BI; ++i) {
@@ -172,6 +193,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a)
     const float* Bs = reinterpret_cast<const float*>(L + A_CH);
     return *reinterpret_cast<const bvec*>(Bs + (8 * g + 4 * lhalf + s) * BN + wn * WTN + lrow * FN);
   };
+  // BNK: B fragment of k-group g, block j: Bt row wn*WTN + 32 j + lrow (C column
+  // 32 j + lrow of the wave's sub-tile), chunk 2g + lhalf: four k, one per step
+  const int b_fbase = (wn * WTN + lrow) * 4;
+  auto bfrag_nk = [&](const f32x4* L, int g, f32x4 (&fb)[FN]) {
+    const int c = (2 * g + lhalf) ^ a_fperm;
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[j] = L[A_CH + b_fbase + j * 128 + c];
+  };
 
   const int nk = (K + BK - 1) / BK;
 #pragma unroll
@@ -191,9 +220,17 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a)
     afrag(L, 1, fa1);
 #pragma unroll
     for (int g = 0; g < BK / 8; ++g) {
+      f32x4 fbk[BNK ? FN : 1];
+      if constexpr (BNK) bfrag_nk(L, g, fbk);
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
-        const bvec fb = bfrag(L, g, s);
+        bvec fb;
+        if constexpr (BNK) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) fb[j] = fbk[j][s];
+        } else {
+          fb = bfrag(L, g, s);
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -213,7 +250,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a)
   for (; kt < nk; ++kt) slice(kt, std::true_type{});
 
   // lane holds, for block (i, j), C[row][col] with row = 8 (r / 4) + 4 (lane / 32)
-  // + r % 4 and col = (lane % 32) * FN + j of the wave's sub-tile.
+  // + r % 4 and col = (lane % 32) * FN + j of the wave's sub-tile (BNK: 32 j +
+  // lane % 32).
   const Epi& e = a.epi;
   const int ob = e.out_dtype == DT_F32 ? 4 : 2;
   const auto rC = frsrc(static_cast<char*>(a.C) + z * a.sC * ob,
@@ -223,12 +261,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a)
                               : static_cast<const char*>(a.C),
                         static_cast<uint32_t>(static_cast<int64_t>(M) * N * ob));
   const int colbase = n0 + wn * WTN + lrow * FN;
+  auto col_of = [&](int j) { return BNK ? n0 + wn * WTN + 32 * j + lrow : colbase + j; };
   float bn[FN];
 #pragma unroll
   for (int j = 0; j < FN; ++j)
-    bn[j] = ((e.flags & EPI_BIAS) && colbase + j < N) ? e.bias[colbase + j] : 0.f;
+    bn[j] = ((e.flags & EPI_BIAS) && col_of(j) < N) ? e.bias[col_of(j)] : 0.f;
   const bool plain = e.flags == 0 && ob == 4;
-  const bool vec_ok = (N % FN) == 0;
+  const bool vec_ok = !BNK && (N % FN) == 0;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -247,7 +286,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a)
       } else {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int col = colbase + j;
+          const int col = col_of(j);
           const uint32_t off =
               (row < M && col < N) ? static_cast<uint32_t>(row * N + col) * ob : FOOB;
           float v = acc[i][j][r];
@@ -273,25 +312,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a)
   }
 }
 
-template <int BM, int BN, int WGM, int WGN, int SA>
+template <int BM, int BN, int WGM, int WGN, int SA, bool BNK>
 hipError_t launch_f32d(const LaunchArgs& a, hipStream_t s) {
   const int64_t tiles = ((a.M + BM - 1) / BM) * ((a.N + BN - 1) / BN);
   dim3 grid(static_cast<unsigned>(tiles), static_cast<unsigned>(a.batch));
-  hipLaunchKernelGGL((gemm_f32d_kernel<BM, BN, WGM, WGN, SA>), grid, dim3(64 * WGM * WGN), 0, s, a);
+  hipLaunchKernelGGL((gemm_f32d_kernel<BM, BN, WGM, WGN, SA, BNK>), grid, dim3(64 * WGM * WGN), 0,
+                     s, a);
   return hipGetLastError();
 }
 
-#define G15_F32D(BM, BN, WGM, WGN, SA)                                                          \
-  {"f32d_" #BM "x" #BN "x16_w" #WGM "x" #WGN "_a" #SA, KIND_F32, DT_F32, BM, BN, 16,            \
-   64 * WGM * WGN, SA * (BM * 64 + 16 * BN * 4), 1, 1, launch_f32d<BM, BN, WGM, WGN, SA>, 1}
+// SFX "" for B [K x N], "_nk" for B given transposed (Bt [N x K])
+#define G15_F32D(BM, BN, WGM, WGN, SA, BNK, SFX)                                               \
+  {"f32d_" #BM "x" #BN "x16_w" #WGM "x" #WGN "_a" #SA SFX, KIND_F32, DT_F32, BM, BN, 16,       \
+   64 * WGM * WGN, SA * (BM * 64 + 16 * BN * 4), 1, 1, launch_f32d<BM, BN, WGM, WGN, SA, BNK>, \
+   1, BNK ? 1 : 0}
+#define G15_F32D_ALL(BNK, SFX)                                                               \
+  G15_F32D(128, 128, 2, 2, 4, BNK, SFX), G15_F32D(128, 128, 2, 2, 3, BNK, SFX),               \
+      G15_F32D(256, 128, 4, 2, 4, BNK, SFX), G15_F32D(128, 256, 2, 4, 4, BNK, SFX),           \
+      G15_F32D(256, 256, 4, 2, 3, BNK, SFX)
 
-const KernelEntry kF32D[] = {
-    G15_F32D(128, 128, 2, 2, 4),
-    G15_F32D(128, 128, 2, 2, 3),
-    G15_F32D(256, 128, 4, 2, 4),
-    G15_F32D(128, 256, 2, 4, 4),
-    G15_F32D(256, 256, 4, 2, 3),
-};
+const KernelEntry kF32D[] = {G15_F32D_ALL(false, ""), G15_F32D_ALL(true, "_nk")};
 
 }  // namespace
 

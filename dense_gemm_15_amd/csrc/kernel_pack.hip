@@ -1,6 +1,6 @@
-// kernel_pack.hip -- copy a 16-bit matrix into rows padded to a multiple of 8
-// elements (16 bytes) with zeros, so that the 16-byte-load kernels can take
-// operands whose rows are not 16-byte multiples (K or N not a multiple of 8).
+// kernel_pack.hip -- copy a 16-bit (fp32) matrix into rows padded to a multiple
+// of 8 (4) elements, 16 bytes, with zeros, so that the 16-byte-load kernels can
+// take operands whose rows are not 16-byte multiples.
 // The padding adds zero products only: A's extra columns meet B rows past K,
 // which the kernels read as zeros, and B's extra columns produce C columns
 // past N, which are never stored.
@@ -26,6 +26,21 @@ __global__ __launch_bounds__(256) void pack16_kernel(const uint16_t* __restrict_
     const uint32_t hi = c + 1 < cols ? s[c + 1] : 0u;
     w[j] = lo | (hi << 16);
   }
+  *reinterpret_cast<u32x4*>(dst + r * ld_dst + c0) = u32x4{w[0], w[1], w[2], w[3]};
+}
+
+// Thread t of the grid fills 4 consecutive fp32 destination elements of one row.
+__global__ __launch_bounds__(256) void pack32_kernel(const uint32_t* __restrict__ src, int64_t rows,
+                                                     int64_t cols, uint32_t* __restrict__ dst,
+                                                     int64_t ld_dst) {
+  const int64_t chunks = ld_dst / 4;
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= rows * chunks) return;
+  const int64_t r = t / chunks, c0 = (t - r * chunks) * 4;
+  const uint32_t* s = src + r * cols;
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) w[j] = c0 + j < cols ? s[c0 + j] : 0u;
   *reinterpret_cast<u32x4*>(dst + r * ld_dst + c0) = u32x4{w[0], w[1], w[2], w[3]};
 }
 
@@ -69,6 +84,18 @@ hipError_t pack_rows16(const void* src, int64_t rows, int64_t cols, void* dst, i
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(pack16_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(src), rows, cols, static_cast<uint16_t*>(dst),
+                     ld_dst);
+  return hipGetLastError();
+}
+
+hipError_t pack_rows32(const void* src, int64_t rows, int64_t cols, void* dst, int64_t ld_dst,
+                       hipStream_t s) {
+  if (rows < 1 || cols < 1 || ld_dst < cols || ld_dst % 4 != 0) return hipErrorInvalidValue;
+  const int64_t threads = rows * (ld_dst / 4);
+  const int64_t blocks = (threads + 255) / 256;
+  if (blocks > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pack32_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                     static_cast<const uint32_t*>(src), rows, cols, static_cast<uint32_t*>(dst),
                      ld_dst);
   return hipGetLastError();
 }

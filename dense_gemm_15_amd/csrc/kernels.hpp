@@ -34,8 +34,9 @@ struct LaunchArgs {
   void* workspace;      // split-K partials (GEMV kind only)
   int64_t workspace_bytes;
   int split;            // split-K factor (GEMV kind); resident workgroups (K1 kind)
-  // Row strides in elements. Every kernel handles lda = K, ldb = N, ldc = N;
-  // only the m16d kernels take other strides (operands packed into padded rows).
+  // Row strides in elements. Every kernel handles lda = K, ldb = N, ldc = N; the
+  // m16d, m16t/m16n, m16s and f32d kernels take other A and B strides (operands
+  // packed into padded rows).
   int64_t lda, ldb, ldc;
   int c_vec;            // 1: C (and resid) base and rows 16-byte aligned, N % 8 == 0
                         // (read by the 16-bit staged epilogue of the m16 kernels)
@@ -44,6 +45,9 @@ struct LaunchArgs {
 // Copy a rows x cols matrix of 16-bit elements (row stride cols) into rows of
 // ld_dst >= cols elements, zero-filling columns cols .. ld_dst-1.
 hipError_t pack_rows16(const void* src, int64_t rows, int64_t cols, void* dst, int64_t ld_dst,
+                       hipStream_t s);
+// The same for fp32 elements, ld_dst a multiple of 4.
+hipError_t pack_rows32(const void* src, int64_t rows, int64_t cols, void* dst, int64_t ld_dst,
                        hipStream_t s);
 
 // Debug aid: fill `batch` items of a rows x cols output (row stride ld, batch stride

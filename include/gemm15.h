@@ -106,8 +106,8 @@ typedef struct gemm_plan gemm_plan;
  * Chooses the kernel configuration (shape-bucket rules, exact-shape cache) for
  * the device current on the calling thread. Host work only: the plan owns no
  * device memory. A configuration that splits K (fp32 partial sums), or that
- * copies 16-bit operands whose rows are not 16-byte multiples (K or N not a
- * multiple of 8) into zero-padded rows, needs device scratch that the caller
+ * copies operands whose rows are not 16-byte multiples (K or N not a multiple
+ * of 8, of 4 for fp32) into zero-padded rows, needs device scratch that the caller
  * passes to gemm_run_ws (size from gemm_plan_workspace_bytes). Rows that are not
  * 16-byte multiples with K <= 64 and M x N >= 2^22 need no copies: the one-slice
  * streaming kernel then reads them through registers (the "_u" configurations,
@@ -137,10 +137,11 @@ gemm_plan* gemm_plan_create_ex(int64_t M, int64_t N, int64_t K, int32_t dtype,
  * section 2: Y = X W^T + b) and of attention scores Q K^T with K stored [S x D],
  * so no transposed copy is needed. With GEMM_B_NK both operands are K-contiguous,
  * as the matrix core reads them, and both stream straight into LDS.
- * GEMM_B_NK needs a 16-bit dtype (GEMM_ERR_DTYPE otherwise) and 16-byte aligned
- * A, Bt and C base pointers and batch strides at run time (GEMM_ERR_ALIGN
- * otherwise); when K is not a multiple of 8 a run with a workspace first copies
- * A and Bt into zero-padded rows there (without one: GEMM_ERR_WORKSPACE).
+ * Every dtype takes GEMM_B_NK (fp32: the f32d kernels with Bt slices loaded like
+ * A's). It needs 16-byte aligned A, Bt and C base pointers and batch strides at
+ * run time (GEMM_ERR_ALIGN otherwise); when K is not a multiple of 8 (4 for fp32)
+ * a run with a workspace first copies A and Bt into zero-padded rows there
+ * (without one: GEMM_ERR_WORKSPACE).
  * GEMM_ERR_ARG for another b_layout.
  */
 gemm_plan* gemm_plan_create_layout(int64_t M, int64_t N, int64_t K, int32_t dtype,

@@ -64,7 +64,7 @@ def test_layout_plan_errors_without_device():
     assert not g.lib.gemm_plan_create_layout(64, 64, 64, g.BF16, ctypes.byref(e), 1, -1, 7)
     assert g.lib.gemm_last_error() == -10  # GEMM_ERR_ARG
     assert not g.lib.gemm_plan_create_layout(64, 64, 64, g.F32, ctypes.byref(e), 1, -1, 1)
-    assert g.lib.gemm_last_error() == -2  # GEMM_ERR_DTYPE: no transposed-B fp32 kernel
+    assert g.lib.gemm_last_error() == -5  # fp32 with a transposed B is valid: no device here
 
 
 def test_attention_probs_argument_errors_without_device():
@@ -148,10 +148,12 @@ def test_select_fits_budget_and_type(dtype, shape):
             # register-load form, which reads the rows as they are
             assert name == f"m16s_{dtype}_256x128x64_w4x2_u" and ch.packed == 0, name
         elif ch.packed:
-            assert dtype != "f32"
-            assert name.startswith("m16d"), name
+            # fp32: only where the copies repay (2^27 multiply-adds and more)
+            assert dtype != "f32" or (M > 8 and M * N * K >= 1 << 27)
+            assert name.startswith("f32d" if dtype == "f32" else "m16d"), name
             assert ch.packed == (1 if pa else 0) | (2 if pb else 0)
         else:
+            assert not (dtype == "f32" and M > 8 and M * N * K >= 1 << 27)
             assert "scalar" in name or name.startswith("simple")
     else:
         assert ch.packed == 0
@@ -199,7 +201,7 @@ TUNED = [
     ((4096, 4096, 4096), 1, "f16", "m16t_f16_256x256x64_w2x4_a3_b2"),
     ((8192, 8192, 8192), 1, "bf16", "m16d_bf16_256x256x64_w4x2_a3_b4_r1"),
     ((8192, 3072, 768), 1, "bf16", "m16t_bf16_128x128x64_w2x2_a2_b2"),
-    ((8192, 768, 3072), 1, "bf16", "m16d_bf16_128x256x64_w2x4_a3_b4_r1"),
+    ((8192, 768, 3072), 1, "bf16", "m16t_bf16_128x256x64_w2x4_a3_b3"),
     ((512, 512, 64), 96, "bf16", "m16s_bf16_256x128x64_w4x2"),
     ((2048, 2048, 2048), 1, "bf16", "m16d_bf16_128x128x64_w2x2_a3_b4_r1"),
     ((512, 64, 512), 96, "bf16", "m16t_bf16_128x128x64_w2x2_a2_b2"),
@@ -262,7 +264,7 @@ def test_select_few_rows_split_k(dtype, M):
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
 def test_select_transposed_b(dtype):
     """A transposed B (Bt [N x K]) takes the both-operands-K-contiguous kernels;
-    K not a multiple of 8 copies both operands; fp32 has no such kernel."""
+    K not a multiple of 8 (4 for fp32) copies both operands."""
     for M, N, K in [(4096, 4096, 4096), (512, 512, 64), (1, 4096, 4096), (300, 264, 200)]:
         ch = g.select(M, N, K, dtype, b_layout="nk", **MI355X)
         assert g.config_names()[ch.config].startswith(f"m16n_{dtype}_") and ch.packed == 0
@@ -270,8 +272,14 @@ def test_select_transposed_b(dtype):
     assert g.config_names()[ch.config].startswith("m16n") and ch.packed == 3
     # the plain layout never takes a transposed-B kernel
     assert not g.config_names()[g.select(4096, 4096, 4096, dtype, **MI355X).config].startswith("m16n")
-    with pytest.raises(g.GemmError):
-        g.select(64, 64, 64, "f32", b_layout="nk", **MI355X)
+    # fp32: the f32d kernels with Bt slices loaded like A's; K not a multiple of 4
+    # copies both operands, and few rows take them too (no few-row kernel for Bt)
+    for M, N, K in [(4096, 4096, 4096), (300, 264, 200), (1, 4096, 4096)]:
+        ch = g.select(M, N, K, "f32", b_layout="nk", **MI355X)
+        assert g.config_names()[ch.config].startswith("f32d_") and ch.packed == 0
+        assert g.config_names()[ch.config].endswith("_nk")
+    ch = g.select(127, 1000, 771, "f32", b_layout="nk", **MI355X)
+    assert g.config_names()[ch.config].startswith("f32d_") and ch.packed == 3
 
 
 def test_exact_shape_cache_hit():

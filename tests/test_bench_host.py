@@ -18,8 +18,10 @@ def test_symbol_to_config():
              " false>(g15::LaunchArgs)") == "m16n_f16_128x128x64_w2x2_a2_b2"
     assert s("void g15::(anonymous namespace)::gemm_m16n_kernel<g15::bf16_t, 128, 128, 2, 2, 2, 2,"
              " true>(g15::LaunchArgs)") == "m16t_bf16_128x128x64_w2x2_a2_b2"
-    assert s("void g15::(anonymous namespace)::gemm_f32d_kernel<256, 256, 4, 2, 3>"
+    assert s("void g15::(anonymous namespace)::gemm_f32d_kernel<256, 256, 4, 2, 3, false>"
              "(g15::LaunchArgs)") == "f32d_256x256x16_w4x2_a3"
+    assert s("void g15::(anonymous namespace)::gemm_f32d_kernel<128, 128, 2, 2, 3, true>"
+             "(g15::LaunchArgs)") == "f32d_128x128x16_w2x2_a3_nk"
     assert s("void g15::(anonymous namespace)::gemv_kernel<g15::f16_t, 1, 4096, 8>"
              "(g15::LaunchArgs, long)") == "gemv_f16_m1"
     assert s("void g15::(anonymous namespace)::gemm_m16s_kernel<g15::bf16_t, 128, 128, 2, 2, true,"

@@ -56,7 +56,7 @@ def _dtype_of(name):
 CONFIGS = _configs()
 TILE_CONFIGS = [c for c in CONFIGS if not c.startswith(("gemv", "m16n", "m16s"))
                 and not c.endswith("_nk") and "acc16" not in c]
-NT_CONFIGS = [c for c in CONFIGS if c.startswith("m16n") or (c.startswith("m16w") and c.endswith("_nk"))]
+NT_CONFIGS = [c for c in CONFIGS if c.startswith("m16n") or (c.startswith(("m16w", "f32d")) and c.endswith("_nk"))]
 GEMV_CONFIGS = [c for c in CONFIGS if c.startswith("gemv")]
 
 
@@ -780,6 +780,79 @@ def test_workspace_required_transposed_padded(g):
     C = _run_nt(plan, A, B)
     r = gc.check_full(C, A, B, "bf16")
     assert r["ok"], r
+
+
+F32_PADDED = [
+    # (M, N, K, packed bits): fp32 rows that are not 16-byte multiples, products large
+    # enough (2^27 multiply-adds, tiles for every CU) for the copies to repay
+    (2050, 2051, 135, 3),
+    (2048, 2051, 260, 2),
+    (2050, 2048, 150, 1),
+]
+
+
+@pytest.mark.parametrize("case", range(len(F32_PADDED)))
+def test_fp32_padded_copies(g, case):
+    """fp32 operands whose rows are not 16-byte multiples (K or N not a multiple of 4)
+    copied into zero-padded rows and run on f32d: float and small-integer inputs, every
+    element, two runs of the plan; then bias + GELU + residual into bf16 C."""
+    M, N, K, bits = F32_PADDED[case]
+    plan = g.Plan(M, N, K, "f32")
+    d = _describe(plan)
+    say(f"[f32 padded] {plan.describe()}")
+    assert d["config"].startswith("f32d_") and int(d["packed"]) == bits
+    for kind in ("uniform", "int"):
+        A, B = gc.inputs(M, N, K, "f32", 2300 + case, kind)
+        for rep in range(2):
+            C = gc.run_gpu(plan, A, B)
+            r = gc.check_full(C, A, B, "f32", exact=(kind == "int"))
+            assert r["ok"], (kind, rep, r)
+    plan = g.Plan(M, N, K, "f32", bias=True, gelu=True, resid=True, out_dtype="bf16")
+    assert int(_describe(plan)["packed"]) == bits
+    A, B = gc.inputs(M, N, K, "f32", 2310 + case)
+    bias = synth.normal(2320 + case, (N,), 0.5, "f32")
+    resid = synth.uniform(2330 + case, (M, N), "bf16")
+    C = gc.run_gpu(plan, A, B, bias, resid)
+    r = gc.check_full(C, A, B, "f32", "bf16", bias, resid, None, True)
+    assert r["ok"], r
+
+
+def test_fp32_4097_cube(g):
+    """4097^3 fp32 (no row a 16-byte multiple): both operands copied into padded rows
+    and an f32d kernel on them; every one of the 16.8M outputs against the oracle,
+    within 1e-3 absolute over all of them (the SGEMM page, section 4.1)."""
+    n = 4097
+    plan = g.Plan(n, n, n, "f32")
+    d = _describe(plan)
+    say(f"[f32 4097] {plan.describe()}")
+    assert d["config"].startswith("f32d_") and int(d["packed"]) == 3
+    A = synth.uniform(2340, (n, n), "f32")
+    B = synth.uniform(2341, (n, n), "f32")
+    C = gc.run_gpu(plan, A, B)
+    r = gc.check_full(C, A, B, "f32", abs_max=1e-3)
+    say(f"[f32 4097] max err/tol {r['max_ratio']:.3f} max abs {r['max_abs']:.3e}")
+    assert r["ok"], r
+
+
+def test_fp32_transposed_b(g):
+    """fp32 with B given transposed (Y = X W^T + b with fp32 weights [out, in]): the
+    selected f32d *_nk plan on an aligned shape with bias + GELU, K not a multiple of
+    4 (A and Bt copied into padded rows), a residual into fp32 C; every element."""
+    cases = [(300, 264, 200, dict(bias=True, gelu=True), 0),
+             (127, 1000, 771, dict(), 3),
+             (257, 130, 203, dict(resid=True, scale=0.5), 3)]
+    for ci, (M, N, K, epi, bits) in enumerate(cases):
+        plan = g.Plan(M, N, K, "f32", b_layout="nk", **epi)
+        d = _describe(plan)
+        say(f"[f32 nt] {plan.describe()}")
+        assert d["b"] == "nk" and d["config"].startswith("f32d_") and int(d["packed"]) == bits
+        A, B = gc.inputs(M, N, K, "f32", 2350 + ci)
+        bias = synth.normal(2360 + ci, (N,), 0.5, "f32") if epi.get("bias") else None
+        resid = synth.uniform(2370 + ci, (M, N), "f32") if epi.get("resid") else None
+        C = _run_nt(plan, A, B, bias, resid)
+        r = gc.check_full(C, A, B, "f32", "f32", bias, resid, epi.get("scale"),
+                          epi.get("gelu", False))
+        assert r["ok"], (ci, r)
 
 
 def test_workspace_two_streams(g):
