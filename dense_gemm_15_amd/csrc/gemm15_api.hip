@@ -61,6 +61,14 @@ struct gemm_plan {
   int64_t lda_p;    // padded row lengths (elements) of the A and B copies
   int64_t ldb_p;
   int64_t pack_b_off;  // byte offset of the B copy in the workspace (the A copy is at 0)
+  // Thin edges (fp32 products whose M and N end a few rows / columns past a 256
+  // boundary): the primary configuration runs the (M - edge_m) x (N - edge_n) block
+  // in whole tiles, the few-row kernel `edge_gemv` (split edge_split, its partial
+  // sums at edge_ws_off in the workspace) the last edge_m rows, and the few-column
+  // kernel the last edge_n columns of the other rows.
+  int edge_m, edge_n;
+  int edge_gemv, edge_split;
+  int64_t edge_ws_off;
 };
 
 namespace {
@@ -305,6 +313,7 @@ struct Selection {
   int fallback = -1;
   int packed = 0;
   int tile = -1;  // best tile configuration that needs no workspace, for aligned pointers
+  int edge = 0;   // 1: thin edges split off (see gemm_plan)
 };
 
 // x rounded up to whole 16-byte chunks of es-byte elements
@@ -396,6 +405,23 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
   double cost = 0;
   s.config = best_for(vec_a, vec_b, K, N, any, &cost);
   const bool pa = (K * es) % 16 != 0, pb = ((b_nk ? K : N) * es) % 16 != 0;
+  // fp32 products whose M and N end at most 8 rows / columns past a multiple of 256
+  // (4097^3) and whose whole-tile block fills every CU: whole tiles would leave a
+  // second round of one-row tiles, each as slow as a full one; the 256 x 256 SGEMM
+  // kernel takes the whole-tile block in full rounds and the few-row and few-column
+  // kernels the edges (operands copied into padded rows when theirs are not 16-byte
+  // multiples).
+  if (dtype == GEMM_F32 && !b_nk && aligned16 && K >= 256 && M % 256 <= 8 && N % 256 <= 8 &&
+      M % 256 + N % 256 > 0 && (M / 256) * (N / 256) >= dev.cu_count) {
+    for (size_t i = 0; i < all.size(); ++i)
+      if (std::strcmp(all[i].name, "f32d_256x256x16_w4x2_a3") == 0 &&
+          cfg_fits(all[i], dtype, true, true, dev, M, N, round_up16B(K, es), epi.out_dtype)) {
+        s.config = static_cast<int>(i);
+        s.packed = (pa ? 1 : 0) | (pb ? 2 : 0);
+        s.edge = 1;
+        return s;
+      }
+  }
   // 16-bit rows that are not 16-byte multiples, K within one 64-deep slice and a
   // large C: the streaming kernel's register-load form reads the rows as they are
   // (no padded copies, no workspace) while C of the previous tile leaves.
@@ -573,6 +599,74 @@ int run_packed(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, con
   return GEMM_OK;
 }
 
+// Run of a plan with thin edges split off (fp32): per batch item, the padded copies
+// (if any), the whole-tile block on the primary configuration, the last edge_m rows
+// on the few-row kernel (partial sums in the workspace) and the last edge_n columns of
+// the other rows on the few-column kernel. C, the residual and the bias are addressed
+// at the block's origin with C's full row stride.
+int run_edges(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, const void* B,
+              int64_t sB, const float* bias, const void* resid, int64_t sR, void* C, int64_t sC,
+              void* ws, hipStream_t s) {
+  const auto& all = registry().all;
+  const KernelEntry& k = all[p->config];
+  const int64_t ie = elem_bytes(p->dtype), oe = elem_bytes(p->epi.out_dtype);
+  const int64_t M1 = p->M - p->edge_m, N1 = p->N - p->edge_n;
+  void* const pack_a = ws;
+  void* const pack_b = static_cast<char*>(ws) + p->pack_b_off;
+  auto base = [&](int64_t m_rows, int64_t n_cols, int64_t K, const void* Ap, int64_t lda,
+                  const void* Bp, int64_t ldb, void* Cp, const void* Rp, const float* bp) {
+    LaunchArgs la{};
+    la.M = m_rows;
+    la.N = n_cols;
+    la.K = K;
+    la.batch = 1;
+    la.A = Ap;
+    la.B = Bp;
+    la.C = Cp;
+    la.epi.flags = p->epi.flags;
+    la.epi.scale = p->epi.scale;
+    la.epi.bias = bp;
+    la.epi.resid = Rp;
+    la.epi.out_dtype = p->epi.out_dtype;
+    la.split = 1;
+    la.lda = lda;
+    la.ldb = ldb;
+    la.ldc = p->N;
+    la.c_vec = 0;
+    return la;
+  };
+  for (int64_t z = 0; z < batch; ++z) {
+    const char* Az = static_cast<const char*>(A) + z * sA * ie;
+    const char* Bz = static_cast<const char*>(B) + z * sB * ie;
+    char* Cz = static_cast<char*>(C) + z * sC * oe;
+    const char* Rz = (p->epi.flags & GEMM_EPI_RESID) ? static_cast<const char*>(resid) + z * sR * oe
+                                                     : nullptr;
+    if ((p->packed & 1) && pack_rows32(Az, p->M, p->K, pack_a, p->lda_p, s) != hipSuccess)
+      return GEMM_ERR_HIP;
+    if ((p->packed & 2) && pack_rows32(Bz, p->K, p->N, pack_b, p->ldb_p, s) != hipSuccess)
+      return GEMM_ERR_HIP;
+    const char* Au = (p->packed & 1) ? static_cast<const char*>(pack_a) : Az;
+    const char* Bu = (p->packed & 2) ? static_cast<const char*>(pack_b) : Bz;
+    const int64_t lda = p->lda_p, ldb = p->ldb_p;  // K and N when not copied
+    LaunchArgs la = base(M1, N1, p->K, Au, lda, Bu, ldb, Cz, Rz, bias);
+    if (k.launch(la, s) != hipSuccess) return GEMM_ERR_HIP;
+    if (p->edge_m > 0) {
+      LaunchArgs lg = base(p->edge_m, p->N, p->K, Au + M1 * lda * ie, lda, Bu, ldb,
+                           Cz + M1 * p->N * oe, Rz ? Rz + M1 * p->N * oe : nullptr, bias);
+      lg.split = p->edge_split;
+      lg.workspace = static_cast<char*>(ws) + p->edge_ws_off;
+      lg.workspace_bytes = p->workspace_bytes - p->edge_ws_off;
+      if (all[p->edge_gemv].launch(lg, s) != hipSuccess) return GEMM_ERR_HIP;
+    }
+    if (p->edge_n > 0) {
+      LaunchArgs lc = base(M1, p->edge_n, p->K, Au, lda, Bu + N1 * ie, ldb, Cz + N1 * oe,
+                           Rz ? Rz + N1 * oe : nullptr, bias ? bias + N1 : nullptr);
+      if (launch_gemv_cols(lc, p->dtype, s) != hipSuccess) return GEMM_ERR_HIP;
+    }
+  }
+  return GEMM_OK;
+}
+
 // Split-K run of a tile configuration: the S slices of K run as the S items of one
 // strided batch (A advanced Kc columns, B Kc rows, K = Kc, C the workspace's fp32
 // partial products, no epilogue; A's row stride stays K, and the kernel's K tail
@@ -627,6 +721,9 @@ int run_split_k(const gemm_plan* p, const KernelEntry& k, int64_t batch, const v
     lr.workspace = ws;
     lr.workspace_bytes = p->workspace_bytes;
     lr.split = S;
+    lr.lda = p->K;
+    lr.ldb = p->N;
+    lr.ldc = p->N;
     if (launch_splitk_reduce(lr, z, p->M, s) != hipSuccess) return GEMM_ERR_HIP;
   }
   return GEMM_OK;
@@ -659,12 +756,13 @@ int describe_plan(const gemm_plan* p, char* buf, size_t len) {
   const int n = std::snprintf(
       tmp, sizeof(tmp),
       "config=%s id=%d tile=%dx%dx%d threads=%d lds=%d workgroups=%lld split=%d packed=%d "
-      "b=%s fallback=%s workspace=%lld nows=%s",
+      "b=%s fallback=%s workspace=%lld nows=%s edge=%d,%d",
       k.name, p->config, k.bm, k.bn, k.bk, k.threads, k.lds_bytes,
       static_cast<long long>(cfg_workgroups(k, p->M, p->N, p->split, p->batch_hint)),
       k.kind == KIND_K1 ? 1 : p->split,  // a K1 plan keeps its resident workgroups there
       p->packed, p->b_nk ? "nk" : "kn", p->fallback >= 0 ? all[p->fallback].name : "none",
-      static_cast<long long>(p->workspace_bytes), p->nows >= 0 ? all[p->nows].name : "none");
+      static_cast<long long>(p->workspace_bytes), p->nows >= 0 ? all[p->nows].name : "none",
+      p->edge_m, p->edge_n);
   if (buf && len > 0) {
     std::strncpy(buf, tmp, len - 1);
     buf[len - 1] = '\0';
@@ -766,11 +864,39 @@ gemm_plan* gemm_plan_create_layout(int64_t M, int64_t N, int64_t K, int32_t dtyp
     p->split = gemv_split(k, N, K, batch_hint, desc);
     p->workspace_bytes = gemv_workspace_bytes(k, N, p->split);
   }
+  p->edge_m = p->edge_n = 0;
+  p->edge_gemv = -1;
+  p->edge_split = 1;
+  p->edge_ws_off = 0;
+  if (sel.edge) {
+    p->edge_m = static_cast<int>(M % 256);
+    p->edge_n = static_cast<int>(N % 256);
+    if (p->edge_m > 0) {
+      for (int i = 0; i < static_cast<int>(all.size()); ++i) {
+        const KernelEntry& g = all[i];
+        if (g.kind != KIND_GEMV || g.in_dtype != dtype || g.bm < p->edge_m ||
+            !cfg_fits(g, dtype, true, true, desc, p->edge_m, N, K, epi.out_dtype))
+          continue;
+        if (p->edge_gemv < 0 || g.bm < all[p->edge_gemv].bm) p->edge_gemv = i;
+      }
+      if (p->edge_gemv < 0) {
+        delete p;
+        return fail(GEMM_ERR_CONFIG);
+      }
+      const KernelEntry& g = all[p->edge_gemv];
+      p->edge_split = gemv_split(g, N, K, 1, desc);
+      p->edge_ws_off = (p->workspace_bytes + 255) / 256 * 256;
+      p->workspace_bytes = p->edge_ws_off + gemv_workspace_bytes(g, N, p->edge_split);
+    }
+  }
   // Without a workspace: the same kernel with K unsplit when it can take all of K,
   // otherwise the best plain tile configuration; padded copies give way to the
   // scalar-load configuration (none for a transposed B).
   p->nows = cfg;
-  if (sel.packed) {
+  if (sel.edge) {
+    // the whole product on the best plain configuration (no edges split off)
+    p->nows = sel.packed ? fb : (sel.tile >= 0 ? sel.tile : fb);
+  } else if (sel.packed) {
     p->nows = b_nk ? -1 : fb;
   } else if (k.kind == KIND_GEMV && p->split > 1 && K > k.bk) {
     int t = sel.tile;
@@ -900,6 +1026,16 @@ int gemm_run_strided_batched_ws(const gemm_plan* p, int64_t batch, const void* A
   const auto& all = registry().all;
   const bool c16 = aligned_to(C, 16) && (p->N * oe) % 16 == 0 && (sC * oe) % 16 == 0 &&
                    (!(e.flags & GEMM_EPI_RESID) || (aligned_to(resid, 16) && (sR * oe) % 16 == 0));
+  if (p->edge_m + p->edge_n > 0 && (use_ws || p->workspace_bytes == 0)) {
+    // thin edges split off: operands not copied, C and the residual must start on
+    // 16 bytes (their rows may have any length)
+    const bool a_ok = (p->packed & 1) || (aligned_to(A, 16) && (sA * ie) % 16 == 0);
+    const bool b_ok = (p->packed & 2) || (aligned_to(B, 16) && (sB * ie) % 16 == 0);
+    const bool c_ok = aligned_to(C, 16) && (sC * oe) % 16 == 0 &&
+                      (!(e.flags & GEMM_EPI_RESID) || (aligned_to(resid, 16) && (sR * oe) % 16 == 0));
+    if (a_ok && b_ok && c_ok)
+      return run_edges(p, batch, A, sA, B, sB, bias, resid, sR, C, sC, ws, st);
+  }
   if (p->packed && use_ws) {
     // operands that are not copied must still be 16-byte aligned for the kernel
     const bool a_ok = (p->packed & 1) || (aligned_to(A, 16) && (sA * ie) % 16 == 0);

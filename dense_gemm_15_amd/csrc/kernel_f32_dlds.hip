@@ -96,6 +96,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a)
   // row strides of A and B: K and N, or those rounded up to 4 (operands copied into
   // zero-padded rows)
   const int LDA = static_cast<int>(a.lda), LDB = static_cast<int>(a.ldb);
+  const int LDC = static_cast<int>(a.ldc);  // C (and residual) row stride, N unless a block of C
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
   ftile(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -255,11 +256,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a)
   const Epi& e = a.epi;
   const int ob = e.out_dtype == DT_F32 ? 4 : 2;
   const auto rC = frsrc(static_cast<char*>(a.C) + z * a.sC * ob,
-                        static_cast<uint32_t>(static_cast<int64_t>(M) * N * ob));
+                        static_cast<uint32_t>(static_cast<int64_t>(M) * LDC * ob));
   const bool has_r = (e.flags & EPI_RESID) != 0;
   const auto rR = frsrc(has_r ? static_cast<const char*>(e.resid) + z * a.sR * ob
                               : static_cast<const char*>(a.C),
-                        static_cast<uint32_t>(static_cast<int64_t>(M) * N * ob));
+                        static_cast<uint32_t>(static_cast<int64_t>(M) * LDC * ob));
   const int colbase = n0 + wn * WTN + lrow * FN;
   auto col_of = [&](int j) { return BNK ? n0 + wn * WTN + 32 * j + lrow : colbase + j; };
   float bn[FN];
@@ -267,7 +268,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a)
   for (int j = 0; j < FN; ++j)
     bn[j] = ((e.flags & EPI_BIAS) && col_of(j) < N) ? e.bias[col_of(j)] : 0.f;
   const bool plain = e.flags == 0 && ob == 4;
+  // a lane's FN consecutive columns leave as one vector store (rows whose start is not
+  // FN-aligned, C's row stride not a multiple of FN: a vector store to a 4-byte aligned
+  // address, which the memory system serves like an aligned one)
   const bool vec_ok = !BNK && (N % FN) == 0;
+  const bool vec_aligned = (LDC % FN) == 0;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -280,15 +285,18 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_f32d_kernel(LaunchArgs a)
           bvec v;
 #pragma unroll
           for (int j = 0; j < FN; ++j) v[j] = acc[i][j][r];
-          *reinterpret_cast<bvec*>(static_cast<float*>(a.C) + z * a.sC +
-                                   static_cast<int64_t>(row) * N + colbase) = v;
+          float* dst = static_cast<float*>(a.C) + z * a.sC + static_cast<int64_t>(row) * LDC + colbase;
+          if (vec_aligned)
+            *reinterpret_cast<bvec*>(dst) = v;
+          else
+            __builtin_memcpy(dst, &v, sizeof(v));
         }
       } else {
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
           const int col = col_of(j);
           const uint32_t off =
-              (row < M && col < N) ? static_cast<uint32_t>(row * N + col) * ob : FOOB;
+              (row < M && col < N) ? static_cast<uint32_t>(row * LDC + col) * ob : FOOB;
           float v = acc[i][j][r];
           if (e.flags & EPI_SCALE) v *= e.scale;
           if (e.flags & EPI_BIAS) v += bn[j];

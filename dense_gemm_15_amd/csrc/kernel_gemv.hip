@@ -90,6 +90,9 @@ __global__ __launch_bounds__(GNT) void gemv_kernel(LaunchArgs a, int64_t z0) {
   __shared__ float red[4][MR][GNS];
 
   const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), K = static_cast<int>(a.K);
+  // row strides: A's (K unless rows of a padded copy), B's (N, likewise) and C's (N
+  // unless a block of a larger C)
+  const int64_t LDA = a.lda, LDB = a.ldb, LDC = a.ldc;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int strip = blockIdx.x, split = blockIdx.y, S = gridDim.y;
   const int64_t z = z0 + blockIdx.z;
@@ -102,7 +105,7 @@ __global__ __launch_bounds__(GNT) void gemv_kernel(LaunchArgs a, int64_t z0) {
 
   const int rg = wave * RPW + lane / LPR;  // this lane's row group
   const int cl = (lane % LPR) * EPL;       // first column of this lane in the strip
-  const auto rB = grsrc(Bp, static_cast<uint32_t>(static_cast<int64_t>(K) * N * in_bytes));
+  const auto rB = grsrc(Bp, static_cast<uint32_t>(static_cast<int64_t>(K) * LDB * in_bytes));
   const bool colok = n0 + cl < N;  // N is a multiple of EPL: a chunk is all in or all out
 
   // rows k0, k0 + RG, ..., k0 + (U - 1) RG of this lane's 16-byte column chunk
@@ -112,7 +115,7 @@ __global__ __launch_bounds__(GNT) void gemv_kernel(LaunchArgs a, int64_t z0) {
     for (int u = 0; u < U; ++u) {
       const int k = k0 + u * RG;
       const uint32_t off = (colok && k < ke)
-                               ? static_cast<uint32_t>((static_cast<int64_t>(k) * N + n0 + cl) * in_bytes)
+                               ? static_cast<uint32_t>((static_cast<int64_t>(k) * LDB + n0 + cl) * in_bytes)
                                : GOOB;
       v[u] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, off, 0, 0));
     }
@@ -127,7 +130,7 @@ __global__ __launch_bounds__(GNT) void gemv_kernel(LaunchArgs a, int64_t z0) {
 #pragma unroll
       for (int u = 0; u < SU; ++u) {
         const int k = j0 + u * GNT;
-        t[u] = (m < M && kb + k < ke) ? gload<T>(Ap, static_cast<int64_t>(m) * K + kb + k) : 0.f;
+        t[u] = (m < M && kb + k < ke) ? gload<T>(Ap, static_cast<int64_t>(m) * LDA + kb + k) : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < SU; ++u)
@@ -185,7 +188,7 @@ __global__ __launch_bounds__(GNT) void gemv_kernel(LaunchArgs a, int64_t z0) {
     const void* Rp =
         (e.flags & EPI_RESID) ? static_cast<const char*>(e.resid) + z * a.sR * ob : nullptr;
     const float bn = (e.flags & EPI_BIAS) ? e.bias[gn] : 0.f;
-    const int64_t idx = static_cast<int64_t>(m) * N + gn;
+    const int64_t idx = static_cast<int64_t>(m) * LDC + gn;
     store_out_elem(Cp, e.out_dtype, idx, apply_epi(e, v, bn, Rp, idx));
   };
 
@@ -205,6 +208,108 @@ __global__ __launch_bounds__(GNT) void gemv_kernel(LaunchArgs a, int64_t z0) {
   }
 }
 
+// Few columns (N <= 8: the strip of a product's last columns past a 256-column tile
+// boundary): C[m][j] = epi(sum_k A[m][k] B[k][j]), j < N. Workgroup: 8 rows, 2 per
+// wave (two workgroups per CU at 4096 rows; one row per wave measured slower, each
+// workgroup staging all of B's strip); K in chunks of KC. B's chunk (KC rows x 8 columns, zeros past N) goes through
+// two LDS buffers: while chunk c is summed, the loads of chunk c + 1's B (into
+// registers, written to the other buffer after the sums) and of chunk c + 1's A values
+// (lane l: k = l + 64 i of each of its wave's rows) are in flight. The 64 lanes'
+// sums of each (row, column) are then added across the wave and lane 0 applies the
+// epilogue. fp32 accumulation in a fixed order.
+template <typename T>
+__global__ __launch_bounds__(256) void gemv_cols_kernel(LaunchArgs a) {
+  constexpr int KC = 512, RW = 2, PER = KC / 64, BPT = KC * 8 / 256;
+  __shared__ float bs[2][KC][8];
+  const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), K = static_cast<int>(a.K);
+  const int64_t LDA = a.lda, LDB = a.ldb, LDC = a.ldc;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t z = blockIdx.y;
+  const int in_bytes = T::code == DT_F32 ? 4 : 2;
+  const char* Ap = static_cast<const char*>(a.A) + z * a.sA * in_bytes;
+  const char* Bp = static_cast<const char*>(a.B) + z * a.sB * in_bytes;
+  const int row0 = blockIdx.x * (4 * RW) + wave * RW;  // the same for the whole wave
+  float acc[RW][8];
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[r][j] = 0.f;
+  // thread t stages elements t + 256 q of a chunk: row (t + 256 q) / 8, column t % 8
+  float bq[BPT], av[RW][PER];
+  auto load_b = [&](int kc) {
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) {
+      const int kk = (tid + 256 * q) >> 3, j = tid & 7;
+      bq[q] = (kc + kk < K && j < N) ? gload<T>(Bp, static_cast<int64_t>(kc + kk) * LDB + j) : 0.f;
+    }
+  };
+  auto store_b = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < BPT; ++q) bs[buf][(tid + 256 * q) >> 3][tid & 7] = bq[q];
+  };
+  auto load_a = [&](int kc) {
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) {
+        const int m = row0 + r, k = kc + lane + 64 * i;
+        av[r][i] = (m < M && k < K) ? gload<T>(Ap, static_cast<int64_t>(m) * LDA + k) : 0.f;
+      }
+  };
+  load_b(0);
+  store_b(0);
+  load_a(0);
+  int buf = 0;
+  for (int kc = 0; kc < K; kc += KC) {
+    const bool more = kc + KC < K;
+    if (more) load_b(kc + KC);  // in flight during this chunk's sums
+    __syncthreads();            // chunk kc's B is in bs[buf]
+    float an[RW][PER];
+#pragma unroll
+    for (int r = 0; r < RW; ++r)
+#pragma unroll
+      for (int i = 0; i < PER; ++i) an[r][i] = av[r][i];
+    if (more) load_a(kc + KC);
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const f32x4 b0 = *reinterpret_cast<const f32x4*>(&bs[buf][lane + 64 * i][0]);
+      const f32x4 b1 = *reinterpret_cast<const f32x4*>(&bs[buf][lane + 64 * i][4]);
+#pragma unroll
+      for (int r = 0; r < RW; ++r)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[r][j] = __builtin_fmaf(an[r][i], b0[j], acc[r][j]);
+          acc[r][j + 4] = __builtin_fmaf(an[r][i], b1[j], acc[r][j + 4]);
+        }
+    }
+    if (more) store_b(buf ^ 1);  // every wave read bs[buf ^ 1] before this chunk's barrier
+    buf ^= 1;
+  }
+#pragma unroll
+  for (int r = 0; r < RW; ++r)
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int d = 1; d < 64; d *= 2) acc[r][j] += __shfl_xor(acc[r][j], d);
+  if (lane != 0) return;
+  const Epi& e = a.epi;
+  const int64_t ob = e.out_dtype == DT_F32 ? 4 : 2;
+  void* Cp = static_cast<char*>(a.C) + z * a.sC * ob;
+  const void* Rp = (e.flags & EPI_RESID) ? static_cast<const char*>(e.resid) + z * a.sR * ob : nullptr;
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int m = row0 + r;
+    if (m >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= N) continue;
+      const float bn = (e.flags & EPI_BIAS) ? e.bias[j] : 0.f;
+      const int64_t idx = static_cast<int64_t>(m) * LDC + j;
+      store_out_elem(Cp, e.out_dtype, idx, apply_epi(e, acc[r][j], bn, Rp, idx));
+    }
+  }
+}
+
 // C[m][n] = epi(sum over s of partial[s][m][n]), s ascending; one thread per element
 // (partial [split][rows][N]).
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(LaunchArgs a, int64_t z, int64_t rows) {
@@ -212,6 +317,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(LaunchArgs a, int64_
   const int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
   if (i >= a.M * N) return;
   const int64_t m = i / N, n = i - m * N;
+  const int64_t o = m * a.ldc + n;  // C (and residual) index: row stride ldc
   const float* ws = static_cast<const float*>(a.workspace);
   const int64_t stride = rows * N;
   const float* p = ws + m * N + n;
@@ -229,7 +335,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(LaunchArgs a, int64_
   const void* Rp =
       (e.flags & EPI_RESID) ? static_cast<const char*>(e.resid) + z * a.sR * ob : nullptr;
   const float bn = (e.flags & EPI_BIAS) ? e.bias[n] : 0.f;
-  store_out_elem(Cp, e.out_dtype, i, apply_epi(e, s, bn, Rp, i));
+  store_out_elem(Cp, e.out_dtype, o, apply_epi(e, s, bn, Rp, o));
 }
 
 template <typename T, int MR, int KMAX, int U>
@@ -281,6 +387,22 @@ hipError_t launch_splitk_reduce(const LaunchArgs& a, int64_t z, int64_t rows, hi
 int gemv_entries(const KernelEntry** out) {
   *out = kGemv;
   return static_cast<int>(sizeof(kGemv) / sizeof(kGemv[0]));
+}
+
+hipError_t launch_gemv_cols(const LaunchArgs& a, int in_dtype, hipStream_t s) {
+  if (a.N < 1 || a.N > 8 || a.M < 1 || a.batch < 1 || a.batch > 65535 ||
+      (a.M + 7) / 8 > 0x7fffffff)
+    return hipErrorInvalidValue;
+  const dim3 grid(static_cast<unsigned>((a.M + 7) / 8), static_cast<unsigned>(a.batch));
+  if (in_dtype == DT_F32)
+    hipLaunchKernelGGL(gemv_cols_kernel<f32_t>, grid, dim3(256), 0, s, a);
+  else if (in_dtype == DT_BF16)
+    hipLaunchKernelGGL(gemv_cols_kernel<bf16_t>, grid, dim3(256), 0, s, a);
+  else if (in_dtype == DT_F16)
+    hipLaunchKernelGGL(gemv_cols_kernel<f16_t>, grid, dim3(256), 0, s, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
 }
 
 }  // namespace g15

@@ -10,7 +10,13 @@ namespace g15 {
 // C[z][m][n] = epi(sum over s < a.split, ascending, of ws[s][m][n]) for m < a.M,
 // n < a.N, with ws = a.workspace as float [a.split][rows][a.N] (rows >= a.M). Bias,
 // residual (batch item z, stride a.sR), scale and output type come from a.epi; C is
-// batch item z of a.C (stride a.sC).
+// batch item z of a.C (stride a.sC), row stride a.ldc.
 hipError_t launch_splitk_reduce(const LaunchArgs& a, int64_t z, int64_t rows, hipStream_t s);
+
+// Few columns: C[z][m][j] = epi(sum_k A[z][m][k] B[z][k][j]) for m < a.M, j < a.N <= 8,
+// A, B of type in_dtype (DT_*) with row strides a.lda, a.ldb, C and the residual with
+// row stride a.ldc, bias[j]; every batch item in one launch. hipErrorInvalidValue for
+// N outside 1..8 or another type.
+hipError_t launch_gemv_cols(const LaunchArgs& a, int in_dtype, hipStream_t s);
 
 }  // namespace g15

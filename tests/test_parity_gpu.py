@@ -825,13 +825,57 @@ def test_fp32_4097_cube(g):
     plan = g.Plan(n, n, n, "f32")
     d = _describe(plan)
     say(f"[f32 4097] {plan.describe()}")
-    assert d["config"].startswith("f32d_") and int(d["packed"]) == 3
+    # the 4096 x 4096 block on the 256 x 256 kernel, the last row and column apart
+    assert d["config"] == "f32d_256x256x16_w4x2_a3" and int(d["packed"]) == 3
+    assert d["edge"] == "1,1"
     A = synth.uniform(2340, (n, n), "f32")
     B = synth.uniform(2341, (n, n), "f32")
     C = gc.run_gpu(plan, A, B)
     r = gc.check_full(C, A, B, "f32", abs_max=1e-3)
     say(f"[f32 4097] max err/tol {r['max_ratio']:.3f} max abs {r['max_abs']:.3e}")
     assert r["ok"], r
+
+
+F32_EDGES = [
+    # (M, N, K, batch, epilogue, out, edge, packed): fp32 products a few rows / columns
+    # past multiples of 256, the whole-tile block in one round
+    (4100, 4100, 4100, 1, dict(), "f32", "4,4", 0),
+    (4096, 4097, 1024, 1, dict(bias=True, gelu=True, resid=True), "bf16", "0,1", 2),
+    (4099, 4096, 600, 2, dict(scale=0.5, bias=True), "f32", "3,0", 0),
+]
+
+
+@pytest.mark.parametrize("case", range(len(F32_EDGES)))
+def test_fp32_thin_edges(g, case):
+    """Thin edges split off: the whole-tile block on the 256 x 256 SGEMM kernel, the
+    last rows on the few-row kernel (partial sums in the workspace), the last columns
+    on the few-column kernel; aligned and padded operands, every epilogue stage into
+    16-bit C, a strided batch, and the same plan without a workspace (the whole product
+    on a plain configuration). Every element against the oracle (fp32 C also within
+    1e-3 absolute)."""
+    M, N, K, nb, epi, od, edge, bits = F32_EDGES[case]
+    plan = g.Plan(M, N, K, "f32", out_dtype=od, batch_hint=nb, **epi)
+    d = _describe(plan)
+    say(f"[f32 edges] {plan.describe()}")
+    assert d["config"] == "f32d_256x256x16_w4x2_a3" and d["edge"] == edge
+    assert int(d["packed"]) == bits
+    dev = torch.device("cuda")
+    As = torch.stack([synth.uniform(2400 + 2 * b, (M, K), "f32") for b in range(nb)])
+    Bs = torch.stack([synth.uniform(2401 + 2 * b, (K, N), "f32") for b in range(nb)])
+    bias = synth.normal(2420, (N,), 0.5, "f32") if epi.get("bias") else None
+    resid = synth.uniform(2421, (M, N), od) if epi.get("resid") else None
+    for ws in (None, False):
+        if nb == 1:
+            C = gc.run_gpu(plan, As[0], Bs[0], bias, resid, workspace=ws)[None]
+        else:
+            C = plan.run_batched(As.to(dev), Bs.to(dev), None if bias is None else bias.to(dev),
+                                 out=gc.nan_out((nb, M, N), od), workspace=ws)
+            torch.cuda.synchronize()
+            C = C.cpu()
+        for b in range(nb):
+            r = gc.check_full(C[b], As[b], Bs[b], "f32", od, bias, resid, epi.get("scale"),
+                              epi.get("gelu", False), abs_max=1e-3 if od == "f32" else None)
+            assert r["ok"], (ws, b, r)
 
 
 def test_fp32_transposed_b(g):
