@@ -507,6 +507,12 @@ def baseline_configs(g, steps, warmup, head, f32):
     out["5_gemv_1x4096x4096"] = gemm_entry("gemv_1x4096x4096", "hbm")
     out["5_odd_127x1000x771"] = gemm_entry("odd_127x1000x771", "launch")
     out["5_odd_4095x4097x63"] = gemm_entry("odd_4095x4097x63", "hbm")
+    # what a plain device-to-device copy reaches on this machine, beside the HBM-bound rows
+    src = torch.empty(64 * 2**20, dtype=torch.float32, device=dev)  # 256 MiB
+    dst = torch.empty_like(src)
+    out["5_copy_reference_256MiB"] = entry(lambda: dst.copy_(src), 0, 2 * src.numel() * 4, "hbm",
+                                           "device copy (torch)", "f32")
+    del src, dst
     print(f"[bench] configs 5 {json.dumps({k: v for k, v in out.items() if k[0] == '5'})}",
           file=sys.stderr, flush=True)
     return out
