@@ -61,7 +61,7 @@ struct gemm_plan {
   int64_t lda_p;    // padded row lengths (elements) of the A and B copies
   int64_t ldb_p;
   int64_t pack_b_off;  // byte offset of the B copy in the workspace (the A copy is at 0)
-  // Thin edges (fp32 products whose M and N end a few rows / columns past a 256
+  // Thin edges (products whose M and N end a few rows / columns past a 256
   // boundary): the primary configuration runs the (M - edge_m) x (N - edge_n) block
   // in whole tiles, the few-row kernel `edge_gemv` (split edge_split, its partial
   // sums at edge_ws_off in the workspace) the last edge_m rows, and the few-column
@@ -405,16 +405,19 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
   double cost = 0;
   s.config = best_for(vec_a, vec_b, K, N, any, &cost);
   const bool pa = (K * es) % 16 != 0, pb = ((b_nk ? K : N) * es) % 16 != 0;
-  // fp32 products whose M and N end at most 8 rows / columns past a multiple of 256
-  // (4097^3) and whose whole-tile block fills every CU: whole tiles would leave a
-  // second round of one-row tiles, each as slow as a full one; the 256 x 256 SGEMM
-  // kernel takes the whole-tile block in full rounds and the few-row and few-column
-  // kernels the edges (operands copied into padded rows when theirs are not 16-byte
-  // multiples).
-  if (dtype == GEMM_F32 && !b_nk && aligned16 && K >= 256 && M % 256 <= 8 && N % 256 <= 8 &&
+  // Products whose M and N end at most 8 rows / columns past a multiple of 256 (4097^3)
+  // and whose whole-tile block fills every CU: whole tiles would leave a second round of
+  // one-row tiles, each as slow as a full one (bf16 4097^3 on the best tiling: 252 us
+  // against 116 us at 4096^3); the 256 x 256 kernel of the input type takes the
+  // whole-tile block in full rounds and the few-row and few-column kernels the edges
+  // (operands copied into padded rows when theirs are not 16-byte multiples).
+  if (!b_nk && aligned16 && K >= 256 && M % 256 <= 8 && N % 256 <= 8 &&
       M % 256 + N % 256 > 0 && (M / 256) * (N / 256) >= dev.cu_count) {
+    const std::string main_cfg = dtype == GEMM_F32 ? std::string("f32d_256x256x16_w4x2_a3")
+                                 : std::string("m16t_") + (dtype == GEMM_BF16 ? "bf16" : "f16") +
+                                       "_256x256x64_w2x4_a3_b2";
     for (size_t i = 0; i < all.size(); ++i)
-      if (std::strcmp(all[i].name, "f32d_256x256x16_w4x2_a3") == 0 &&
+      if (main_cfg == all[i].name &&
           cfg_fits(all[i], dtype, true, true, dev, M, N, round_up16B(K, es), epi.out_dtype)) {
         s.config = static_cast<int>(i);
         s.packed = (pa ? 1 : 0) | (pb ? 2 : 0);
@@ -599,14 +602,14 @@ int run_packed(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, con
   return GEMM_OK;
 }
 
-// Run of a plan with thin edges split off (fp32): per batch item, the padded copies
+// Run of a plan with thin edges split off: per batch item, the padded copies
 // (if any), the whole-tile block on the primary configuration, the last edge_m rows
 // on the few-row kernel (partial sums in the workspace) and the last edge_n columns of
 // the other rows on the few-column kernel. C, the residual and the bias are addressed
 // at the block's origin with C's full row stride.
 int run_edges(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, const void* B,
               int64_t sB, const float* bias, const void* resid, int64_t sR, void* C, int64_t sC,
-              void* ws, hipStream_t s) {
+              bool c16, void* ws, hipStream_t s) {
   const auto& all = registry().all;
   const KernelEntry& k = all[p->config];
   const int64_t ie = elem_bytes(p->dtype), oe = elem_bytes(p->epi.out_dtype);
@@ -635,20 +638,22 @@ int run_edges(const gemm_plan* p, int64_t batch, const void* A, int64_t sA, cons
     la.c_vec = 0;
     return la;
   };
+  auto pack = p->dtype == GEMM_F32 ? pack_rows32 : pack_rows16;
   for (int64_t z = 0; z < batch; ++z) {
     const char* Az = static_cast<const char*>(A) + z * sA * ie;
     const char* Bz = static_cast<const char*>(B) + z * sB * ie;
     char* Cz = static_cast<char*>(C) + z * sC * oe;
     const char* Rz = (p->epi.flags & GEMM_EPI_RESID) ? static_cast<const char*>(resid) + z * sR * oe
                                                      : nullptr;
-    if ((p->packed & 1) && pack_rows32(Az, p->M, p->K, pack_a, p->lda_p, s) != hipSuccess)
+    if ((p->packed & 1) && pack(Az, p->M, p->K, pack_a, p->lda_p, s) != hipSuccess)
       return GEMM_ERR_HIP;
-    if ((p->packed & 2) && pack_rows32(Bz, p->K, p->N, pack_b, p->ldb_p, s) != hipSuccess)
+    if ((p->packed & 2) && pack(Bz, p->K, p->N, pack_b, p->ldb_p, s) != hipSuccess)
       return GEMM_ERR_HIP;
     const char* Au = (p->packed & 1) ? static_cast<const char*>(pack_a) : Az;
     const char* Bu = (p->packed & 2) ? static_cast<const char*>(pack_b) : Bz;
     const int64_t lda = p->lda_p, ldb = p->ldb_p;  // K and N when not copied
     LaunchArgs la = base(M1, N1, p->K, Au, lda, Bu, ldb, Cz, Rz, bias);
+    la.c_vec = (c16 && p->N % 8 == 0) ? 1 : 0;  // 16-bit C rows 16-byte aligned: staged stores
     if (k.launch(la, s) != hipSuccess) return GEMM_ERR_HIP;
     if (p->edge_m > 0) {
       LaunchArgs lg = base(p->edge_m, p->N, p->K, Au + M1 * lda * ie, lda, Bu, ldb,
@@ -1034,7 +1039,7 @@ int gemm_run_strided_batched_ws(const gemm_plan* p, int64_t batch, const void* A
     const bool c_ok = aligned_to(C, 16) && (sC * oe) % 16 == 0 &&
                       (!(e.flags & GEMM_EPI_RESID) || (aligned_to(resid, 16) && (sR * oe) % 16 == 0));
     if (a_ok && b_ok && c_ok)
-      return run_edges(p, batch, A, sA, B, sB, bias, resid, sR, C, sC, ws, st);
+      return run_edges(p, batch, A, sA, B, sB, bias, resid, sR, C, sC, c16, ws, st);
   }
   if (p->packed && use_ws) {
     // operands that are not copied must still be 16-byte aligned for the kernel

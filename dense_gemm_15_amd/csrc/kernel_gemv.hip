@@ -211,16 +211,24 @@ __global__ __launch_bounds__(GNT) void gemv_kernel(LaunchArgs a, int64_t z0) {
 // Few columns (N <= 8: the strip of a product's last columns past a 256-column tile
 // boundary): C[m][j] = epi(sum_k A[m][k] B[k][j]), j < N. Workgroup: 8 rows, 2 per
 // wave (two workgroups per CU at 4096 rows; one row per wave measured slower, each
-// workgroup staging all of B's strip); K in chunks of KC. B's chunk (KC rows x 8 columns, zeros past N) goes through
-// two LDS buffers: while chunk c is summed, the loads of chunk c + 1's B (into
-// registers, written to the other buffer after the sums) and of chunk c + 1's A values
-// (lane l: k = l + 64 i of each of its wave's rows) are in flight. The 64 lanes'
-// sums of each (row, column) are then added across the wave and lane 0 applies the
-// epilogue. fp32 accumulation in a fixed order.
+// workgroup staging all of B's strip); K in chunks of KC = 512. Lane l takes
+// the EPL consecutive k at EPL (l + 64 i) of a chunk, one 16-byte load per row and i
+// (A's rows must hold whole 16-byte chunks up to roundup(K, EPL): zero-padded copies,
+// or K a multiple of EPL). B's chunk (KC rows x 8 columns, zeros past N and K; 16-byte
+// loads of each row's columns, so B's rows too must hold whole 16-byte chunks up to N
+// rounded up) goes through two LDS buffers, stored as [e][l][8] so that a lane's reads
+// are contiguous:
+// while chunk c is summed, the loads of chunk c + 1's B (into registers, written to the
+// other buffer after the sums) and A are in flight. The 64 lanes' sums of each (row,
+// column) are then added across the wave and lane 0 applies the epilogue. fp32
+// accumulation in a fixed order.
 template <typename T>
 __global__ __launch_bounds__(256) void gemv_cols_kernel(LaunchArgs a) {
-  constexpr int KC = 512, RW = 2, PER = KC / 64, BPT = KC * 8 / 256;
-  __shared__ float bs[2][KC][8];
+  constexpr int EPL = T::code == DT_F32 ? 4 : 8;  // elements per 16-byte load
+  constexpr int RW = 2, PER = 8 / EPL;             // KC = 512 rows of B per chunk
+  constexpr int H = 8 / EPL;  // 16-byte chunks of a B row's 8 columns
+  constexpr int KC = 64 * EPL * PER, BPT = KC * H / 256;
+  __shared__ float bs[2][PER][EPL][64][8];  // chunk row kk = EPL (l + 64 i) + e at [i][e][l]
   const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), K = static_cast<int>(a.K);
   const int64_t LDA = a.lda, LDB = a.ldb, LDC = a.ldc;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -229,31 +237,52 @@ __global__ __launch_bounds__(256) void gemv_cols_kernel(LaunchArgs a) {
   const char* Ap = static_cast<const char*>(a.A) + z * a.sA * in_bytes;
   const char* Bp = static_cast<const char*>(a.B) + z * a.sB * in_bytes;
   const int row0 = blockIdx.x * (4 * RW) + wave * RW;  // the same for the whole wave
+  const int kpad = (K + EPL - 1) / EPL * EPL;
+  __amdgpu_buffer_rsrc_t rA[RW];
+#pragma unroll
+  for (int r = 0; r < RW; ++r) {
+    const int m = row0 + r;
+    rA[r] = grsrc(Ap + static_cast<int64_t>(m < M ? m : 0) * LDA * in_bytes,
+                  m < M ? static_cast<uint32_t>(kpad * in_bytes) : 0u);
+  }
   float acc[RW][8];
 #pragma unroll
   for (int r = 0; r < RW; ++r)
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[r][j] = 0.f;
-  // thread t stages elements t + 256 q of a chunk: row (t + 256 q) / 8, column t % 8
-  float bq[BPT], av[RW][PER];
+  // B's chunk row kk: its 8 columns as H 16-byte loads (B's rows start on 16 bytes and
+  // hold whole chunks up to N rounded up); thread t takes loads t + 256 q (row / H,
+  // chunk % H); chunks wholly past N or rows past K are zeros
+  u32x4 bq[BPT];
+  u32x4 av[RW][PER];
   auto load_b = [&](int kc) {
 #pragma unroll
     for (int q = 0; q < BPT; ++q) {
-      const int kk = (tid + 256 * q) >> 3, j = tid & 7;
-      bq[q] = (kc + kk < K && j < N) ? gload<T>(Bp, static_cast<int64_t>(kc + kk) * LDB + j) : 0.f;
+      const int idx = tid + 256 * q, kk = idx / H, h = idx % H;
+      bq[q] = u32x4{0u, 0u, 0u, 0u};
+      if (kc + kk < K && h * EPL < N)
+        bq[q] = *reinterpret_cast<const u32x4*>(
+            Bp + (static_cast<int64_t>(kc + kk) * LDB + h * EPL) * in_bytes);
     }
   };
   auto store_b = [&](int buf) {
 #pragma unroll
-    for (int q = 0; q < BPT; ++q) bs[buf][(tid + 256 * q) >> 3][tid & 7] = bq[q];
+    for (int q = 0; q < BPT; ++q) {
+      const int idx = tid + 256 * q, kk = idx / H, h = idx % H;
+      const int e = kk % EPL, l = (kk / EPL) % 64, i = kk / (EPL * 64);
+      float x[EPL];
+      unpack<T>(bq[q], x);
+#pragma unroll
+      for (int c = 0; c < EPL; ++c) bs[buf][i][e][l][h * EPL + c] = x[c];
+    }
   };
   auto load_a = [&](int kc) {
 #pragma unroll
     for (int r = 0; r < RW; ++r)
 #pragma unroll
       for (int i = 0; i < PER; ++i) {
-        const int m = row0 + r, k = kc + lane + 64 * i;
-        av[r][i] = (m < M && k < K) ? gload<T>(Ap, static_cast<int64_t>(m) * LDA + k) : 0.f;
+        const uint32_t off = static_cast<uint32_t>((kc + EPL * (lane + 64 * i)) * in_bytes);
+        av[r][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rA[r], off, 0, 0));
       }
   };
   load_b(0);
@@ -264,7 +293,7 @@ __global__ __launch_bounds__(256) void gemv_cols_kernel(LaunchArgs a) {
     const bool more = kc + KC < K;
     if (more) load_b(kc + KC);  // in flight during this chunk's sums
     __syncthreads();            // chunk kc's B is in bs[buf]
-    float an[RW][PER];
+    u32x4 an[RW][PER];
 #pragma unroll
     for (int r = 0; r < RW; ++r)
 #pragma unroll
@@ -272,15 +301,21 @@ __global__ __launch_bounds__(256) void gemv_cols_kernel(LaunchArgs a) {
     if (more) load_a(kc + KC);
 #pragma unroll
     for (int i = 0; i < PER; ++i) {
-      const f32x4 b0 = *reinterpret_cast<const f32x4*>(&bs[buf][lane + 64 * i][0]);
-      const f32x4 b1 = *reinterpret_cast<const f32x4*>(&bs[buf][lane + 64 * i][4]);
+      float x[RW][EPL];
 #pragma unroll
-      for (int r = 0; r < RW; ++r)
+      for (int r = 0; r < RW; ++r) unpack<T>(an[r][i], x[r]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          acc[r][j] = __builtin_fmaf(an[r][i], b0[j], acc[r][j]);
-          acc[r][j + 4] = __builtin_fmaf(an[r][i], b1[j], acc[r][j + 4]);
-        }
+      for (int e = 0; e < EPL; ++e) {
+        const f32x4 b0 = *reinterpret_cast<const f32x4*>(&bs[buf][i][e][lane][0]);
+        const f32x4 b1 = *reinterpret_cast<const f32x4*>(&bs[buf][i][e][lane][4]);
+#pragma unroll
+        for (int r = 0; r < RW; ++r)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            acc[r][j] = __builtin_fmaf(x[r][e], b0[j], acc[r][j]);
+            acc[r][j + 4] = __builtin_fmaf(x[r][e], b1[j], acc[r][j + 4]);
+          }
+      }
     }
     if (more) store_b(buf ^ 1);  // every wave read bs[buf ^ 1] before this chunk's barrier
     buf ^= 1;
@@ -390,8 +425,12 @@ int gemv_entries(const KernelEntry** out) {
 }
 
 hipError_t launch_gemv_cols(const LaunchArgs& a, int in_dtype, hipStream_t s) {
+  const int64_t es = in_dtype == DT_F32 ? 4 : 2, epl = 16 / es;
   if (a.N < 1 || a.N > 8 || a.M < 1 || a.batch < 1 || a.batch > 65535 ||
-      (a.M + 7) / 8 > 0x7fffffff)
+      (a.M + 7) / 8 > 0x7fffffff || (a.lda * es) % 16 != 0 || (a.sA * es) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(a.A) % 16 != 0 || a.lda < (a.K + epl - 1) / epl * epl ||
+      a.K * es >= (int64_t(1) << 31) || (a.ldb * es) % 16 != 0 || (a.sB * es) % 16 != 0 ||
+      reinterpret_cast<uintptr_t>(a.B) % 16 != 0 || a.ldb < (a.N + epl - 1) / epl * epl)
     return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>((a.M + 7) / 8), static_cast<unsigned>(a.batch));
   if (in_dtype == DT_F32)

@@ -15,8 +15,10 @@ hipError_t launch_splitk_reduce(const LaunchArgs& a, int64_t z, int64_t rows, hi
 
 // Few columns: C[z][m][j] = epi(sum_k A[z][m][k] B[z][k][j]) for m < a.M, j < a.N <= 8,
 // A, B of type in_dtype (DT_*) with row strides a.lda, a.ldb, C and the residual with
-// row stride a.ldc, bias[j]; every batch item in one launch. hipErrorInvalidValue for
-// N outside 1..8 or another type.
+// row stride a.ldc, bias[j]; every batch item in one launch. A's and B's rows must start
+// on 16 bytes and hold whole 16-byte chunks up to K (A) and N (B) rounded up, zero past
+// K (padded copies, or K a multiple of 16 bytes); hipErrorInvalidValue otherwise, for N
+// outside 1..8 or another type.
 hipError_t launch_gemv_cols(const LaunchArgs& a, int in_dtype, hipStream_t s);
 
 }  // namespace g15

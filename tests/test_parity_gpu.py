@@ -836,32 +836,37 @@ def test_fp32_4097_cube(g):
     assert r["ok"], r
 
 
-F32_EDGES = [
-    # (M, N, K, batch, epilogue, out, edge, packed): fp32 products a few rows / columns
-    # past multiples of 256, the whole-tile block in one round
-    (4100, 4100, 4100, 1, dict(), "f32", "4,4", 0),
-    (4096, 4097, 1024, 1, dict(bias=True, gelu=True, resid=True), "bf16", "0,1", 2),
-    (4099, 4096, 600, 2, dict(scale=0.5, bias=True), "f32", "3,0", 0),
+EDGES = [
+    # (dtype, M, N, K, batch, epilogue, out, edge, packed): products a few rows / columns
+    # past multiples of 256, the whole-tile block in full rounds of 256 x 256 tiles
+    ("f32", 4100, 4100, 4100, 1, dict(), "f32", "4,4", 0),
+    ("f32", 4096, 4097, 1024, 1, dict(bias=True, gelu=True, resid=True), "bf16", "0,1", 2),
+    ("f32", 4099, 4096, 600, 2, dict(scale=0.5, bias=True), "f32", "3,0", 0),
+    ("bf16", 4097, 4097, 4097, 1, dict(), "f32", "1,1", 3),
+    ("f16", 4104, 4104, 1024, 1, dict(bias=True, gelu=True, resid=True), "f16", "8,8", 0),
+    ("bf16", 4096, 4097, 2048, 2, dict(scale=0.5), "bf16", "0,1", 2),
+    ("f16", 4099, 4096, 600, 1, dict(resid=True), "f32", "3,0", 0),
 ]
 
 
-@pytest.mark.parametrize("case", range(len(F32_EDGES)))
-def test_fp32_thin_edges(g, case):
-    """Thin edges split off: the whole-tile block on the 256 x 256 SGEMM kernel, the
-    last rows on the few-row kernel (partial sums in the workspace), the last columns
-    on the few-column kernel; aligned and padded operands, every epilogue stage into
-    16-bit C, a strided batch, and the same plan without a workspace (the whole product
-    on a plain configuration). Every element against the oracle (fp32 C also within
-    1e-3 absolute)."""
-    M, N, K, nb, epi, od, edge, bits = F32_EDGES[case]
-    plan = g.Plan(M, N, K, "f32", out_dtype=od, batch_hint=nb, **epi)
+@pytest.mark.parametrize("case", range(len(EDGES)))
+def test_thin_edges(g, case):
+    """Thin edges split off: the whole-tile block on the 256 x 256 kernel of the input
+    type (f32d, m16t), the last rows on the few-row kernel (partial sums in the
+    workspace), the last columns on the few-column kernel; aligned and padded operands,
+    every epilogue stage into 16-bit C (staged and register store forms), strided
+    batches, and the same plan without a workspace (the whole product on a plain
+    configuration). Every element against the oracle (fp32 also within 1e-3 absolute)."""
+    dt, M, N, K, nb, epi, od, edge, bits = EDGES[case]
+    plan = g.Plan(M, N, K, dt, out_dtype=od, batch_hint=nb, **epi)
     d = _describe(plan)
-    say(f"[f32 edges] {plan.describe()}")
-    assert d["config"] == "f32d_256x256x16_w4x2_a3" and d["edge"] == edge
+    say(f"[edges] {plan.describe()}")
+    main = "f32d_256x256x16_w4x2_a3" if dt == "f32" else f"m16t_{dt}_256x256x64_w2x4_a3_b2"
+    assert d["config"] == main and d["edge"] == edge
     assert int(d["packed"]) == bits
     dev = torch.device("cuda")
-    As = torch.stack([synth.uniform(2400 + 2 * b, (M, K), "f32") for b in range(nb)])
-    Bs = torch.stack([synth.uniform(2401 + 2 * b, (K, N), "f32") for b in range(nb)])
+    As = torch.stack([synth.uniform(2400 + 2 * b, (M, K), dt) for b in range(nb)])
+    Bs = torch.stack([synth.uniform(2401 + 2 * b, (K, N), dt) for b in range(nb)])
     bias = synth.normal(2420, (N,), 0.5, "f32") if epi.get("bias") else None
     resid = synth.uniform(2421, (M, N), od) if epi.get("resid") else None
     for ws in (None, False):
@@ -873,8 +878,9 @@ def test_fp32_thin_edges(g, case):
             torch.cuda.synchronize()
             C = C.cpu()
         for b in range(nb):
-            r = gc.check_full(C[b], As[b], Bs[b], "f32", od, bias, resid, epi.get("scale"),
-                              epi.get("gelu", False), abs_max=1e-3 if od == "f32" else None)
+            r = gc.check_full(C[b], As[b], Bs[b], dt, od, bias, resid, epi.get("scale"),
+                              epi.get("gelu", False),
+                              abs_max=1e-3 if (dt, od) == ("f32", "f32") else None)
             assert r["ok"], (ws, b, r)
 
 
