@@ -420,7 +420,7 @@ __global__ __launch_bounds__(64 * NW, 2) void attention_probs_kernel(LaunchArgs 
       zp = z;
       m0p = m0;
     } else {
-      store_tile<1, FN, BM, WTN, NW, static_cast<int>(sizeof(lds))>(
+      store_tile_rt<1, FN, BM, WTN, NW, static_cast<int>(sizeof(lds))>(
           out, acc, reinterpret_cast<float*>(lds), m0, 0, 0, wave, wave, lane, z);
     }
     z = zn;

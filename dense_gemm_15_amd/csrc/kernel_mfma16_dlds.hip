@@ -299,10 +299,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16d_kernel(LaunchArgs a)
   }
   if (kt < nk) slice(std::integral_constant<int, 0>{}, Tail{}, kt);
 
-  // ---- epilogue (store_tile)
+  // ---- epilogue (store_tile_rt)
   wait_vm<0>();
   lds_barrier();  // every wave is done with the operand ring; LDS is free
-  store_tile<FM, FN, WTM, WTN, NW, static_cast<int>(sizeof(lds))>(
+  store_tile_rt<FM, FN, WTM, WTN, NW, static_cast<int>(sizeof(lds))>(
       a, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, wave, lane, z);
 }
 

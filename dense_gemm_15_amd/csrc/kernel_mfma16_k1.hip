@@ -451,7 +451,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16s_kernel(LaunchArgs a)
         m0p = m0;
         n0p = n0;
       } else {
-        store_tile<FM, FN, WTM, WTN, NW, static_cast<int>(sizeof(lds))>(
+        store_tile_rt<FM, FN, WTM, WTN, NW, static_cast<int>(sizeof(lds))>(
             out, acc, reinterpret_cast<float*>(lds), m0, n0, wm, wn, wave, lane, z);
       }
       have = next;

@@ -86,20 +86,33 @@ struct WGeom {
   static_assert(RING <= 163840, "ring exceeds gfx950 LDS");
 };
 
-// Epilogue of a wave's WTM x WTN sub-tile of 16 x 16 blocks at tile (m0, n0). In
-// the accumulators lane l holds C[row][col] of block (i, j) with col = l % 16 and
-// row = 4 (l / 16) + r. Scale, bias and GELU are applied in registers, the residual
-// where the value is stored.
+// Epilogue of a wave's WTM x WTN sub-tile of 16 x 16 blocks at tile (m0, n0). The
+// matrix ops take the B fragment as their first operand, so each block accumulates
+// the transposed product and lane l holds four consecutive columns of one row:
+// C[row][col + t], t = 0 .. 3, row = 16 i + l % 16, col = 16 j + 4 (l / 16). Scale,
+// bias and GELU are applied in registers, the residual where the value is stored.
+// With 16-byte aligned C rows (a.c_vec: C, the residual and their rows on 16 bytes,
+// N % 8 == 0) a lane's four values leave as one 16-byte (fp32) or 8-byte (16-bit)
+// store straight from the registers; otherwise one element at a time.
 //
 // The residual and the output type are template parameters, chosen once per
 // launch: with a run-time residual test inside the store loop the compiler puts a
 // wait for every vector-memory operation in flight where the two paths join, and
 // on gfx950 stores count there too, so each block of stores would wait for the
 // previous block's to reach memory.
-__device__ __forceinline__ float epi_reg(const Epi& e, float v, float bias) {
-  if (e.flags & EPI_SCALE) v *= e.scale;
-  if (e.flags & EPI_BIAS) v += bias;
-  if (e.flags & EPI_GELU) v = gelu(v);
+// Scale, bias and GELU on a lane's four values of one block, each stage behind one
+// uniform branch per block (sc is the scale, or 1 without EPI_SCALE; the bias reads
+// as 0 without EPI_BIAS): with one wave per SIMD, per-element tests and selects in
+// the store sequence cost more than the stores.
+__device__ __forceinline__ f32x4 epi_block(const Epi& e, f32x4 v, f32x4 bias, float sc) {
+  if (e.flags & (EPI_SCALE | EPI_BIAS)) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = v[t] * sc + bias[t];
+  }
+  if (e.flags & EPI_GELU) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = gelu(v[t]);
+  }
   return v;
 }
 
@@ -113,194 +126,122 @@ __device__ __forceinline__ float widen_out(uint32_t h) {
                         : widen(f16_t{}, static_cast<uint16_t>(h));
 }
 
-// One store per element (fp32), or per pair of columns after an exchange between
-// neighbouring lanes (16-bit, even LDC and N), else per element.
 template <int FM, int FN, int WTM, int WTN, bool HAS_R, int OUT>
 __device__ __forceinline__ void store_tile_w(const LaunchArgs& a, f32x4 (&acc)[FM][FN], int m0,
                                              int n0, int wm, int wn, int lane, int64_t z) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), LDC = static_cast<int>(a.ldc);
-  const int lcol = lane & 15, lg = lane >> 4;
+  const int lr = lane & 15, lg = lane >> 4;
   const Epi& e = a.epi;
   constexpr int ob = OUT == DT_F32 ? 4 : 2;
   char* Cz = static_cast<char*>(a.C) + z * a.sC * ob;
   const char* Rz = HAS_R ? static_cast<const char*>(e.resid) + z * a.sR * ob : Cz;
   const auto rC = rsrc(Cz, static_cast<uint32_t>(static_cast<int64_t>(M) * LDC * ob));
   const auto rR = rsrc(Rz, static_cast<uint32_t>(static_cast<int64_t>(M) * LDC * ob));
-  float bj[FN];
+  const int row0 = m0 + wm * WTM + lr;      // + 16 i
+  const int col0 = n0 + wn * WTN + 4 * lg;  // + 16 j + t
+  // bias through a buffer descriptor: columns past N read as 0 with no branch (a
+  // guarded load per element puts 32 divergent regions into the epilogue)
+  f32x4 bj[FN];
+  const auto rB = rsrc(e.bias, (e.flags & EPI_BIAS) ? static_cast<uint32_t>(N) * 4u : 0u);
+  const float sc = (e.flags & EPI_SCALE) ? e.scale : 1.f;
 #pragma unroll
   for (int j = 0; j < FN; ++j) {
-    const int col = n0 + wn * WTN + 16 * j + lcol;
-    bj[j] = ((e.flags & EPI_BIAS) && col < N) ? e.bias[col] : 0.f;
-  }
-  if constexpr (OUT == DT_F32) {
+    const uint32_t col = static_cast<uint32_t>(col0 + 16 * j);
+    if (a.c_vec) {  // N % 8 == 0: the four columns lie wholly inside or past N
+      bj[j] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rB, col * 4u, 0, 0));
+    } else {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
+      for (int t = 0; t < 4; ++t)
+        bj[j][t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rB, (col + t) * 4u, 0, 0));
+    }
+  }
+  if (a.c_vec) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int row = row0 + 16 * i;
+      uint32_t off[FN];
+      u32x4 res[FN];
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int cl = n0 + wn * WTN + 16 * j + lcol;
-        const int rb = m0 + wm * WTM + 16 * i + 4 * lg;
-        uint32_t off[4];
-        float rv[4];
+        const int col = col0 + 16 * j;  // N % 8 == 0: col < N covers col + 3
+        off[j] = (row < M && col < N) ? static_cast<uint32_t>(row * LDC + col) * ob : OOB;
+        if constexpr (HAS_R) {  // the block row's residual loads all in flight at once
+          if constexpr (OUT == DT_F32) {
+            res[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rR, off[j], 0, 0));
+          } else {
+            const u32x2 h = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rR, off[j], 0, 0));
+            res[j] = u32x4{h[0], h[1], 0u, 0u};
+          }
+        }
+      }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          off[r] = (rb + r < M && cl < N) ? static_cast<uint32_t>((rb + r) * LDC + cl) * 4u : OOB;
+      for (int j = 0; j < FN; ++j) {
+        f32x4 v = epi_block(e, acc[i][j], bj[j], sc);
+        if constexpr (OUT == DT_F32) {
           if constexpr (HAS_R)
-            rv[r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rR, off[r], 0, 0));
-        }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          float v = epi_reg(e, acc[i][j][r], bj[j]);
-          if constexpr (HAS_R) v += rv[r];
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rC, off[r], 0, 0);
-        }
-      }
-    return;
-  } else {
-    // registers 2p, 2p+1 are rows R, R+1 of one column; lanes l, l^1 hold neighbouring
-    // columns: after one exchange the even lane has columns (c, c+1) of row R and the
-    // odd lane those of row R+1
-    const bool odd = (lane & 1) != 0;
-    const bool pairs = ((LDC | N) & 1) == 0;
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int cl = n0 + wn * WTN + 16 * j + lcol;
-        const int rb = m0 + wm * WTM + 16 * i + 4 * lg;
-        float v[4];
-#pragma unroll
-        for (int r = 0; r < 4; ++r) v[r] = epi_reg(e, acc[i][j][r], bj[j]);
-        if (pairs) {
-          const int ce = cl & ~1;
-          uint32_t off[2], res[2];
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            const int row = rb + 2 * p + (odd ? 1 : 0);
-            off[p] = (row < M && ce < N) ? static_cast<uint32_t>(row * LDC + ce) * 2u : OOB;
-            if constexpr (HAS_R) res[p] = __builtin_amdgcn_raw_buffer_load_b32(rR, off[p], 0, 0);
-          }
-#pragma unroll
-          for (int p = 0; p < 2; ++p) {
-            // DPP quad_perm [1, 0, 3, 2]: each lane receives its neighbour's value
-            const float recv = __int_as_float(__builtin_amdgcn_mov_dpp(
-                __float_as_int(odd ? v[2 * p] : v[2 * p + 1]), 0xB1, 0xF, 0xF, false));
-            float lo = odd ? recv : v[2 * p];
-            float hi = odd ? v[2 * p + 1] : recv;
-            if constexpr (HAS_R) {
-              lo += widen_out<OUT>(res[p] & 0xffffu);
-              hi += widen_out<OUT>(res[p] >> 16);
-            }
-            const uint32_t w = static_cast<uint32_t>(narrow_out<OUT>(lo)) |
-                               (static_cast<uint32_t>(narrow_out<OUT>(hi)) << 16);
-            __builtin_amdgcn_raw_buffer_store_b32(w, rC, off[p], 0, 0);
-          }
+            for (int t = 0; t < 4; ++t) v[t] += __uint_as_float(res[j][t]);
+          __builtin_amdgcn_raw_buffer_store_b128(
+              u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                    __float_as_uint(v[3])},
+              rC, off[j], 0, 0);
         } else {
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int row = rb + r;
-            const uint32_t o = (row < M && cl < N) ? static_cast<uint32_t>(row * LDC + cl) * 2u : OOB;
-            float x = v[r];
-            if constexpr (HAS_R) x += widen_out<OUT>(__builtin_amdgcn_raw_buffer_load_b16(rR, o, 0, 0));
-            __builtin_amdgcn_raw_buffer_store_b16(narrow_out<OUT>(x), rC, o, 0, 0);
+          if constexpr (HAS_R) {
+            v[0] += widen_out<OUT>(res[j][0] & 0xffffu);
+            v[1] += widen_out<OUT>(res[j][0] >> 16);
+            v[2] += widen_out<OUT>(res[j][1] & 0xffffu);
+            v[3] += widen_out<OUT>(res[j][1] >> 16);
           }
+          const u32x2 w{static_cast<uint32_t>(narrow_out<OUT>(v[0])) |
+                            (static_cast<uint32_t>(narrow_out<OUT>(v[1])) << 16),
+                        static_cast<uint32_t>(narrow_out<OUT>(v[2])) |
+                            (static_cast<uint32_t>(narrow_out<OUT>(v[3])) << 16)};
+          __builtin_amdgcn_raw_buffer_store_b64(w, rC, off[j], 0, 0);
         }
       }
+    }
+    return;
   }
-}
-
-// The same epilogue staged through LDS when C (and the residual) rows are 16-byte
-// aligned and N % 8 == 0 (a.c_vec): each wave writes 16 rows of its sub-tile at a
-// time into its own LDS area (fp32, rows padded by 4 floats: the 64 lanes of one
-// write touch 4 rows x 16 columns on 64 distinct banks) and reads them back as 4
-// (fp32 C) or 8 (16-bit C) consecutive columns per lane, so every C store writes
-// whole 512-byte (fp32) or 256-byte (16-bit) row runs in 16-byte pieces.
-// stg: the wave's area, 16 (WTN + 4) floats; every wave must be done with the
-// main loop's use of LDS.
-template <int FM, int FN, int WTM, int WTN, bool HAS_R, int OUT>
-__device__ __forceinline__ void store_tile_w_staged(const LaunchArgs& a, f32x4 (&acc)[FM][FN],
-                                                    float* stg, int m0, int n0, int wm, int wn,
-                                                    int lane, int64_t z) {
-  constexpr int EP = WTN + 4;
-  constexpr int ob = OUT == DT_F32 ? 4 : 2;
-  constexpr int CPL = OUT == DT_F32 ? 4 : 8;                // columns per lane
-  constexpr int LPR = WTN / CPL, RPP = 64 / LPR, PASSES = 16 / RPP;
-  static_assert(64 % LPR == 0 && 16 % RPP == 0, "staged store passes");
-  const int M = static_cast<int>(a.M), N = static_cast<int>(a.N), LDC = static_cast<int>(a.ldc);
-  const int lcol = lane & 15, lg = lane >> 4;
-  const Epi& e = a.epi;
-  char* Cz = static_cast<char*>(a.C) + z * a.sC * ob;
-  const char* Rz = HAS_R ? static_cast<const char*>(e.resid) + z * a.sR * ob : Cz;
-  const auto rC = rsrc(Cz, static_cast<uint32_t>(static_cast<int64_t>(M) * LDC * ob));
-  const auto rR = rsrc(Rz, static_cast<uint32_t>(static_cast<int64_t>(M) * LDC * ob));
-  float bj[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int col = n0 + wn * WTN + 16 * j + lcol;
-    bj[j] = ((e.flags & EPI_BIAS) && col < N) ? e.bias[col] : 0.f;
-  }
-  const int row0 = m0 + wm * WTM, col0 = n0 + wn * WTN;
-  const int lrow = lane / LPR, lc = CPL * (lane % LPR);  // this lane's row and column in a pass
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
+    const int row = row0 + 16 * i;
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
+    for (int j = 0; j < FN; ++j) {
+      uint32_t off[4];
+      float rv[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r)
-        stg[(4 * lg + r) * EP + 16 * j + lcol] = epi_reg(e, acc[i][j][r], bj[j]);
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // the wave's staging writes are done
-    const int rb = row0 + 16 * i;
-    uint32_t off[PASSES];
-    u32x4 res[PASSES];
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const int row = p * RPP + lrow;
-      off[p] = (rb + row < M && col0 + lc < N)
-                   ? static_cast<uint32_t>((rb + row) * LDC + col0 + lc) * ob : OOB;
-      if constexpr (HAS_R)
-        res[p] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rR, off[p], 0, 0));
-    }
-#pragma unroll
-    for (int p = 0; p < PASSES; ++p) {
-      const float* src = stg + (p * RPP + lrow) * EP + lc;
-      if constexpr (OUT == DT_F32) {
-        f32x4 v = *reinterpret_cast<const f32x4*>(src);
-        if constexpr (HAS_R)
-#pragma unroll
-          for (int t = 0; t < 4; ++t) v[t] += __uint_as_float(res[p][t]);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rC, off[p], 0, 0);
-      } else {
-        const f32x4 lo = *reinterpret_cast<const f32x4*>(src);
-        const f32x4 hi = *reinterpret_cast<const f32x4*>(src + 4);
-        const float v[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        uint32_t w[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          float x0 = v[2 * t], x1 = v[2 * t + 1];
-          if constexpr (HAS_R) {
-            x0 += widen_out<OUT>(res[p][t] & 0xffffu);
-            x1 += widen_out<OUT>(res[p][t] >> 16);
-          }
-          w[t] = static_cast<uint32_t>(narrow_out<OUT>(x0)) |
-                 (static_cast<uint32_t>(narrow_out<OUT>(x1)) << 16);
+      for (int t = 0; t < 4; ++t) {
+        const int col = col0 + 16 * j + t;
+        off[t] = (row < M && col < N) ? static_cast<uint32_t>(row * LDC + col) * ob : OOB;
+        if constexpr (HAS_R) {
+          if constexpr (OUT == DT_F32)
+            rv[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rR, off[t], 0, 0));
+          else
+            rv[t] = widen_out<OUT>(__builtin_amdgcn_raw_buffer_load_b16(rR, off[t], 0, 0));
         }
-        __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, rC, off[p], 0, 0);
+      }
+      const f32x4 vb = epi_block(e, acc[i][j], bj[j], sc);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float v = vb[t];
+        if constexpr (HAS_R) v += rv[t];
+        if constexpr (OUT == DT_F32)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rC, off[t], 0, 0);
+        else
+          __builtin_amdgcn_raw_buffer_store_b16(narrow_out<OUT>(v), rC, off[t], 0, 0);
       }
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");  // reads done before the next block row
   }
 }
 
 // Dispatch of the epilogue on (residual, output type), once per launch.
 template <int FM, int FN, int WTM, int WTN>
-__device__ __forceinline__ void store_w(const LaunchArgs& a, f32x4 (&acc)[FM][FN], float* stg,
-                                        int m0, int n0, int wm, int wn, int lane, int64_t z) {
+__device__ __forceinline__ void store_w(const LaunchArgs& a, f32x4 (&acc)[FM][FN], int m0, int n0,
+                                        int wm, int wn, int lane, int64_t z) {
   auto go = [&](auto HR, auto OD) __attribute__((always_inline)) {
-    constexpr bool hr = decltype(HR)::value;
-    constexpr int od = decltype(OD)::value;
-    if (a.c_vec)
-      store_tile_w_staged<FM, FN, WTM, WTN, hr, od>(a, acc, stg, m0, n0, wm, wn, lane, z);
-    else
-      store_tile_w<FM, FN, WTM, WTN, hr, od>(a, acc, m0, n0, wm, wn, lane, z);
+    store_tile_w<FM, FN, WTM, WTN, decltype(HR)::value, decltype(OD)::value>(a, acc, m0, n0, wm,
+                                                                             wn, lane, z);
   };
   auto by_out = [&](auto HR) __attribute__((always_inline)) {
     if (a.epi.out_dtype == DT_F32)
@@ -499,7 +440,8 @@ void gemm_m16w_kernel(LaunchArgs a) {
     const int k0 = (kt + R) * WBK;
     static_for<0, NM>([&](auto QC) __attribute__((always_inline)) {
       constexpr int q = decltype(QC)::value;
-      acc[q / FN][q % FN] = mma16<T>(cur.a[q / FN], cur.b[q % FN], acc[q / FN][q % FN]);
+      // B fragment first: the block accumulates C^T (rows along the lanes)
+      acc[q / FN][q % FN] = mma16<T>(cur.b[q % FN], cur.a[q / FN], acc[q / FN][q % FN]);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (q == Q0 - 1) {
         wait_vm<(R - 2) * NV>();
@@ -544,11 +486,8 @@ void gemm_m16w_kernel(LaunchArgs a) {
     step(std::false_type{}, fy, fx);
   }
 
-  wait_vm<0>();
-  lds_barrier();  // every wave is done with the ring; LDS is free
-  static_assert(4 * 16 * (WTN + 4) * 4 <= G::RING, "staging must fit in LDS");
-  store_w<FM, FN, WTM, WTN>(a, acc, reinterpret_cast<float*>(lds) + wave * 16 * (WTN + 4), m0, n0,
-                            wm, wn, lane, z);
+  wait_vm<0>();  // no direct load still writing LDS when the wave ends
+  store_w<FM, FN, WTM, WTN>(a, acc, m0, n0, wm, wn, lane, z);
 }
 
 template <typename T, int BM, int BN, int R, bool BROW>

@@ -698,9 +698,9 @@ W_CONFIGS = [c for c in CONFIGS if c.startswith("m16w")]
 @pytest.mark.parametrize("name", W_CONFIGS)
 def test_epilogues_each_m16w(g, name):
     """The one-wave-per-SIMD kernels with every epilogue stage and output type:
-    16-byte-aligned C rows with N % 8 == 0 (the LDS-staged store), and for B given
-    transposed also N even but not a multiple of 8 (two columns per lane) and N odd
-    (one element per lane); K with a ragged 32-deep tail. Every element."""
+    16-byte-aligned C rows with N % 8 == 0 (a lane's four columns in one vector
+    store), and for B given transposed also N even but not a multiple of 8 and N odd
+    (one element at a time); K with a ragged 32-deep tail. Every element."""
     dtype = _dtype_of(name)
     nk = name.endswith("_nk")
     cases = [(300, 264, 200, dict(bias=True, gelu=True, out_dtype="bf16")),
