@@ -90,6 +90,30 @@ __device__ __forceinline__ float gelu(float v) {
   return v * phi;
 }
 
+// GELU for results that are rounded to 16 bits (bf16 / fp16 output), about half
+// the VALU work of gelu(): with h = erfc(|v| / sqrt 2) / 2, GELU(v) = v (1 - h) for
+// v >= 0 and v h below, i.e. max(v, 0) - |v| h in both cases (no select). With
+// s = 1 / (2 + |v| / sqrt 2) (= t / 2 in the form above), |v| h = (|v| s) 2^(-log2(e) v^2 / 2
+// + Q(s)), where Q is a degree-5 polynomial fitted (minimax, erfc_fit16.py beside
+// this file) to log2(erfc(z) / 2s) + log2(e) z^2 over all z >= 0: erfc to 5.1e-5
+// relative, GELU to 2.5e-5 |v| absolute and 6.1e-5 relative, a few percent of the
+// 16-bit rounding step. One reciprocal, one base-2 exponential, eight fused
+// multiply-adds / multiplies, a min and a max. GELU(+inf) = +inf, GELU(-inf) = 0.
+__device__ __forceinline__ float gelu16(float v) {
+  const float av = __builtin_fabsf(v);
+  const float s = __builtin_amdgcn_rcpf(__builtin_fmaf(av, 0.70710678f, 2.0f));
+  float p = 8.29845524f;
+  p = __builtin_fmaf(p, s, -13.1949415f);
+  p = __builtin_fmaf(p, s, 3.82766771f);
+  p = __builtin_fmaf(p, s, 1.85619426f);
+  p = __builtin_fmaf(p, s, 2.89719629f);
+  p = __builtin_fmaf(p, s, -1.82582092f);
+  const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(v, v * -0.72134752f, p));
+  // |v| s tends to sqrt 2; the min keeps it finite (inf * 0) for infinite v
+  const float q = __builtin_fminf(av * s, 1.41421356f);
+  return __builtin_fmaf(-q, e, __builtin_fmaxf(v, 0.f));
+}
+
 __device__ __forceinline__ float load_out_elem(const void* p, int dt, int64_t idx) {
   if (dt == DT_F32) return static_cast<const float*>(p)[idx];
   const uint16_t h = static_cast<const uint16_t*>(p)[idx];

@@ -103,7 +103,8 @@ struct WGeom {
 // Scale, bias and GELU on a lane's four values of one block, each stage behind one
 // uniform branch per block (sc is the scale, or 1 without EPI_SCALE; the bias reads
 // as 0 without EPI_BIAS): with one wave per SIMD, per-element tests and selects in
-// the store sequence cost more than the stores.
+// the store sequence cost more than the stores. 16-bit results take gelu16.
+template <int OUT>
 __device__ __forceinline__ f32x4 epi_block(const Epi& e, f32x4 v, f32x4 bias, float sc) {
   if (e.flags & (EPI_SCALE | EPI_BIAS)) {
 #pragma unroll
@@ -111,7 +112,7 @@ __device__ __forceinline__ f32x4 epi_block(const Epi& e, f32x4 v, f32x4 bias, fl
   }
   if (e.flags & EPI_GELU) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) v[t] = gelu(v[t]);
+    for (int t = 0; t < 4; ++t) v[t] = OUT == DT_F32 ? gelu(v[t]) : gelu16(v[t]);
   }
   return v;
 }
@@ -177,7 +178,7 @@ __device__ __forceinline__ void store_tile_w(const LaunchArgs& a, f32x4 (&acc)[F
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        f32x4 v = epi_block(e, acc[i][j], bj[j], sc);
+        f32x4 v = epi_block<OUT>(e, acc[i][j], bj[j], sc);
         if constexpr (OUT == DT_F32) {
           if constexpr (HAS_R)
 #pragma unroll
@@ -221,7 +222,7 @@ __device__ __forceinline__ void store_tile_w(const LaunchArgs& a, f32x4 (&acc)[F
             rv[t] = widen_out<OUT>(__builtin_amdgcn_raw_buffer_load_b16(rR, off[t], 0, 0));
         }
       }
-      const f32x4 vb = epi_block(e, acc[i][j], bj[j], sc);
+      const f32x4 vb = epi_block<OUT>(e, acc[i][j], bj[j], sc);
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         float v = vb[t];

@@ -106,7 +106,7 @@ __device__ __forceinline__ float widen16(uint32_t h) {
 // compiler wait for every store in flight where the paths join). Scale and bias
 // are one multiply-add per element (sc = 1 without EPI_SCALE; the bias reads as 0
 // without EPI_BIAS, through a buffer descriptor, so no guarded loads), and each
-// stage is one uniform branch per block.
+// stage is one uniform branch per block. 16-bit results take gelu16.
 template <int FM, int FN, int WTM, int WTN, int NW, int LDS_BYTES, int OUT, bool HAS_R>
 __device__ __forceinline__ void store_tile_t(const LaunchArgs& a, f32x16 (&acc)[FM][FN],
                                              float* lds_f, int m0, int n0, int wm, int wn,
@@ -135,7 +135,7 @@ __device__ __forceinline__ void store_tile_t(const LaunchArgs& a, f32x16 (&acc)[
     }
     if (e.flags & EPI_GELU) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) v[r] = gelu(v[r]);
+      for (int r = 0; r < 16; ++r) v[r] = OUT == DT_F32 ? gelu(v[r]) : gelu16(v[r]);
     }
   };
 
