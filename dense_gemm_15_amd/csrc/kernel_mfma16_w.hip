@@ -117,15 +117,6 @@ __device__ __forceinline__ f32x4 epi_block(const Epi& e, f32x4 v, f32x4 bias, fl
   return v;
 }
 
-template <int OUT>
-__device__ __forceinline__ uint16_t narrow_out(float x) {
-  return OUT == DT_BF16 ? narrow_bf16(x) : narrow_f16(x);
-}
-template <int OUT>
-__device__ __forceinline__ float widen_out(uint32_t h) {
-  return OUT == DT_BF16 ? widen(bf16_t{}, static_cast<uint16_t>(h))
-                        : widen(f16_t{}, static_cast<uint16_t>(h));
-}
 
 template <int FM, int FN, int WTM, int WTN, bool HAS_R, int OUT>
 __device__ __forceinline__ void store_tile_w(const LaunchArgs& a, f32x4 (&acc)[FM][FN], int m0,
@@ -189,15 +180,12 @@ __device__ __forceinline__ void store_tile_w(const LaunchArgs& a, f32x4 (&acc)[F
               rC, off[j], 0, 0);
         } else {
           if constexpr (HAS_R) {
-            v[0] += widen_out<OUT>(res[j][0] & 0xffffu);
-            v[1] += widen_out<OUT>(res[j][0] >> 16);
-            v[2] += widen_out<OUT>(res[j][1] & 0xffffu);
-            v[3] += widen_out<OUT>(res[j][1] >> 16);
+            v[0] += widen16<OUT>(res[j][0] & 0xffffu);
+            v[1] += widen16<OUT>(res[j][0] >> 16);
+            v[2] += widen16<OUT>(res[j][1] & 0xffffu);
+            v[3] += widen16<OUT>(res[j][1] >> 16);
           }
-          const u32x2 w{static_cast<uint32_t>(narrow_out<OUT>(v[0])) |
-                            (static_cast<uint32_t>(narrow_out<OUT>(v[1])) << 16),
-                        static_cast<uint32_t>(narrow_out<OUT>(v[2])) |
-                            (static_cast<uint32_t>(narrow_out<OUT>(v[3])) << 16)};
+          const u32x2 w{pack16<OUT>(v[0], v[1]), pack16<OUT>(v[2], v[3])};
           __builtin_amdgcn_raw_buffer_store_b64(w, rC, off[j], 0, 0);
         }
       }
@@ -219,7 +207,7 @@ __device__ __forceinline__ void store_tile_w(const LaunchArgs& a, f32x4 (&acc)[F
           if constexpr (OUT == DT_F32)
             rv[t] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rR, off[t], 0, 0));
           else
-            rv[t] = widen_out<OUT>(__builtin_amdgcn_raw_buffer_load_b16(rR, off[t], 0, 0));
+            rv[t] = widen16<OUT>(__builtin_amdgcn_raw_buffer_load_b16(rR, off[t], 0, 0));
         }
       }
       const f32x4 vb = epi_block<OUT>(e, acc[i][j], bj[j], sc);
@@ -230,7 +218,7 @@ __device__ __forceinline__ void store_tile_w(const LaunchArgs& a, f32x4 (&acc)[F
         if constexpr (OUT == DT_F32)
           __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rC, off[t], 0, 0);
         else
-          __builtin_amdgcn_raw_buffer_store_b16(narrow_out<OUT>(v), rC, off[t], 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(narrow16<OUT>(v), rC, off[t], 0, 0);
       }
     }
   }

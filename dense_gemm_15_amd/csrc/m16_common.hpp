@@ -94,6 +94,23 @@ template <int OUT>
 __device__ __forceinline__ uint16_t narrow16(float x) {
   return OUT == DT_BF16 ? narrow_bf16(x) : narrow_f16(x);
 }
+// Two values rounded to OUT in one instruction (v_cvt_pk_bf16_f32 /
+// v_cvt_pk_f16_f32, the conversion narrow16 uses): x0 in the low half.
+template <int OUT>
+__device__ __forceinline__ uint32_t pack16(float x0, float x1) {
+  typedef float f32x2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  uint32_t w;
+  if constexpr (OUT == DT_BF16) {
+    const bf16x2 r = __builtin_convertvector(f32x2{x0, x1}, bf16x2);
+    __builtin_memcpy(&w, &r, 4);
+  } else {
+    const f16x2 r = __builtin_convertvector(f32x2{x0, x1}, f16x2);
+    __builtin_memcpy(&w, &r, 4);
+  }
+  return w;
+}
 template <int OUT>
 __device__ __forceinline__ float widen16(uint32_t h) {
   return OUT == DT_BF16 ? widen(bf16_t{}, static_cast<uint16_t>(h))
@@ -201,9 +218,7 @@ __device__ __forceinline__ void store_tile_t(const LaunchArgs& a, f32x16 (&acc)[
                 lo += widen16<OUT>(res[p] & 0xffffu);
                 hi += widen16<OUT>(res[p] >> 16);
               }
-              const uint32_t w = static_cast<uint32_t>(narrow16<OUT>(lo)) |
-                                 (static_cast<uint32_t>(narrow16<OUT>(hi)) << 16);
-              __builtin_amdgcn_raw_buffer_store_b32(w, rC, off[p], 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(pack16<OUT>(lo, hi), rC, off[p], 0, 0);
             }
           } else {
 #pragma unroll
@@ -264,8 +279,7 @@ __device__ __forceinline__ void store_tile_t(const LaunchArgs& a, f32x16 (&acc)[
             x0 += widen16<OUT>(res[p][t] & 0xffffu);
             x1 += widen16<OUT>(res[p][t] >> 16);
           }
-          w[t] = static_cast<uint32_t>(narrow16<OUT>(x0)) |
-                 (static_cast<uint32_t>(narrow16<OUT>(x1)) << 16);
+          w[t] = pack16<OUT>(x0, x1);
         }
         __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, rC, off[p], 0, 0);
       }
