@@ -147,8 +147,10 @@ int oracle_ulp16_n(int dtype, const double* x, int64_t n, double* out) {
   return 0;
 }
 
-/* GELU(v) = v * Phi(v), Phi the standard normal CDF = (1 + erf(v/sqrt2)) / 2. */
-double oracle_gelu(double v) { return 0.5 * v * (1.0 + erf(v / sqrt(2.0))); }
+/* GELU(v) = v * Phi(v), Phi the standard normal CDF = (1 + erf(v/sqrt2)) / 2, evaluated
+   as erfc(-v/sqrt2) / 2 (the same function: 1 + erf(x) = erfc(-x)), which keeps full
+   relative accuracy in the negative tail where 1 + erf cancels. */
+double oracle_gelu(double v) { return 0.5 * v * erfc(-v / sqrt(2.0)); }
 
 static double epilogue(double acc, unsigned flags, double scale, const float* bias, int64_t j,
                        int resid_dtype, const void* resid, int64_t ij) {

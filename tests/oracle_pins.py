@@ -106,11 +106,16 @@ def pin_ulp16(lib):
 # ---------------------------------------------------------------------- GELU --
 
 def pin_gelu(lib):
-    """GELU(x) = x Phi(x) against scipy's normal CDF; GELU(x) - GELU(-x) = x."""
+    """GELU(x) = x Phi(x) against scipy's normal CDF; GELU(x) - GELU(-x) = x; and full
+    relative accuracy in the negative tail, where Phi is tiny (scipy's normal CDF is
+    accurate there; a 1 + erf form loses every digit below about x = -8)."""
     xs = np.linspace(-8, 8, 641)
     got = np.array([oracle.gelu(x, lib=lib) for x in xs])
     want = xs * norm.cdf(xs)
     assert np.allclose(got, want, rtol=1e-14, atol=1e-15)
+    tail = -np.linspace(1.0, 37.0, 361)
+    got = np.array([oracle.gelu(x, lib=lib) for x in tail])
+    assert np.allclose(got, tail * norm.cdf(tail), rtol=1e-12, atol=0.0)
     odd = np.array([oracle.gelu(x, lib=lib) - oracle.gelu(-x, lib=lib) for x in xs])
     assert np.allclose(odd, xs, rtol=1e-14, atol=1e-15)
     assert oracle.gelu(0.0, lib=lib) == 0.0

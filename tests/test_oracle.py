@@ -39,8 +39,9 @@ MUTANTS = [
      "for (int64_t k = 0; k + 1 < K; ++k) {\n      const double p"),
     ("signed_abs_sum", "s[j] += fabs(p);", "s[j] += p;"),
     ("bias_wrong_index", "v += (double)bias[j];", "v += (double)bias[0];"),
-    ("gelu_no_sqrt2", "erf(v / sqrt(2.0))", "erf(v)"),
-    ("gelu_tanh_form", "0.5 * v * (1.0 + erf(v / sqrt(2.0)))",
+    ("gelu_no_sqrt2", "erfc(-v / sqrt(2.0))", "erfc(-v)"),
+    ("gelu_one_plus_erf", "0.5 * v * erfc(-v / sqrt(2.0))", "0.5 * v * (1.0 + erf(v / sqrt(2.0)))"),
+    ("gelu_tanh_form", "0.5 * v * erfc(-v / sqrt(2.0))",
      "0.5 * v * (1.0 + tanh(0.7978845608 * (v + 0.044715 * v * v * v)))"),
     ("scale_after_bias", "if (flags & OR_SCALE) v = scale * v;\n  if (flags & OR_BIAS) v += (double)bias[j];",
      "if (flags & OR_BIAS) v += (double)bias[j];\n  if (flags & OR_SCALE) v = scale * v;"),

@@ -1001,3 +1001,52 @@ def test_poison_mode(g, monkeypatch):
     for b in range(5):
         r = gc.check_full(S[b].cpu(), Q[b], Kt[b], "bf16")
         assert r["ok"], (b, r)
+
+
+GELU_RANGE_CONFIGS = ["m16t_bf16_128x128x64_w2x2_a2_b2", "m16w_bf16_256x128x32_r6",
+                      "m16d_bf16_64x128x64_w2x2_a4_b4_r2", "m16s_bf16_128x128x64_w2x2"]
+
+
+@pytest.mark.parametrize("name", GELU_RANGE_CONFIGS)
+@pytest.mark.parametrize("od", ["f32", "bf16", "f16"])
+def test_gelu_epilogue_range(g, name, od):
+    """The GELU epilogue over its whole range, on each epilogue form (per-launch variants
+    with the 16-bit GELU, the one-wave-per-SIMD form, the one-body form): A and B carry
+    one non-zero k column / row, so each pre-activation A[i,0] B[0,j] + bias[j] is exact
+    in fp32 and they span about -19 .. 19 (far negative tail included). fp32 results
+    within 5e-7 (|v| + |GELU|) of the oracle; 16-bit results equal to the oracle's
+    rounded value in nearly every element and never more than one unit in the last
+    place away from it (where that value is well inside the normal range)."""
+    if name not in CONFIGS:
+        pytest.skip(f"{name} not built")
+    M, N, K = 300, 264, 16
+    A = torch.zeros(M, K, dtype=torch.float32)
+    A[:, 0] = 0.25 + (torch.arange(M) % 64).float() / 16
+    B = torch.zeros(K, N, dtype=torch.float32)
+    B[0, :] = torch.linspace(-4.5, 4.5, N)
+    A, B = A.to(torch.bfloat16), B.to(torch.bfloat16)
+    bias = synth.normal(1530, (N,), 0.1, "f32")
+    plan = g.Plan(M, N, K, "bf16", config=name, bias=True, gelu=True, out_dtype=od)
+    say(f"[{name}] GELU range -> {od}")
+    C = gc.run_gpu(plan, A, B, bias)
+    ref, _ = oracle.gemm(gc.to_bits(A), gc.to_bits(B), "bf16", oracle.BIAS | oracle.GELU, 1.0,
+                         bias.numpy(), None, od)
+    pre = A.float()[:, :1].double().numpy() * B.float()[:1, :].double().numpy() + bias.double().numpy()
+    assert pre.min() < -15 and pre.max() > 15
+    got = oracle.decode(od, gc.to_bits(C))
+    assert np.all(np.isfinite(got)), name
+    if od == "f32":
+        err = np.abs(got - ref)
+        assert np.all(err <= 5e-7 * (np.abs(pre) + np.abs(ref)) + 1e-37), (name, float(err.max()))
+        return
+    want = oracle.decode(od, oracle.round16(od, ref))
+    # results near or below the output type's smallest normal come from fp32 intermediates
+    # (Phi ~ |GELU| / |v|, the exponential) in or near fp32's subnormal range, which the
+    # kernels' arithmetic does not keep: there, the result must be that tiny too
+    tiny = 2.0 ** (-120 if od == "bf16" else -14)
+    normal = np.abs(want) >= tiny
+    assert np.all(np.abs(got[~normal]) <= tiny), (name, od)
+    ulps = np.abs(got - want)[normal] / oracle.ulp16(od, np.abs(want[normal]))
+    assert ulps.max() <= 1.0, (name, od, float(ulps.max()))
+    exact = float(np.mean(got[normal] == want[normal]))
+    assert exact >= (0.95 if od == "bf16" else 0.80), (name, od, exact)
