@@ -507,11 +507,16 @@ Selection choose(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, i
       return it->second;
     }
   }
+  // chosen outside the lock; a thread that raced another one on the same shape finds
+  // its entry here and counts a hit, so misses = entries
   const Selection sel = select_config(dev, M, N, K, dtype, epi, batch, aligned16, b_nk);
   std::lock_guard<std::mutex> lk(c.mu);
-  ++c.misses;
-  c.map[key] = sel;
-  return sel;
+  const auto ins = c.map.try_emplace(key, sel);
+  if (ins.second)
+    ++c.misses;
+  else
+    ++c.hits;
+  return ins.first->second;
 }
 
 int check_problem(int64_t M, int64_t N, int64_t K, int32_t dtype, const gemm_epilogue& e,

@@ -299,3 +299,32 @@ def test_package_never_touches_oracle():
             if f.endswith((".py", ".hip", ".hpp", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f
+
+
+def test_selection_and_cache_under_threads():
+    """Plans may be created from several threads at once: the exact-shape cache is
+    process-global and guarded by a lock. Eight threads choose configurations for a
+    mix of fresh and repeated shapes at the same time (ctypes releases the GIL during
+    the call); every answer equals the one-thread answer, and the cache counts one
+    miss and one entry per distinct shape, hits for every other call."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    fields = [f for f, _ in g.Choice._fields_]
+    shapes = [(64 + 37 * i, 96 + 53 * (i % 7), 48 + 29 * (i % 5), ("bf16", "f16", "f32")[i % 3])
+              for i in range(48)]
+    shapes = [(m + 90001, n, k, dt) for m, n, k, dt in shapes]  # not chosen before in this process
+    h0, m0, e0 = g.cache_stats()
+    calls = [s for s in shapes for _ in range(6)]
+
+    def pick(s):
+        ch = g.select(*s, **MI355X)
+        return s, tuple(getattr(ch, f) for f in fields)
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        got = list(ex.map(pick, calls))
+    h1, m1, e1 = g.cache_stats()
+    assert m1 - m0 == len(shapes) and e1 - e0 == len(shapes)
+    assert h1 - h0 == len(calls) - len(shapes)
+    serial = {s: tuple(getattr(g.select(*s, **MI355X), f) for f in fields) for s in shapes}
+    for s, c in got:
+        assert c == serial[s], s
