@@ -52,6 +52,7 @@ KERNEL_SOURCES = {
     "m16n": ["kernel_mfma16_nt.hip", "m16_common.hpp"] + _COMMON,
     "m16t": ["kernel_mfma16_nt.hip", "m16_common.hpp"] + _COMMON,
     "m16s": ["kernel_mfma16_k1.hip", "m16_common.hpp"] + _COMMON,
+    "m16w": ["kernel_mfma16_w.hip", "m16_common.hpp"] + _COMMON,
     "f32d": ["kernel_f32_dlds.hip"] + _COMMON,
     "gemv": ["kernel_gemv.hip"] + _COMMON,
 }
@@ -584,6 +585,10 @@ def symbol_to_config(sym: str):
         t, bm, bn, wm, wn, brow, un = m.groups()
         return (f"m16s_{t}_{bm}x{bn}x64_w{wm}x{wn}" + ("_nk" if brow == "false" else "")
                 + ("_u" if un == "true" else ""))
+    m = re.search(r"gemm_m16w_kernel<g15::(\w+)_t, (\d+), (\d+), (\d+), (true|false)>", sym)
+    if m:
+        t, bm, bn, r, brow = m.groups()
+        return f"m16w_{t}_{bm}x{bn}x32_r{r}" + ("" if brow == "true" else "_nk")
     m = re.search(r"gemm_f32d_kernel<(\d+), (\d+), (\d+), (\d+), (\d+)(?:, (true|false))?>", sym)
     if m:
         bm, bn, wm, wn, sa, bnk = m.groups()

@@ -149,44 +149,67 @@ __device__ __forceinline__ void store_tile_w(const LaunchArgs& a, f32x4 (&acc)[F
     }
   }
   if (a.c_vec) {
+    // Two neighbouring blocks j0 = 2p, j1 = 2p + 1 per step. Lanes 8 apart within
+    // each 16-lane row exchange registers (DPP row rotate by 8) so that one store
+    // covers rows 0-7 of the block row and the next rows 8-15, each row's 32 columns
+    // j0, j1 by 8 lanes: whole 128-byte spans (fp32) instead of 64-byte halves.
+    static_assert(FN % 2 == 0, "block pairs");
+    const bool hi = lr >= 8;
+    const int rlo = m0 + wm * WTM + (lr & 7);  // + 16 i (first store), + 8 (second)
+    auto ror8 = [](float x) {
+      return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x128, 0xF, 0xF, false));
+    };
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int row = row0 + 16 * i;
-      uint32_t off[FN];
+      uint32_t off[FN];  // [2p]: rows 0-7 of the pair, [2p + 1]: rows 8-15
       u32x4 res[FN];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = col0 + 16 * j;  // N % 8 == 0: col < N covers col + 3
-        off[j] = (row < M && col < N) ? static_cast<uint32_t>(row * LDC + col) * ob : OOB;
+      for (int q = 0; q < FN; ++q) {
+        const int row = rlo + 16 * i + 8 * (q & 1);
+        const int col = col0 + 16 * ((q & ~1) + (hi ? 1 : 0));  // N % 8 == 0: covers col + 3
+        off[q] = (row < M && col < N) ? static_cast<uint32_t>(row * LDC + col) * ob : OOB;
         if constexpr (HAS_R) {  // the block row's residual loads all in flight at once
           if constexpr (OUT == DT_F32) {
-            res[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rR, off[j], 0, 0));
+            res[q] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rR, off[q], 0, 0));
           } else {
-            const u32x2 h = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rR, off[j], 0, 0));
-            res[j] = u32x4{h[0], h[1], 0u, 0u};
+            const u32x2 h = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rR, off[q], 0, 0));
+            res[q] = u32x4{h[0], h[1], 0u, 0u};
           }
         }
       }
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        f32x4 v = epi_block<OUT>(e, acc[i][j], bj[j], sc);
-        if constexpr (OUT == DT_F32) {
-          if constexpr (HAS_R)
+      for (int p = 0; p < FN / 2; ++p) {
+        const f32x4 v0 = epi_block<OUT>(e, acc[i][2 * p], bj[2 * p], sc);
+        const f32x4 v1 = epi_block<OUT>(e, acc[i][2 * p + 1], bj[2 * p + 1], sc);
+        f32x4 d[2];
 #pragma unroll
-            for (int t = 0; t < 4; ++t) v[t] += __uint_as_float(res[j][t]);
-          __builtin_amdgcn_raw_buffer_store_b128(
-              u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
-                    __float_as_uint(v[3])},
-              rC, off[j], 0, 0);
-        } else {
-          if constexpr (HAS_R) {
-            v[0] += widen16<OUT>(res[j][0] & 0xffffu);
-            v[1] += widen16<OUT>(res[j][0] >> 16);
-            v[2] += widen16<OUT>(res[j][1] & 0xffffu);
-            v[3] += widen16<OUT>(res[j][1] >> 16);
+        for (int t = 0; t < 4; ++t) {
+          const float x = ror8(v1[t]), y = ror8(v0[t]);
+          d[0][t] = hi ? x : v0[t];
+          d[1][t] = hi ? v1[t] : y;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          f32x4 v = d[h];
+          const int q = 2 * p + h;
+          if constexpr (OUT == DT_F32) {
+            if constexpr (HAS_R)
+#pragma unroll
+              for (int t = 0; t < 4; ++t) v[t] += __uint_as_float(res[q][t]);
+            __builtin_amdgcn_raw_buffer_store_b128(
+                u32x4{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
+                      __float_as_uint(v[3])},
+                rC, off[q], 0, 0);
+          } else {
+            if constexpr (HAS_R) {
+              v[0] += widen16<OUT>(res[q][0] & 0xffffu);
+              v[1] += widen16<OUT>(res[q][0] >> 16);
+              v[2] += widen16<OUT>(res[q][1] & 0xffffu);
+              v[3] += widen16<OUT>(res[q][1] >> 16);
+            }
+            const u32x2 w{pack16<OUT>(v[0], v[1]), pack16<OUT>(v[2], v[3])};
+            __builtin_amdgcn_raw_buffer_store_b64(w, rC, off[q], 0, 0);
           }
-          const u32x2 w{pack16<OUT>(v[0], v[1]), pack16<OUT>(v[2], v[3])};
-          __builtin_amdgcn_raw_buffer_store_b64(w, rC, off[j], 0, 0);
         }
       }
     }

@@ -197,8 +197,8 @@ def test_select_keeps_slice_offsets_32bit():
 
 
 TUNED = [
-    ((4096, 4096, 4096), 1, "bf16", "m16t_bf16_256x256x64_w2x4_a3_b2"),
-    ((4096, 4096, 4096), 1, "f16", "m16t_f16_256x256x64_w2x4_a3_b2"),
+    ((4096, 4096, 4096), 1, "bf16", "m16w_bf16_256x256x32_r4"),
+    ((4096, 4096, 4096), 1, "f16", "m16w_f16_256x256x32_r4"),
     ((8192, 8192, 8192), 1, "bf16", "m16d_bf16_256x256x64_w4x2_a3_b4_r1"),
     ((8192, 3072, 768), 1, "bf16", "m16t_bf16_128x128x64_w2x2_a2_b2"),
     ((8192, 768, 3072), 1, "bf16", "m16t_bf16_128x256x64_w2x4_a3_b3"),
@@ -328,3 +328,17 @@ def test_selection_and_cache_under_threads():
     serial = {s: tuple(getattr(g.select(*s, **MI355X), f) for f in fields) for s in shapes}
     for s, c in got:
         assert c == serial[s], s
+
+
+def test_select_tuned_by_output_type():
+    """The 4096^3 row is keyed on the output type too: fp32 output takes the
+    one-wave-per-SIMD kernel, 16-bit output keeps m16t (measured faster there)."""
+    names = g.config_names()
+    assert names[g.select(4096, 4096, 4096, "bf16", **MI355X).config] == "m16w_bf16_256x256x32_r4"
+    assert names[g.select(4096, 4096, 4096, "bf16", out_dtype="bf16", **MI355X).config] == \
+        "m16t_bf16_256x256x64_w2x4_a3_b2"
+    assert names[g.select(4096, 4096, 4096, "f16", out_dtype="f16", **MI355X).config] == \
+        "m16t_f16_256x256x64_w2x4_a3_b2"
+    # a B given transposed keeps its own row
+    assert names[g.select(4096, 4096, 4096, "bf16", b_layout="nk", **MI355X).config] == \
+        "m16n_bf16_256x256x64_w2x4_a3_b2"

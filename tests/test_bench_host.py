@@ -22,6 +22,10 @@ def test_symbol_to_config():
              "(g15::LaunchArgs)") == "f32d_256x256x16_w4x2_a3"
     assert s("void g15::(anonymous namespace)::gemm_f32d_kernel<128, 128, 2, 2, 3, true>"
              "(g15::LaunchArgs)") == "f32d_128x128x16_w2x2_a3_nk"
+    assert s("void g15::(anonymous namespace)::gemm_m16w_kernel<g15::bf16_t, 256, 256, 4, true>"
+             "(g15::LaunchArgs)") == "m16w_bf16_256x256x32_r4"
+    assert s("void g15::(anonymous namespace)::gemm_m16w_kernel<g15::f16_t, 256, 128, 6, false>"
+             "(g15::LaunchArgs)") == "m16w_f16_256x128x32_r6_nk"
     assert s("void g15::(anonymous namespace)::gemv_kernel<g15::f16_t, 1, 4096, 8>"
              "(g15::LaunchArgs, long)") == "gemv_f16_m1"
     assert s("void g15::(anonymous namespace)::gemm_m16s_kernel<g15::bf16_t, 128, 128, 2, 2, true,"
@@ -36,7 +40,7 @@ def test_committed_traffic_matches_sources():
     the headline kernels (re-collect them after changing those kernels)."""
     with open(bench.TRAFFIC_FILE) as f:
         t = json.load(f)
-    for cfg in ("m16t_bf16_256x256x64_w2x4_a3_b2", "f32d_256x256x16_w4x2_a3"):
+    for cfg in ("m16w_bf16_256x256x32_r4", "f32d_256x256x16_w4x2_a3"):
         assert t["kernels"][cfg]["source_hash"] == bench.kernel_source_hash(cfg), cfg
         v = bench.measured_traffic(cfg)
         assert v is not None and v > 134e6, (cfg, v)  # at least A + B + C once
