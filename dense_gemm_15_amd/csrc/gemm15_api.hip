@@ -117,20 +117,26 @@ gemm_epilogue norm_epi(const gemm_epilogue* e) {
 }
 
 // Relative sustained throughput of one CU running a configuration at full
-// occupancy (1.0 = the fastest configuration of the same input type). Measured
-// on MI355X with square 4096 products (whole rounds of tiles, so wave
-// quantisation does not enter) and rounded; the cost model below adds the
+// occupancy (1.0 = m16d 256 x 256, the reference configuration of the 16-bit
+// types; the fastest fp32 configuration for fp32), and the fixed cost of one tile
+// (prologue, epilogue) in rows of K. Measured on MI355X with square 4096 products
+// (whole rounds of tiles, so wave quantisation does not enter) and rounded; the
+// 256 x 256 m16t and m16w rows were refitted on products with K from 1024 to
+// 16384 (m16t is fastest up to K of about 4096, m16w beyond: its longer prologue
+// and epilogue cost about 250 rows of K per tile). The cost model below adds the
 // rounds of tiles a shape needs.
 struct EffRow {
   const char* name_prefix;
   double eff;
+  double fixed = 64.0;
 };
 const EffRow kEff[] = {
     // bf16 / fp16
+    {"m16w_bf16_256x256x32_r4", 1.08, 250.0}, {"m16w_f16_256x256x32_r4", 1.08, 250.0},
     {"m16d_bf16_256x256x64_w4x2_a3_b4_r1", 1.00}, {"m16d_f16_256x256x64_w4x2_a3_b4_r1", 1.00},
     {"m16d_bf16_256x256x64_w2x4_a3_b4_r1", 0.99}, {"m16d_f16_256x256x64_w2x4_a3_b4_r1", 0.99},
     {"m16d_bf16_256x256x64_w2x4_a3_b4_r2", 0.96}, {"m16d_f16_256x256x64_w2x4_a3_b4_r2", 0.96},
-    {"m16d_bf16_128x256", 0.86}, {"m16d_f16_128x256", 0.86},
+    {"m16d_bf16_128x256", 0.84}, {"m16d_f16_128x256", 0.84},
     {"m16d_bf16_256x128x64_w2x2_a4_b4_r1", 0.82}, {"m16d_f16_256x128x64_w2x2_a4_b4_r1", 0.82},
     {"m16d_bf16_256x128", 0.80}, {"m16d_f16_256x128", 0.80},
     {"m16d_bf16_256x256x64_w2x2", 0.88}, {"m16d_f16_256x256x64_w2x2", 0.88},
@@ -140,6 +146,7 @@ const EffRow kEff[] = {
     {"m16d_bf16_64x128", 0.62}, {"m16d_f16_64x128", 0.62},
     {"m16n_bf16_256x256x64_w2x4", 1.05}, {"m16n_f16_256x256x64_w2x4", 1.05},
     {"m16n_bf16_256x256x64_w4x2", 1.01}, {"m16n_f16_256x256x64_w4x2", 1.01},
+    {"m16t_bf16_256x256x64_w2x4", 1.03}, {"m16t_f16_256x256x64_w2x4", 1.03},
     {"m16t_bf16_256x256", 0.97}, {"m16t_f16_256x256", 0.97},
     {"m16t_bf16_128x128x64_w2x2_a2_b2", 0.78}, {"m16t_f16_128x128x64_w2x2_a2_b2", 0.78},
     {"m16t_bf16_", 0.75}, {"m16t_f16_", 0.75},
@@ -170,16 +177,15 @@ const EffRow kEff[] = {
 struct TunedRow {
   bool f32;
   int64_t M, N, K, batch;
-  const char* config;  // an "m16n" configuration answers problems with a transposed B
-  int out = -1;        // output type the row is for (-1: any)
+  const char* config;  // an "m16n" or "_nk" configuration answers a transposed B
 };
 const TunedRow kTuned[] = {
-    // 4096^3 with fp32 output: the one-wave-per-SIMD kernel, 1.7% faster than m16t in
-    // alternating graph-replay runs on three boxes (bf16 109.5 against 111.4 us, fp16
-    // 114.2 against 116.2); with 16-bit output and at K = 8192 m16t is faster
-    {false, 4096, 4096, 4096, 1, "m16w_{t}_256x256x32_r4", GEMM_F32},
-    {false, 4096, 4096, 4096, 1, "m16t_{t}_256x256x64_w2x4_a3_b2"},
-    {false, 8192, 8192, 8192, 1, "m16d_{t}_256x256x64_w4x2_a3_b4_r1"},
+    // 4096^3 and 8192^3: the one-wave-per-SIMD kernel, in alternating graph-replay
+    // runs faster than m16t at 4096^3 (bf16 103.6 against 105.3 us with bf16 output,
+    // fp16 109.4 against 111.8 with fp16 output, 111.5 against 117.1 with fp32
+    // output) and than m16d at 8192^3 (bf16 763 against 828 us, fp16 814 against 889)
+    {false, 4096, 4096, 4096, 1, "m16w_{t}_256x256x32_r4"},
+    {false, 8192, 8192, 8192, 1, "m16w_{t}_256x256x32_r4"},
     {false, 2048, 2048, 2048, 1, "m16d_{t}_128x128x64_w2x2_a3_b4_r1"},
     {false, 1024, 1024, 1024, 1, "m16d_{t}_64x128x64_w2x2_a4_b4_r2"},
     {false, 512, 512, 512, 1, "m16d_{t}_64x128x64_w2x2_a4_b4_r2"},
@@ -187,6 +193,8 @@ const TunedRow kTuned[] = {
     {false, 8192, 768, 3072, 1, "m16t_{t}_128x256x64_w2x4_a3_b3"},  // encoder FFN, second GEMM
     {false, 512, 512, 64, 96, "m16s_{t}_256x128x64_w4x2"},             // 96 heads of Q K^T
     {false, 4096, 4096, 4096, 1, "m16n_{t}_256x256x64_w2x4_a3_b2"},
+    // transposed B at 8192^3: 825 against 838 us for m16n (bf16)
+    {false, 8192, 8192, 8192, 1, "m16w_{t}_256x256x32_r5_nk"},
     {false, 2048, 2048, 2048, 1, "m16n_{t}_128x128x64_w2x2_a3_b3"},
     {false, 8192, 3072, 768, 1, "m16n_{t}_128x128x64_w2x2_a2_b2"},
     {false, 8192, 768, 3072, 1, "m16n_{t}_128x256x64_w2x4_a3_b3"},
@@ -200,11 +208,22 @@ const TunedRow kTuned[] = {
     {true, 512, 512, 512, 1, "f32_64x64_w2x2"},
 };
 
-double cfg_efficiency(const KernelEntry& k) {
+const EffRow* eff_row(const KernelEntry& k) {
   for (const EffRow& r : kEff)
-    if (std::strncmp(k.name, r.name_prefix, std::strlen(r.name_prefix)) == 0) return r.eff;
+    if (std::strncmp(k.name, r.name_prefix, std::strlen(r.name_prefix)) == 0) return &r;
+  return nullptr;
+}
+
+double cfg_efficiency(const KernelEntry& k) {
+  if (const EffRow* r = eff_row(k)) return r->eff;
   if (k.kind == KIND_SIMPLE) return 0.03;
   return 0.3;  // other tiles: measured well below the configurations above
+}
+
+// Fixed cost of one tile, in rows of K.
+double cfg_fixed(const KernelEntry& k) {
+  const EffRow* r = eff_row(k);
+  return r ? r->fixed : 64.0;
 }
 
 // Workgroups one CU can hold for a configuration (LDS-limited; registers allow
@@ -291,18 +310,17 @@ double cfg_cost(const KernelEntry& k, int64_t M, int64_t N, int64_t K, int64_t b
     const int c = static_cast<int>(left < occ ? left : occ);
     t += c * tile_work / (cfg_efficiency(k) * concurrency_gain(c, occ));
   }
-  t += static_cast<double>(per_cu) * k.bm * k.bn * 64.0;
+  t += static_cast<double>(per_cu) * k.bm * k.bn * cfg_fixed(k);
   return t;
 }
 
 int tuned_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64_t K, int dtype,
-                 int64_t batch, bool b_nk, int out_dtype) {
+                 int64_t batch, bool b_nk) {
   if (dev.cu_count != 256 || dev.lds_bytes < 163840) return -1;
   const auto& all = registry().all;
   for (const TunedRow& r : kTuned) {
     if (r.f32 != (dtype == GEMM_F32) || r.M != M || r.N != N || r.K != K || r.batch != batch)
       continue;
-    if (r.out >= 0 && r.out != out_dtype) continue;
     std::string name(r.config);
     const size_t at = name.find("{t}");
     if (at != std::string::npos) name.replace(at, 3, dtype == GEMM_BF16 ? "bf16" : "f16");
@@ -387,23 +405,25 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
     if (s.config < 0 || k.bm < all[s.config].bm) s.config = i;
   }
   if (s.config >= 0) return s;
-  const int tuned = tuned_config(dev, M, N, K, dtype, batch, b_nk, epi.out_dtype);
+  const int tuned = tuned_config(dev, M, N, K, dtype, batch, b_nk);
   if (tuned >= 0 && cfg_fits(all[tuned], dtype, vec_a, vec_b, dev, M, N, K, epi.out_dtype, b_nk)) {
     s.config = tuned;
     return s;
   }
-  // Few tiles and a long K: the m16d configuration with the smallest tile that
-  // runs the product split along K (the cost model does not model the split).
+  // Few tiles and a long K: when even the smallest m16d tile leaves most CUs idle,
+  // that configuration runs the product split along K (the cost model does not
+  // model the split). A larger tile is never split instead: where the smallest
+  // tile already fills the chip, a split of a larger one measured far slower
+  // (bf16 4096 x 2048 x 4096: 256 x 256 split 4 ways 143 us, 128 x 128 tiles 66 us).
   if (!b_nk && dtype != GEMM_F32 && vec_a && vec_b) {
     int pick = -1;
     for (int i = 0; i < static_cast<int>(all.size()); ++i) {
       const KernelEntry& k = all[i];
       if (!is_m16d(k) || !cfg_fits(k, dtype, vec_a, vec_b, dev, M, N, K, epi.out_dtype, b_nk))
         continue;
-      if (tile_split(k, M, N, K, batch, dev) < 2) continue;
       if (pick < 0 || k.bm * k.bn < all[pick].bm * all[pick].bn) pick = i;
     }
-    if (pick >= 0) {
+    if (pick >= 0 && tile_split(all[pick], M, N, K, batch, dev) >= 2) {
       s.config = pick;
       return s;
     }

@@ -154,13 +154,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
     }
   };
 
+  // no clearing: the first k-step of slice 0 takes a zero accumulator operand (an
+  // inline constant), which saves one register write per accumulator element
   f32x16 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
   const int nk = (K + BK - 1) / BK;
   const int lrow = lane & 31, lhalf = lane >> 5;
@@ -216,15 +212,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
     return L8 + (SA * A_STAGE + sl * B_STAGE) * 16;
   };
 
-  // matrix-core ops of one k-step on rows [I0, I1) of the wave's blocks
-  auto mmas = [&](const u32x4 (&fa)[FM], const u32x4 (&fb)[FN], int i0, int i1) {
+  // matrix-core ops of one k-step on rows [I0, I1) of the wave's blocks; ZERO: the
+  // first k-step (accumulators start from zero)
+  auto mmas = [&](auto ZeroC, const u32x4 (&fa)[FM], const u32x4 (&fb)[FN], int i0, int i1) {
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       if (i < i0 || i >= i1) continue;
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mma<T>(fa[i], fb[j], acc[i][j]);
+      for (int j = 0; j < FN; ++j) {
+        if constexpr (decltype(ZeroC)::value)
+          acc[i][j] = mma<T>(fa[i], fb[j], f32x16{});
+        else
+          acc[i][j] = mma<T>(fa[i], fb[j], acc[i][j]);
+      }
     }
   };
+  const std::false_type acc_in{};
 
   // Prologue: B slices 0 .. SB-2 and A slices 0 .. SA-2 (B of a slice before its A).
   for (int s = 0; s < SA - 1; ++s) {
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
   // loads left in flight at a slice boundary: everything issued after B(kt+1)
   constexpr int WAITN = SA == SB ? NV * (SA - 2) : NV * (SB - 2) + AI;
   int ca = 0, cb = 0;  // ring slots of A(kt), B(kt)
-  auto slice = [&](auto TailC, int kt) {
+  auto slice = [&](auto TailC, auto FirstC, int kt) {
     constexpr bool TAIL = decltype(TailC)::value;
     const int na = ca + 1 == SA ? 0 : ca + 1, nb = cb + 1 == SB ? 0 : cb + 1;
     const int fa = ca == 0 ? SA - 1 : ca - 1;  // slot of A(kt-1), refilled with A(kt+SA-1)
@@ -303,11 +306,14 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
       }
     };
     // k-step s (0..2) on fragments (xa, xb), reading step s+1 into (ya, yb)
-    auto step = [&](int s, const u32x4 (&xa)[FM], const u32x4 (&xb)[FN], u32x4 (&ya)[FM],
-                    u32x4 (&yb)[FN]) {
+    auto step = [&](auto ZeroC, int s, const u32x4 (&xa)[FM], const u32x4 (&xb)[FN],
+                    u32x4 (&ya)[FM], u32x4 (&yb)[FN]) {
 #pragma unroll
       for (int q = 0; q < NM; ++q) {
-        acc[q / FN][q % FN] = mma<T>(xa[q / FN], xb[q % FN], acc[q / FN][q % FN]);
+        if constexpr (decltype(ZeroC)::value)
+          acc[q / FN][q % FN] = mma<T>(xa[q / FN], xb[q % FN], f32x16{});
+        else
+          acc[q / FN][q % FN] = mma<T>(xa[q / FN], xb[q % FN], acc[q / FN][q % FN]);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int r = 0; r < NR; ++r)
@@ -322,7 +328,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
       // m16t keeps the grouped order (measured faster for it): each k-step's
       // fragment reads, then its ops, with the direct loads in k-step 1
       frags(LA, LB, 1, f1a, f1b);
-      mmas(f0a, f0b, 0, FM);
+      mmas(FirstC, f0a, f0b, 0, FM);
       plan_slice<0, FM * FN, FM + FN, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
       // the B fragments of k-step 3 are read here too, before the slice's direct
@@ -335,7 +341,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
       for (int j = 0; j < FN; ++j) read_frag(LA, LB, 3, 1 + j, f1a, f3b);
 #pragma unroll
       for (int v = 0; v < NV; ++v) dma(v);
-      mmas(f1a, f1b, 0, FM);
+      mmas(acc_in, f1a, f1b, 0, FM);
       plan_slice<0, FM * FN, FM + 2 * FN, 0, NV>();
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -343,22 +349,22 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
         if (r == 0 || r > FN) read_frag(LA, LB, 3, r, f1a, f1b);
 #pragma unroll
       for (int j = 0; j < FN; ++j) f1b[j] = f3b[j];
-      mmas(f0a, f0b, 0, FM);
+      mmas(acc_in, f0a, f0b, 0, FM);
       plan_slice<0, FM * FN, FM, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
-      mmas(f1a, f1b, 0, HALF);
+      mmas(acc_in, f1a, f1b, 0, HALF);
       __builtin_amdgcn_sched_barrier(0);
       wait_vm<WAITN>();
       lds_barrier();
       frags(NA, NB, 0, f0a, f0b);
-      mmas(f1a, f1b, HALF, FM);
+      mmas(acc_in, f1a, f1b, HALF, FM);
       plan_slice<0, (FM - HALF) * FN, FM + FN, 0, 0>();
       __builtin_amdgcn_sched_barrier(0);
       return;
     }
-    step(0, f0a, f0b, f1a, f1b);
-    step(1, f1a, f1b, f0a, f0b);
-    step(2, f0a, f0b, f1a, f1b);
+    step(FirstC, 0, f0a, f0b, f1a, f1b);
+    step(acc_in, 1, f1a, f1b, f0a, f0b);
+    step(acc_in, 2, f0a, f0b, f1a, f1b);
 #pragma unroll
     for (int q = 0; q < Q3; ++q) {
       acc[q / FN][q % FN] = mma<T>(f1a[q / FN], f1b[q % FN], acc[q / FN][q % FN]);
@@ -378,11 +384,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
     ca = na;
     cb = nb;
   };
-  // Slices whose issues (A(kt + SA - 1), B(kt + SB - 1)) lie wholly inside K run
-  // the branch-free issue; the last few take the masked one.
-  int kt = 0;
-  for (; kt < nk && (kt + SA) * BK <= K; ++kt) slice(std::false_type{}, kt);
-  for (; kt < nk; ++kt) slice(std::true_type{}, kt);
+  // Slice 0 (K >= 1, so there is one) starts the accumulators. Slices whose issues
+  // (A(kt + SA - 1), B(kt + SB - 1)) lie wholly inside K run the branch-free issue;
+  // the last few take the masked one.
+  if (SA * BK <= K)
+    slice(std::false_type{}, std::true_type{}, 0);
+  else
+    slice(std::true_type{}, std::true_type{}, 0);
+  int kt = 1;
+  for (; kt < nk && (kt + SA) * BK <= K; ++kt) slice(std::false_type{}, acc_in, kt);
+  for (; kt < nk; ++kt) slice(std::true_type{}, acc_in, kt);
 
   wait_vm<0>();
   lds_barrier();  // every wave is done with the rings; LDS is free

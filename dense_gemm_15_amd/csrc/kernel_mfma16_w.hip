@@ -406,11 +406,9 @@ void gemm_m16w_kernel(LaunchArgs a) {
   };
   constexpr int NR = FM + FN;
 
+  // no clearing: the first slice's ops take a zero accumulator operand (an inline
+  // constant), which saves one register write per accumulator element per call
   f32x4 acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // slot s holds A then B of one slice
   constexpr int SLOT = A_SLOT + B_SLOT;
@@ -446,14 +444,17 @@ void gemm_m16w_kernel(LaunchArgs a) {
   constexpr int Q0 = 4;
   constexpr int QR = NM * 9 / 16;  // ops that carry the NR reads
   static_assert(Q0 + QR + NV <= NM, "slice schedule");
-  auto slice = [&](auto FullC, const Frag& cur, Frag& nxt, lds_char* __restrict__ ra,
+  auto slice = [&](auto FullC, auto FirstC, const Frag& cur, Frag& nxt, lds_char* __restrict__ ra,
                    lds_char* __restrict__ rb, lds_char* __restrict__ wa, lds_char* __restrict__ wb,
                    int kt) __attribute__((always_inline)) {
     const int k0 = (kt + R) * WBK;
     static_for<0, NM>([&](auto QC) __attribute__((always_inline)) {
       constexpr int q = decltype(QC)::value;
       // B fragment first: the block accumulates C^T (rows along the lanes)
-      acc[q / FN][q % FN] = mma16<T>(cur.b[q % FN], cur.a[q / FN], acc[q / FN][q % FN]);
+      if constexpr (decltype(FirstC)::value)
+        acc[q / FN][q % FN] = mma16<T>(cur.b[q % FN], cur.a[q / FN], f32x4{0.f, 0.f, 0.f, 0.f});
+      else
+        acc[q / FN][q % FN] = mma16<T>(cur.b[q % FN], cur.a[q / FN], acc[q / FN][q % FN]);
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (q == Q0 - 1) {
         wait_vm<(R - 2) * NV>();
@@ -477,25 +478,31 @@ void gemm_m16w_kernel(LaunchArgs a) {
 
   int ws = 0;  // slot of slice kt (loaded with slice kt + R during it)
   int kt = 0;
-  auto step = [&](auto FullC, const Frag& cur, Frag& nxt) __attribute__((always_inline)) {
+  auto step = [&](auto FullC, auto FirstC, const Frag& cur, Frag& nxt)
+                  __attribute__((always_inline)) {
     const int rs = ws + 1 == R ? 0 : ws + 1;
-    slice(FullC, cur, nxt, slotA(rs), slotB(rs), slotA(ws), slotB(ws), kt);
+    slice(FullC, FirstC, cur, nxt, slotA(rs), slotB(rs), slotA(ws), slotB(ws), kt);
     ws = rs;
     ++kt;
   };
-  // slices whose load (slice kt + R) lies inside K, two at a time, then the rest
+  // slice 0 (K >= 1, so there is one), then the slices whose load (slice kt + R) lies
+  // inside K, two at a time, then the rest
   const int nfull = K / WBK - R;
+  if (nfull >= 1)
+    step(std::true_type{}, std::true_type{}, fx, fy);
+  else
+    step(std::false_type{}, std::true_type{}, fx, fy);
   while (kt + 2 <= nfull) {
-    step(std::true_type{}, fx, fy);
-    step(std::true_type{}, fy, fx);
+    step(std::true_type{}, std::false_type{}, fy, fx);
+    step(std::true_type{}, std::false_type{}, fx, fy);
   }
   while (kt < nk) {
-    step(std::false_type{}, fx, fy);
+    step(std::false_type{}, std::false_type{}, fy, fx);
     if (kt >= nk) {
-      fx = fy;
+      fy = fx;
       break;
     }
-    step(std::false_type{}, fy, fx);
+    step(std::false_type{}, std::false_type{}, fx, fy);
   }
 
   wait_vm<0>();  // no direct load still writing LDS when the wave ends

@@ -199,7 +199,8 @@ def test_select_keeps_slice_offsets_32bit():
 TUNED = [
     ((4096, 4096, 4096), 1, "bf16", "m16w_bf16_256x256x32_r4"),
     ((4096, 4096, 4096), 1, "f16", "m16w_f16_256x256x32_r4"),
-    ((8192, 8192, 8192), 1, "bf16", "m16d_bf16_256x256x64_w4x2_a3_b4_r1"),
+    ((8192, 8192, 8192), 1, "bf16", "m16w_bf16_256x256x32_r4"),
+    ((8192, 8192, 8192), 1, "f16", "m16w_f16_256x256x32_r4"),
     ((8192, 3072, 768), 1, "bf16", "m16t_bf16_128x128x64_w2x2_a2_b2"),
     ((8192, 768, 3072), 1, "bf16", "m16t_bf16_128x256x64_w2x4_a3_b3"),
     ((512, 512, 64), 96, "bf16", "m16s_bf16_256x128x64_w4x2"),
@@ -330,15 +331,34 @@ def test_selection_and_cache_under_threads():
         assert c == serial[s], s
 
 
-def test_select_tuned_by_output_type():
-    """The 4096^3 row is keyed on the output type too: fp32 output takes the
-    one-wave-per-SIMD kernel, 16-bit output keeps m16t (measured faster there)."""
+def test_select_tuned_every_output_type():
+    """The 4096^3 and 8192^3 rows hold for every output type (the one-wave-per-SIMD
+    kernel was measured fastest with fp32 and 16-bit output alike); a B given
+    transposed keeps rows of its own."""
     names = g.config_names()
-    assert names[g.select(4096, 4096, 4096, "bf16", **MI355X).config] == "m16w_bf16_256x256x32_r4"
-    assert names[g.select(4096, 4096, 4096, "bf16", out_dtype="bf16", **MI355X).config] == \
-        "m16t_bf16_256x256x64_w2x4_a3_b2"
-    assert names[g.select(4096, 4096, 4096, "f16", out_dtype="f16", **MI355X).config] == \
-        "m16t_f16_256x256x64_w2x4_a3_b2"
-    # a B given transposed keeps its own row
-    assert names[g.select(4096, 4096, 4096, "bf16", b_layout="nk", **MI355X).config] == \
+    for M in (4096, 8192):
+        for dt, outs in (("bf16", ("f32", "bf16")), ("f16", ("f32", "f16"))):
+            for od in outs:
+                assert names[g.select(M, M, M, dt, out_dtype=od, **MI355X).config] == \
+                    f"m16w_{dt}_256x256x32_r4", (M, dt, od)
+    nk = dict(b_layout="nk", **MI355X)
+    assert names[g.select(4096, 4096, 4096, "bf16", **nk).config] == \
         "m16n_bf16_256x256x64_w2x4_a3_b2"
+    assert names[g.select(8192, 8192, 8192, "f16", **nk).config] == "m16w_f16_256x256x32_r5_nk"
+
+
+@pytest.mark.parametrize("shape,prefix", [
+    ((3072, 3072, 3072), "m16t_{t}_256x256x64_w2x4"),
+    ((4096, 4096, 2048), "m16t_{t}_256x256x64_w2x4"),
+    ((8192, 8192, 2048), "m16t_{t}_256x256x64_w2x4"),
+    ((6144, 6144, 6144), "m16w_{t}_256x256x32_r4"),
+    ((4096, 4096, 16384), "m16w_{t}_256x256x32_r4"),
+    ((2048, 8192, 8192), "m16w_{t}_256x256x32_r4"),
+])
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+def test_cost_model_large_shapes(shape, prefix, dtype):
+    """Large shapes outside the shape table: the cost model takes m16t's 256 x 256 tile
+    up to K of about 4096 and the one-wave-per-SIMD kernel beyond, as measured on
+    MI355X (its longer prologue and epilogue only pay off over a long K)."""
+    ch = g.select(*shape, dtype, **MI355X)
+    assert g.config_names()[ch.config].startswith(prefix.format(t=dtype)), shape
