@@ -278,6 +278,28 @@ def test_workload_square_4096(g, name):
     say(f"[{name}] max err/tol {r['max_ratio']:.3f} max abs {r['max_abs']:.3e}")
     assert r["ok"], r
 
+@pytest.mark.parametrize("shape,dtype,config", [
+    ((3000, 3000, 9000), "bf16", "m16w_bf16_256x256x32_r4"),
+    ((3072, 3072, 5000), "f16", "m16w_f16_256x256x32_r4"),
+    ((4000, 3000, 2056), "f16", "m16t_f16_256x256x64_w2x4_a3_b2"),
+])
+def test_cost_model_choices(g, shape, dtype, config):
+    """Large products outside the shape table, on the configuration the cost model
+    picks (the one-wave-per-SIMD kernel for a long K, m16t's 256 x 256 tile below K of
+    about 4096), with ragged M, N or K: sampled outputs (random, corners, tile edges)
+    against the oracle, for uniform inputs and, bit-exact, small integers."""
+    M, N, K = shape
+    plan = g.Plan(M, N, K, dtype)
+    say(f"[{shape} {dtype}]", plan.describe())
+    assert plan.config_name == config
+    rows, cols = gc.sample_indices(M, N, 2000, 11)
+    for kind in ("uniform", "int"):
+        A, B = gc.inputs(M, N, K, dtype, 4100 + K, kind)
+        C = gc.run_gpu(plan, A, B)
+        r = gc.check_sampled(C, A, B, dtype, rows, cols, exact=(kind == "int"))
+        assert r["ok"], (shape, dtype, kind, r)
+
+
 @pytest.mark.parametrize("name", ["longk_256x256x4096", "longk_64x4096x4096"])
 def test_workload_long_k(g, name):
     """The long-K benchmark workloads at their launch configuration (split along K):
