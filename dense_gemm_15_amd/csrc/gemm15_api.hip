@@ -157,9 +157,12 @@ const EffRow kEff[] = {
     {"m16n_bf16_64x128", 0.66}, {"m16n_f16_64x128", 0.66},
     {"mfma16_bf16_128x128_w2x2_scalar", 0.10}, {"mfma16_f16_128x128_w2x2_scalar", 0.10},
     {"mfma16_bf16_64x64_w2x2_scalar", 0.08}, {"mfma16_f16_64x64_w2x2_scalar", 0.08},
-    {"mfma16_bf16_128x128", 0.52}, {"mfma16_f16_128x128", 0.52},
-    {"mfma16_bf16_128x64", 0.45}, {"mfma16_f16_128x64", 0.45},
-    {"mfma16_bf16_64x64", 0.33}, {"mfma16_f16_64x64", 0.33},
+    // the register-staged kernels, measured against m16d 64 x 128 on products of 8 to
+    // 32 tiles (512^3, 1024^3, M or N of 256 with K up to 1024): 1.3-2x its time
+    // even with twice its tiles, so they rank below every direct-to-LDS tile
+    {"mfma16_bf16_128x128", 0.20}, {"mfma16_f16_128x128", 0.20},
+    {"mfma16_bf16_128x64", 0.15}, {"mfma16_f16_128x64", 0.15},
+    {"mfma16_bf16_64x64", 0.16}, {"mfma16_f16_64x64", 0.16},
     // fp32 (relative to the fastest fp32 configuration)
     {"f32d_256x256x16_w4x2_a3", 1.00}, {"f32d_128x256x16_w2x4_a4", 0.95},
     {"f32d_128x128x16_w2x2_a3", 0.95}, {"f32d_128x128x16_w2x2_a4", 0.93},

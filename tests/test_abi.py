@@ -362,3 +362,13 @@ def test_cost_model_large_shapes(shape, prefix, dtype):
     MI355X (its longer prologue and epilogue only pay off over a long K)."""
     ch = g.select(*shape, dtype, **MI355X)
     assert g.config_names()[ch.config].startswith(prefix.format(t=dtype)), shape
+
+
+@pytest.mark.parametrize("shape", [(256, 512, 1024), (127, 1000, 768), (4096, 256, 1024),
+                                   (256, 256, 64), (512, 2048, 768)])
+def test_small_products_take_direct_lds_tiles(shape):
+    """Products of a few dozen tiles go to the direct-to-LDS 64 x 128 tile, not to the
+    register-staged kernels (measured on MI355X: those take 1.3-2x its time even with
+    twice as many tiles)."""
+    ch = g.select(*shape, "bf16", **MI355X)
+    assert g.config_names()[ch.config].startswith("m16d_bf16_64x128"), shape
