@@ -149,6 +149,7 @@ const EffRow kEff[] = {
     {"m16t_bf16_256x256x64_w2x4", 1.03}, {"m16t_f16_256x256x64_w2x4", 1.03},
     {"m16t_bf16_256x256", 0.97}, {"m16t_f16_256x256", 0.97},
     {"m16t_bf16_128x128x64_w2x2_a2_b2", 0.78}, {"m16t_f16_128x128x64_w2x2_a2_b2", 0.78},
+    {"m16t_bf16_128x256", 0.91}, {"m16t_f16_128x256", 0.91},
     {"m16t_bf16_", 0.75}, {"m16t_f16_", 0.75},
     {"m16n_bf16_128x256", 0.92}, {"m16n_f16_128x256", 0.92},
     {"m16n_bf16_256x128", 0.86}, {"m16n_f16_256x128", 0.86},
