@@ -298,6 +298,8 @@ int64_t cfg_workgroups(const KernelEntry& k, int64_t M, int64_t N, int split, in
 // workgroup alone reaches 0.63 of a pair's throughput).
 double concurrency_gain(int c, int occ) { return c >= occ ? 1.0 : 0.63; }
 
+constexpr double kRoundUs = 3.0;  // fixed latency per round of workgroups, microseconds
+
 // Modelled time (arbitrary units) of a configuration on a problem: the busiest
 // CU's tiles, run occ at a time at the configuration's relative efficiency,
 // plus a fixed per-tile cost (prologue, epilogue) that keeps tiny-K shapes honest.
@@ -310,11 +312,19 @@ double cfg_cost(const KernelEntry& k, int64_t M, int64_t N, int64_t K, int64_t b
   const int64_t kpad = ((K + k.bk - 1) / k.bk) * k.bk;
   const double tile_work = static_cast<double>(k.bm) * k.bn * kpad;
   double t = 0.0;
+  int64_t rounds = 0;
   for (int64_t left = per_cu; left > 0; left -= occ) {
     const int c = static_cast<int>(left < occ ? left : occ);
     t += c * tile_work / (cfg_efficiency(k) * concurrency_gain(c, occ));
+    ++rounds;
   }
   t += static_cast<double>(per_cu) * k.bm * k.bn * cfg_fixed(k);
+  // each round of workgroups also pays a fixed latency (launch, first loads, last
+  // stores) whatever its tile: ROUND_US in the units above, where one microsecond is
+  // about 2.6e6 (16-bit inputs: a 256 x 256 x 4096 tile at efficiency 1.03 takes
+  // ~100 us) or 1.6e5 (fp32: 1/16 of the matrix rate)
+  const double unit_per_us = k.in_dtype == DT_F32 ? 1.6e5 : 2.6e6;
+  t += static_cast<double>(rounds) * kRoundUs * unit_per_us;
   return t;
 }
 

@@ -374,3 +374,19 @@ def test_small_products_take_direct_lds_tiles(shape):
     twice as many tiles)."""
     ch = g.select(*shape, "bf16", **MI355X)
     assert g.config_names()[ch.config].startswith("m16d_bf16_64x128"), shape
+
+
+@pytest.mark.parametrize("shape,layout,prefix", [
+    ((3072, 3072, 128), "kn", "m16t_bf16_256x256"),
+    ((4096, 3072, 128), "kn", "m16t_bf16_256x256"),
+    ((1536, 4096, 128), "nk", "m16n_bf16_128x256"),
+    ((3072, 3072, 64), "nk", "m16n_bf16_256x256"),
+])
+def test_cost_model_counts_rounds(shape, layout, prefix):
+    """A short K leaves each round of workgroups mostly fixed latency (launch, first
+    loads, last stores): the cost model charges it per round, so the fewer, larger
+    tiles win there (measured on MI355X: 3072^2 x 128 13.3 us on 256 x 256 tiles
+    against 18.9 us on 128 x 128, B transposed 1536 x 4096 x 128 9.8 against 15.4 us
+    on 64 x 128)."""
+    ch = g.select(*shape, "bf16", b_layout=layout, **MI355X)
+    assert g.config_names()[ch.config].startswith(prefix), (shape, layout)
