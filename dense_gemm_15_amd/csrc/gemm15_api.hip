@@ -129,6 +129,7 @@ struct EffRow {
   const char* name_prefix;
   double eff;
   double fixed = 64.0;
+  double lone = 0.63;  // throughput of a lone workgroup of an occupancy-2 configuration
 };
 const EffRow kEff[] = {
     // bf16 / fp16
@@ -150,6 +151,8 @@ const EffRow kEff[] = {
     {"m16t_bf16_256x256", 0.97}, {"m16t_f16_256x256", 0.97},
     {"m16t_bf16_128x128x64_w2x2_a2_b2", 0.78}, {"m16t_f16_128x128x64_w2x2_a2_b2", 0.78},
     {"m16t_bf16_128x256", 0.91}, {"m16t_f16_128x256", 0.91},
+    // the small direct-to-LDS tile: fitted on 66 measured shapes (best of 13 tiles on 28)
+    {"m16t_bf16_64x128", 0.68, 16.0}, {"m16t_f16_64x128", 0.68, 16.0},
     {"m16t_bf16_", 0.75}, {"m16t_f16_", 0.75},
     {"m16n_bf16_128x256", 0.92}, {"m16n_f16_128x256", 0.92},
     {"m16n_bf16_256x128", 0.86}, {"m16n_f16_256x128", 0.86},
@@ -190,9 +193,12 @@ const TunedRow kTuned[] = {
     // output) and than m16d at 8192^3 (bf16 763 against 828 us, fp16 814 against 889)
     {false, 4096, 4096, 4096, 1, "m16w_{t}_256x256x32_r4"},
     {false, 8192, 8192, 8192, 1, "m16w_{t}_256x256x32_r4"},
-    {false, 2048, 2048, 2048, 1, "m16d_{t}_128x128x64_w2x2_a3_b4_r1"},
-    {false, 1024, 1024, 1024, 1, "m16d_{t}_64x128x64_w2x2_a4_b4_r2"},
-    {false, 512, 512, 512, 1, "m16d_{t}_64x128x64_w2x2_a4_b4_r2"},
+    // 2048^3, 1024^3, 512^3: the 64 x 128 direct-to-LDS tile (fp16, fp32 output: 26.9
+    // against 27.9 us for m16d 128 x 128, 10.0 against 11.2 and 6.9 against 7.8 us for
+    // m16d 64 x 128)
+    {false, 2048, 2048, 2048, 1, "m16t_{t}_64x128x64_w2x2_a3_b3"},
+    {false, 1024, 1024, 1024, 1, "m16t_{t}_64x128x64_w2x2_a3_b3"},
+    {false, 512, 512, 512, 1, "m16t_{t}_64x128x64_w2x2_a3_b3"},
     {false, 8192, 3072, 768, 1, "m16t_{t}_128x128x64_w2x2_a2_b2"},     // encoder FFN, first GEMM
     {false, 8192, 768, 3072, 1, "m16t_{t}_128x256x64_w2x4_a3_b3"},  // encoder FFN, second GEMM
     {false, 512, 512, 64, 96, "m16s_{t}_256x128x64_w4x2"},             // 96 heads of Q K^T
@@ -228,6 +234,11 @@ double cfg_efficiency(const KernelEntry& k) {
 double cfg_fixed(const KernelEntry& k) {
   const EffRow* r = eff_row(k);
   return r ? r->fixed : 64.0;
+}
+
+double cfg_lone(const KernelEntry& k) {
+  const EffRow* r = eff_row(k);
+  return r ? r->lone : 0.63;
 }
 
 // Workgroups one CU can hold for a configuration (LDS-limited; registers allow
@@ -296,7 +307,9 @@ int64_t cfg_workgroups(const KernelEntry& k, int64_t M, int64_t N, int split, in
 // Throughput of one CU running c < occ workgroups of an occupancy-occ
 // configuration, relative to running occ of them (measured: one 128 x 128
 // workgroup alone reaches 0.63 of a pair's throughput).
-double concurrency_gain(int c, int occ) { return c >= occ ? 1.0 : 0.63; }
+double concurrency_gain(const KernelEntry& k, int c, int occ) {
+  return c >= occ ? 1.0 : cfg_lone(k);
+}
 
 constexpr double kRoundUs = 3.0;  // fixed latency per round of workgroups, microseconds
 
@@ -315,7 +328,7 @@ double cfg_cost(const KernelEntry& k, int64_t M, int64_t N, int64_t K, int64_t b
   int64_t rounds = 0;
   for (int64_t left = per_cu; left > 0; left -= occ) {
     const int c = static_cast<int>(left < occ ? left : occ);
-    t += c * tile_work / (cfg_efficiency(k) * concurrency_gain(c, occ));
+    t += c * tile_work / (cfg_efficiency(k) * concurrency_gain(k, c, occ));
     ++rounds;
   }
   t += static_cast<double>(per_cu) * k.bm * k.bn * cfg_fixed(k);
@@ -363,6 +376,7 @@ int64_t round_up16B(int64_t x, int64_t es) {
 bool is_f32d(const KernelEntry& k) { return std::strncmp(k.name, "f32d_", 5) == 0; }
 
 bool is_m16d(const KernelEntry& k) { return std::strncmp(k.name, "m16d_", 5) == 0; }
+bool is_m16t(const KernelEntry& k) { return std::strncmp(k.name, "m16t_", 5) == 0; }
 
 // Split-K factor of a tile configuration on a problem with few tiles and a long K
 // (at most half the CUs busy, at least 32 K slices each): S slices of K, each a
@@ -492,7 +506,8 @@ Selection select_config(const gemm_device_desc& dev, int64_t M, int64_t N, int64
     const int pk = best_for(true, true, pa ? round_up16B(K, es) : K,
                             (pb && !b_nk) ? round_up16B(N, es) : N,
                             [&](const KernelEntry& k) {
-                              return dtype == GEMM_F32 ? is_f32d(k) : (b_nk || is_m16d(k));
+                              return dtype == GEMM_F32 ? is_f32d(k)
+                                                       : (b_nk || is_m16d(k) || is_m16t(k));
                             },
                             &pcost);
     if (pk >= 0 && (s.config < 0 || pcost < cost)) {

@@ -436,7 +436,8 @@ hipError_t launch_m16n(const LaunchArgs& a, hipStream_t s) {
   G15_M16T(T, TN, 256, 128, 2, 2, 3, 3),        \
   G15_M16T(T, TN, 128, 256, 2, 4, 3, 3),        \
   G15_M16T(T, TN, 128, 128, 2, 2, 3, 3),        \
-  G15_M16T(T, TN, 128, 128, 2, 2, 2, 2)
+  G15_M16T(T, TN, 128, 128, 2, 2, 2, 2),        \
+  G15_M16T(T, TN, 64, 128, 2, 2, 3, 3)
 
 const KernelEntry kM16N[] = {
     G15_M16N_ALL(bf16_t, "bf16"), G15_M16N_ALL(f16_t, "f16"),
