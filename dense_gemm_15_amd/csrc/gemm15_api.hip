@@ -158,6 +158,7 @@ const EffRow kEff[] = {
     {"m16n_bf16_256x128", 0.86}, {"m16n_f16_256x128", 0.86},
     {"m16n_bf16_128x128x64_w2x2_a2_b2", 0.86}, {"m16n_f16_128x128x64_w2x2_a2_b2", 0.86},
     {"m16n_bf16_128x128x64_w2x2_a3_b3", 0.85}, {"m16n_f16_128x128x64_w2x2_a3_b3", 0.85},
+    {"m16n_bf16_64x128x64_w2x2_a3_b3", 0.70, 16.0, 1.0}, {"m16n_f16_64x128x64_w2x2_a3_b3", 0.70, 16.0, 1.0},
     {"m16n_bf16_64x128", 0.66}, {"m16n_f16_64x128", 0.66},
     {"mfma16_bf16_128x128_w2x2_scalar", 0.10}, {"mfma16_f16_128x128_w2x2_scalar", 0.10},
     {"mfma16_bf16_64x64_w2x2_scalar", 0.08}, {"mfma16_f16_64x64_w2x2_scalar", 0.08},

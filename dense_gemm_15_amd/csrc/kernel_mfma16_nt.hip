@@ -428,7 +428,8 @@ hipError_t launch_m16n(const LaunchArgs& a, hipStream_t s) {
   G15_M16N(T, TN, 128, 256, 2, 4, 3, 3),        \
   G15_M16N(T, TN, 128, 128, 2, 2, 3, 3),        \
   G15_M16N(T, TN, 128, 128, 2, 2, 2, 2),        \
-  G15_M16N(T, TN, 64, 128, 2, 2, 4, 4)
+  G15_M16N(T, TN, 64, 128, 2, 2, 4, 4),        \
+  G15_M16N(T, TN, 64, 128, 2, 2, 3, 3)
 
 #define G15_M16T_ALL(T, TN)                     \
   G15_M16T(T, TN, 256, 256, 4, 2, 3, 2),        \

@@ -391,3 +391,11 @@ def test_cost_model_counts_rounds(shape, layout, prefix):
     on 64 x 128)."""
     ch = g.select(*shape, "bf16", b_layout=layout, **MI355X)
     assert g.config_names()[ch.config].startswith(prefix), (shape, layout)
+
+
+@pytest.mark.parametrize("shape", [(512, 512, 512), (1024, 1024, 1024), (768, 4096, 128)])
+def test_small_transposed_products_take_three_slot_tile(shape):
+    """With B given transposed, small products take the 64 x 128 tile with the 3-slot
+    ring (measured 3-9% faster than the 4-slot one and than 128 x 128 tiles)."""
+    ch = g.select(*shape, "bf16", b_layout="nk", **MI355X)
+    assert g.config_names()[ch.config] == "m16n_bf16_64x128x64_w2x2_a3_b3", shape
