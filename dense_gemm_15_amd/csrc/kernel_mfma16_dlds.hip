@@ -62,9 +62,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16d_kernel(LaunchArgs a)
             LDC = static_cast<int>(a.ldc);
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  int64_t z;
+  batch_tile_of(tiles_m, tiles_n, tm, tn, z);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int64_t z = blockIdx.y;
 
   // 16-byte chunk c of LDS row `row` (A and B alike) sits at c ^ (row & 7) ^
   // ((row >> 3) & 3). A fragment read (32 consecutive rows, one chunk) is then free

@@ -70,9 +70,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_m16n_kernel(LaunchArgs a)
   const int LDA = static_cast<int>(a.lda), LDB = static_cast<int>(a.ldb);
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
   int tm, tn;
-  tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  int64_t z;
+  batch_tile_of(tiles_m, tiles_n, tm, tn, z);
   const int m0 = tm * BM, n0 = tn * BN;
-  const int64_t z = blockIdx.y;
 
   // 16-byte chunk c of an LDS row sits at c ^ (row & 7) ^ ((row >> 3) & 3) in both
   // rings (conflict-free fragment reads). Instruction i of a wave fills 8 rows
