@@ -116,20 +116,21 @@ gemm_epilogue norm_epi(const gemm_epilogue* e) {
   return e ? *e : d;
 }
 
-// Relative sustained throughput of one CU running a configuration at full
-// occupancy (1.0 = m16d 256 x 256, the reference configuration of the 16-bit
-// types; the fastest fp32 configuration for fp32), and the fixed cost of one tile
-// (prologue, epilogue) in rows of K. Measured on MI355X with square 4096 products
-// (whole rounds of tiles, so wave quantisation does not enter) and rounded; the
-// 256 x 256 m16t and m16w rows were refitted on products with K from 1024 to
-// 16384 (m16t is fastest up to K of about 4096, m16w beyond: its longer prologue
-// and epilogue cost about 250 rows of K per tile). The cost model below adds the
-// rounds of tiles a shape needs.
+// Per configuration: the relative sustained throughput of one CU at full occupancy
+// (1.0 = m16d 256 x 256 for the 16-bit types, f32d 256 x 256 for fp32), the fixed
+// cost of one tile (prologue, epilogue) in rows of K, and the throughput of a lone
+// workgroup of an occupancy-2 configuration relative to a pair. First measured on
+// MI355X with square 4096 products (whole rounds of tiles), then refitted on sweeps
+// of 16-bit products timed on every main tile configuration (66 shapes, M, N, K
+// from 96 to 8192: the model's picks within 0.8% of the per-shape best); m16t is
+// fastest up to K of about 4096, m16w beyond (its longer prologue and epilogue
+// cost about 250 rows of K per tile). The cost model below adds the rounds of
+// tiles a shape needs.
 struct EffRow {
   const char* name_prefix;
   double eff;
   double fixed = 64.0;
-  double lone = 0.63;  // throughput of a lone workgroup of an occupancy-2 configuration
+  double lone = 0.63;
 };
 const EffRow kEff[] = {
     // bf16 / fp16
