@@ -82,19 +82,19 @@ __device__ __forceinline__ void tile_of(int wid, int tiles_m, int tiles_n, int& 
 // Tile and batch item of this workgroup in a (tiles, items) grid. Workgroups reach
 // the 8 XCDs round-robin in dispatch order (x fastest), so with few tiles per item
 // XCD k would take tile k of every item and its L2 would share no operand rows. With
-// the items a whole number of groups of 8, XCD x takes the items x, x + 8, ... whole
-// (measured: 64 items of 256 x 256 x 256 on 64 x 128 tiles 14.1 us in the tile-major
-// order); otherwise the tile-major order of tile_of.
+// several items and a whole number of workgroups per XCD, the (item, tile) pairs are
+// taken item by item and XCD x gets the x-th eighth of them: whole items where the
+// items divide by 8 (measured: 64 items of 256 x 256 x 256 on 64 x 128 tiles 14.1 us
+// in the tile-major order, 10.4 us so); otherwise the tile-major order of tile_of.
 __device__ __forceinline__ void batch_tile_of(int tiles_m, int tiles_n, int& tm, int& tn,
                                               int64_t& z) {
-  const int64_t items = gridDim.y;
-  if (items >= 8 && (items & 7) == 0) {
-    const int64_t per_item = static_cast<int64_t>(tiles_m) * tiles_n;  // gridDim.x
+  const int64_t per_item = static_cast<int64_t>(tiles_m) * tiles_n;  // gridDim.x
+  const int64_t total = per_item * gridDim.y;
+  if (gridDim.y > 1 && (total & 7) == 0) {
     const int64_t l = static_cast<int64_t>(blockIdx.y) * gridDim.x + blockIdx.x;
-    const int64_t u = l >> 3;  // this workgroup's index on its XCD (l & 7)
-    const int64_t i = u / per_item;
-    z = (l & 7) + 8 * i;
-    tile_in_groups(static_cast<int>(u - i * per_item), tiles_m, tiles_n, tm, tn);
+    const int64_t w = (l & 7) * (total >> 3) + (l >> 3);  // XCD l & 7 takes a contiguous run
+    z = w / per_item;
+    tile_in_groups(static_cast<int>(w - z * per_item), tiles_m, tiles_n, tm, tn);
     return;
   }
   tile_of(blockIdx.x, tiles_m, tiles_n, tm, tn);
