@@ -541,6 +541,33 @@ def test_packed_operands(g, case):
             assert r["ok"], (kind, rep, plan.describe(), r)
 
 
+@pytest.mark.parametrize("name", ["m16t_bf16_64x128x64_w2x2_a3_b3", "m16t_bf16_128x128x64_w2x2_a2_b2",
+                                  "m16d_bf16_64x128x64_w2x2_a4_b4_r2", "m16n_bf16_64x128x64_w2x2_a3_b3"])
+@pytest.mark.parametrize("shape,nb", [((200, 136, 96), 8), ((200, 136, 96), 12), ((130, 120, 72), 5),
+                                      ((130, 120, 72), 8), ((70, 248, 40), 17)])
+def test_batched_grid_order(g, name, shape, nb):
+    """Batched grids in both workgroup orders: item by item with a contiguous share per
+    XCD when the workgroups divide by 8 (8 and 12 items of 8 tiles, 8 items of 3 tiles
+    on 64 x 128), tile-major otherwise (5 items of 3 tiles); ragged M, N and K; every
+    element of every item against the oracle."""
+    M, N, K = shape
+    nk = name.startswith("m16n")
+    plan = g.Plan(M, N, K, "bf16", config=name, batch_hint=nb, b_layout="nk" if nk else "kn")
+    say(f"[{name}] {nb} x {M}x{N}x{K}")
+    As = torch.stack([gc.inputs(M, N, K, "bf16", 1800 + 2 * b)[0] for b in range(nb)])
+    Bs = torch.stack([gc.inputs(M, N, K, "bf16", 1800 + 2 * b)[1] for b in range(nb)])
+    if nk:
+        Cs = _run_nt(plan, As, Bs, batched=True)
+    else:
+        dev = torch.device("cuda")
+        Cs = plan.run_batched(As.to(dev), Bs.to(dev))
+        torch.cuda.synchronize()
+        Cs = Cs.cpu()
+    for b in range(nb):
+        r = gc.check_full(Cs[b], As[b], Bs[b], "bf16")
+        assert r["ok"], (name, shape, nb, b, r)
+
+
 def test_packed_batched_and_misaligned(g):
     """A strided batch through the padded copies (one item at a time), and an
     operand that is not copied but starts off a 16-byte boundary: the plan then
